@@ -1,0 +1,151 @@
+/*
+ * qmm_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU reference for the block-quantized
+ * weight matmul y = x * W^T over GGUF Q4_0 / Q8_0 weight blocks. Only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * this library; the product path never calls it and shares no code with it.
+ *
+ * What is computed (the plain definition, evaluated in f64):
+ *   y[m][n] = sum_k x[m][k] * w[n][k],  w[n][k] = d * (q - 8)   (Q4_0)
+ *                                        w[n][k] = d * q         (Q8_0)
+ *   s[m][n] = sum_k |x[m][k] * w[n][k]|   (the scale of the error bound)
+ * The pages ("Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3,
+ * and GLiNER2", section Validation) name the two formats by their GGUF
+ * names (Q4_0, Q8_0) and count their dispatches; the block layout is GGUF's:
+ *   Q4_0 block (18 B): fp16 d, then qs[16]; element j < 16 is the low
+ *     nibble of qs[j], element j + 16 the high nibble of qs[j].
+ *   Q8_0 block (34 B): fp16 d, then 32 int8 values, element j = qs[j].
+ *
+ * Exactness: d has at most 11 significant bits, (q - 8) at most 4, a Q8_0
+ * value at most 8, and an f32 activation 24, so every product term fits in
+ * 43 bits and is exact in f64; the only rounding is the f64 summation,
+ * at most (K-1) * 2^-53 * s[m][n].
+ *
+ * Parallelism: OpenMP over independent (m, n) outputs only; each output is
+ * summed serially in k order, so results do not depend on thread count.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16 -> double, written from the format definition:
+ * sign bit 15, exponent bits 14..10 (bias 15), fraction bits 9..0.
+ * Exponent 0 is zero/subnormal (f * 2^-24), 31 is Inf/NaN. */
+double qmm_oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+static double block_scale(const uint8_t *blk)
+{
+    return qmm_oracle_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/* Dequantized weight k (0..31) of one Q4_0 block. */
+static double q4_0_weight(const uint8_t *blk, double d, int j)
+{
+    int q = (j < 16) ? (blk[2 + j] & 15) : (blk[2 + j - 16] >> 4);
+    return d * (double)(q - 8);
+}
+
+/* Dequantized weight k (0..31) of one Q8_0 block. */
+static double q8_0_weight(const uint8_t *blk, double d, int j)
+{
+    return d * (double)(int8_t)blk[2 + j];
+}
+
+static void one_output(int fmt, const float *xrow, const uint8_t *wrow,
+                       int64_t nblocks, double *y, double *s)
+{
+    const int64_t bs = fmt == 0 ? 18 : 34;
+    double acc = 0.0, abs_acc = 0.0;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const uint8_t *blk = wrow + b * bs;
+        double d = block_scale(blk);
+        for (int j = 0; j < 32; ++j) {
+            double w = fmt == 0 ? q4_0_weight(blk, d, j) : q8_0_weight(blk, d, j);
+            double t = w * (double)xrow[b * 32 + j];
+            acc += t;
+            abs_acc += fabs(t);
+        }
+    }
+    *y = acc;
+    *s = abs_acc;
+}
+
+static void full(int fmt, const float *x, const uint8_t *w, int64_t M,
+                 int64_t N, int64_t K, double *y, double *s)
+{
+    const int64_t nblocks = K / 32;
+    const int64_t row_bytes = nblocks * (fmt == 0 ? 18 : 34);
+    const int64_t total = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        one_output(fmt, x + m * K, w + n * row_bytes, nblocks, y + i, s + i);
+    }
+}
+
+static void at(int fmt, const float *x, const uint8_t *w, int64_t K,
+               const int64_t *ms, const int64_t *ns, int64_t count, double *y,
+               double *s)
+{
+    const int64_t nblocks = K / 32;
+    const int64_t row_bytes = nblocks * (fmt == 0 ? 18 : 34);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        one_output(fmt, x + ms[i] * K, w + ns[i] * row_bytes, nblocks, y + i, s + i);
+}
+
+/* Full outputs: x f32[M][K] row-major, w N x (K/32) blocks, y and s
+ * f64[M][N] row-major. K must be a multiple of 32 (checked by the caller). */
+void qmm_oracle_q4_0(const float *x, const uint8_t *w, int64_t M, int64_t N,
+                     int64_t K, double *y, double *s)
+{
+    full(0, x, w, M, N, K, y, s);
+}
+
+void qmm_oracle_q8_0(const float *x, const uint8_t *w, int64_t M, int64_t N,
+                     int64_t K, double *y, double *s)
+{
+    full(1, x, w, M, N, K, y, s);
+}
+
+/* Sampled outputs: y[i], s[i] for the pair (ms[i], ns[i]), i < count. */
+void qmm_oracle_q4_0_at(const float *x, const uint8_t *w, int64_t K,
+                        const int64_t *ms, const int64_t *ns, int64_t count,
+                        double *y, double *s)
+{
+    at(0, x, w, K, ms, ns, count, y, s);
+}
+
+void qmm_oracle_q8_0_at(const float *x, const uint8_t *w, int64_t K,
+                        const int64_t *ms, const int64_t *ns, int64_t count,
+                        double *y, double *s)
+{
+    at(1, x, w, K, ms, ns, count, y, s);
+}
+
+/* Threads an OpenMP region of this library uses (1 without OpenMP). */
+int qmm_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,51 @@
+"""Plant plausible mistakes in a copy of the oracle's C source, build each
+copy, and check that the pins catch every one (CPU only). The planted copies
+live in a temporary directory; the oracle itself is never modified."""
+
+import pathlib
+
+import pytest
+
+import oracle
+import pins
+from oracle import build as oracle_build
+
+SRC = pathlib.Path(oracle.SOURCE).read_text()
+
+# (name, text in the oracle source, replacement)
+MUTANTS = [
+    ("nibble_order_swapped", "(blk[2 + j] & 15) : (blk[2 + j - 16] >> 4)",
+     "(blk[2 + j] >> 4) : (blk[2 + j - 16] & 15)"),
+    ("nibbles_interleaved", "(blk[2 + j] & 15) : (blk[2 + j - 16] >> 4)",
+     "((j & 1) ? (blk[2 + j / 2] >> 4) : (blk[2 + j / 2] & 15)) : "
+     "((j & 1) ? (blk[2 + j / 2] >> 4) : (blk[2 + j / 2] & 15))"),
+    ("zero_point_7", "(double)(q - 8)", "(double)(q - 7)"),
+    ("zero_point_dropped", "(double)(q - 8)", "(double)(q)"),
+    ("q8_unsigned", "(int8_t)blk[2 + j]", "(uint8_t)blk[2 + j]"),
+    ("scale_bytes_swapped", "blk[0] | (blk[1] << 8)", "blk[1] | (blk[0] << 8)"),
+    ("scale_sign_dropped", "return sign ? -v : v;", "return v;"),
+    ("exponent_bias_off", "e - 25)", "e - 24)"),
+    ("subnormal_flushed", "v = ldexp((double)f, -24);", "v = 0.0;"),
+    ("subnormal_as_normal", "v = ldexp((double)f, -24);", "v = ldexp((double)(1024 + f), -25);"),
+    ("abs_dropped", "abs_acc += fabs(t);", "abs_acc += t;"),
+    ("x_index_transposed", "xrow[b * 32 + j]", "xrow[j * (nblocks) + b]"),
+    ("x_neighbour", "xrow[b * 32 + j]", "xrow[b * 32 + (j ^ 1)]"),
+    ("last_block_dropped", "b < nblocks; ++b", "b < nblocks - 1; ++b"),
+    ("q8_block_size_18", "const int64_t bs = fmt == 0 ? 18 : 34;", "const int64_t bs = 18;"),
+    ("row_stride_wrong", "one_output(fmt, x + m * K, w + n * row_bytes",
+     "one_output(fmt, x + m * K, w + n * (row_bytes - 2)"),
+    ("output_transposed", "int64_t m = i / N, n = i % N;", "int64_t n = i / M, m = i % M;"),
+    ("x_row_ignored", "one_output(fmt, x + m * K,", "one_output(fmt, x,"),
+    ("d_applied_twice", "return d * (double)(q - 8);", "return d * d * (double)(q - 8);"),
+    ("f32_accumulation", "acc += t;", "acc = (float)(acc + t);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(old, new, 1))
+    lib = oracle_build.build(src, tmp_path / "libmutant.so", werror=False)
+    failed = pins.failures(oracle.Oracle(lib), quick=True)
+    assert failed, f"no pin catches mutant {name}"
