@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized matmul hot path on one MI355X.
+
+Headline: Q4_0 decode GEMV HBM throughput (GB/s, algorithmic bytes) over the
+Gemma-class FFN pair of one decode step, M = 1: K=2048 -> N=8192 (up) then
+K=8192 -> N=2048 (down). One "step" = those two GEMVs. Weights are cold:
+every launch reads a different copy from a rotating pool of >= 1 GiB, so
+they stream from HBM as in a real decode (the 256 MB Infinity Cache cannot
+hold them). Activations stay resident, as they would right after the
+previous layer produced them.
+
+Timing:
+* ms_per_step / value: K steps captured in one HIP graph and replayed
+  between two device synchronizations (wall clock); the GPU runs the steps
+  back to back.
+* per-kernel durations: an event pair recorded natively on the launch
+  stream around every launch, with the stream kept backlogged so that host
+  overhead never shows in the interval; mean / median / p10 / p90.
+* the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
+  vocabulary GEMV and the Q4_0 prefill GEMM, reported under "rows".
+
+The CPU baseline times the f64 oracle (test infrastructure, plain C with
+OpenMP) on full decode steps for a bounded number of seconds.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import pathlib
+import statistics
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+POOL_BYTES = 1 << 30           # rotating weight pool per shape (>= 1 GiB)
+TRAFFIC_FILE = ROOT / "profiles" / "gemv_q4_0_decode_pair_traffic.json"
+DOMINANT_SOURCES = [ROOT / "block_quantized_matmul_q4_amd" / "csrc" / "gemv_m1.hip",
+                    ROOT / "block_quantized_matmul_q4_amd" / "csrc" / "qmm_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--samples", type=int, default=200,
+                    help="event-timed launches per kernel and shape")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bounded wall time of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode pair (for profiling runs)")
+    return ap.parse_args()
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(pathlib.Path(p).read_bytes())
+    return h.hexdigest()
+
+
+class Hip:
+    """Native HIP event calls (the runtime torch already loaded)."""
+
+    def __init__(self):
+        lib = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventSynchronize.argtypes = [vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        for f in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize",
+                  "hipEventElapsedTime", "hipEventDestroy"):
+            getattr(lib, f).restype = ctypes.c_int
+        self.lib = lib
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def summarize(us):
+    s = sorted(us)
+    q = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
+    return {"mean_us": statistics.fmean(s), "median_us": statistics.median(s),
+            "p10_us": q(0.1), "p90_us": q(0.9), "n": len(s)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_matmul_q4_amd as qmm
+    import synth
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = qmm.library()
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs")
+
+    # ---------------------------------------------------------------- inputs
+    def pool(w_host, min_copies=2):
+        r = max(min_copies, math.ceil(POOL_BYTES / w_host.nbytes))
+        base = torch.from_numpy(w_host.reshape(-1)).to(dev)
+        copies = [base] + [base.clone() for _ in range(r - 1)]
+        return copies
+
+    up = synth.WORKLOADS["q4_0_gemv_ffn_up"]
+    down = synth.WORKLOADS["q4_0_gemv_ffn_down"]
+    log("[bench] generating inputs")
+    x_up_h, w_up_h = synth.workload_inputs("q4_0_gemv_ffn_up")
+    x_dn_h, w_dn_h = synth.workload_inputs("q4_0_gemv_ffn_down")
+    w_up = pool(w_up_h)
+    w_dn = pool(w_dn_h)
+    x_up = torch.from_numpy(x_up_h).to(dev)
+    x_dn = torch.from_numpy(x_dn_h).to(dev)
+    y_up = torch.empty((1, up["N"]), device=dev)
+    y_dn = torch.empty((1, down["N"]), device=dev)
+    bytes_up = w_up_h.nbytes + x_up_h.nbytes + y_up.numel() * 4
+    bytes_dn = w_dn_h.nbytes + x_dn_h.nbytes + y_dn.numel() * 4
+    bytes_step = bytes_up + bytes_dn
+    flops_step = 2 * (up["K"] * up["N"] + down["K"] * down["N"])
+    log(f"[bench] pools: {len(w_up)} x {w_up_h.nbytes} B (up), {len(w_dn)} x "
+        f"{w_dn_h.nbytes} B (down)")
+
+    def ok(st):
+        if st != 0:
+            raise qmm.QmmError(st, qmm.qmm_last_error())
+
+    def launch_up(i, s=sh):
+        ok(lib.qmm_gemv_q4_0(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
+                             y_up.data_ptr(), 1, up["N"], up["K"], s))
+
+    def launch_dn(i, s=sh):
+        ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[i % len(w_dn)].data_ptr(),
+                             y_dn.data_ptr(), 1, down["N"], down["K"], s))
+
+    filler = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def backlog(ms_of_work):
+        # ~0.1 ms per pass; keeps the stream busy while the host enqueues
+        for _ in range(max(1, int(ms_of_work / 0.1))):
+            filler.zero_()
+
+    def time_launches(fn, arglists, est_us=5.0):
+        """Event pair around each launch of fn(*arglists[i], stream)."""
+        count = len(arglists)
+        ev = hip.events(2 * count)
+        rec = hip.lib.hipEventRecord
+        torch.cuda.synchronize()
+        backlog(count * 0.006 + 1.0)   # host needs < 6 us per launch
+        for i in range(count):
+            rec(ev[2 * i], sh)
+            ok(fn(*arglists[i], sh))
+            rec(ev[2 * i + 1], sh)
+        torch.cuda.synchronize()
+        us = [1e3 * hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(count)]
+        for e in ev:
+            hip.lib.hipEventDestroy(e)
+        return summarize(us)
+
+    def gemv_args(x, pool_, y, m, n_, k, count):
+        return [(x.data_ptr(), pool_[i % len(pool_)].data_ptr(), y.data_ptr(), m, n_, k)
+                for i in range(count)]
+
+    # ---------------------------------------------------- eager sanity check
+    launch_up(0)
+    launch_dn(0)
+    torch.cuda.synchronize()
+    ref_up, ref_dn = y_up.clone(), y_dn.clone()
+
+    # ------------------------------------------------ graph-replayed steps
+    def capture(nsteps, offset):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for s in range(nsteps):
+                launch_up(offset + s, cs)
+                launch_dn(offset + s, cs)
+        return g
+
+    log(f"[bench] capturing {args.warmup} warmup + {args.steps} timed steps")
+    g_warm = capture(args.warmup, len(w_up) // 2) if args.warmup > 0 else None
+    g_timed = capture(args.steps, 0)
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = hip.events(2)
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ev0, sh)
+    g_timed.replay()
+    hip.lib.hipEventRecord(ev1, sh)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    gpu_ms = hip.elapsed_ms(ev0, ev1)
+    ms_per_step = 1e3 * wall_s / args.steps
+    # the last replayed step read pool copy steps-1; same bytes as copy 0
+    graph_ok = bool(torch.equal(y_up, ref_up) and torch.equal(y_dn, ref_dn))
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] graph: {ms_per_step * 1e3:.2f} us/step wall, "
+        f"{gpu_ms * 1e3 / args.steps:.2f} us/step GPU events, bitwise vs eager: {graph_ok}")
+
+    # ------------------------------------------------ per-kernel durations
+    n = args.samples
+    t_up = time_launches(lib.qmm_gemv_q4_0, gemv_args(x_up, w_up, y_up, 1, up["N"], up["K"], n))
+    t_dn = time_launches(lib.qmm_gemv_q4_0, gemv_args(x_dn, w_dn, y_dn, 1, down["N"], down["K"], n))
+    log(f"[bench] up   {t_up['mean_us']:.2f} us mean, {t_up['median_us']:.2f} median")
+    log(f"[bench] down {t_dn['mean_us']:.2f} us mean, {t_dn['median_us']:.2f} median")
+    pair_us = t_up["mean_us"] + t_dn["mean_us"]
+    achieved = bytes_step / (pair_us * 1e-6) / 1e9
+
+    rows = {
+        "q4_0_gemv_ffn_up": dict(t_up, bytes=bytes_up,
+                                 gbs=bytes_up / (t_up["mean_us"] * 1e-6) / 1e9),
+        "q4_0_gemv_ffn_down": dict(t_dn, bytes=bytes_dn,
+                                   gbs=bytes_dn / (t_dn["mean_us"] * 1e-6) / 1e9),
+    }
+
+    if not args.decode_only:
+        # small-M GEMV on the up shape (same weight pool)
+        for m in (2, 4, 8, 16):
+            xm = torch.from_numpy(synth.activations(m, up["K"])).to(dev)
+            ym = torch.empty((m, up["N"]), device=dev)
+
+            t = time_launches(lib.qmm_gemv_q4_0, gemv_args(xm, w_up, ym, m, up["N"], up["K"], n))
+            b = w_up_h.nbytes + xm.numel() * 4 + ym.numel() * 4
+            fl = 2 * m * up["N"] * up["K"]
+            rows[f"q4_0_gemv_small_m{m}"] = dict(
+                t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
+                tflops=fl / (t["mean_us"] * 1e-6) / 1e12,
+                tokens_per_s=m / (t["mean_us"] * 1e-6))
+            log(f"[bench] small M={m}: {t['mean_us']:.2f} us")
+        # Q8_0 vocabulary GEMV
+        voc = synth.WORKLOADS["q8_0_gemv_vocab"]
+        xv_h, wv_h = synth.workload_inputs("q8_0_gemv_vocab")
+        wv = pool(wv_h)
+        xv = torch.from_numpy(xv_h).to(dev)
+        yv = torch.empty((1, voc["N"]), device=dev)
+
+        tv = time_launches(lib.qmm_gemv_q8_0,
+                           gemv_args(xv, wv, yv, 1, voc["N"], voc["K"], max(20, n // 4)))
+        bv = wv_h.nbytes + xv_h.nbytes + yv.numel() * 4
+        rows["q8_0_gemv_vocab"] = dict(tv, bytes=bv, gbs=bv / (tv["mean_us"] * 1e-6) / 1e9)
+        log(f"[bench] q8 vocab: {tv['mean_us']:.2f} us")
+        del wv
+        # Q4_0 prefill GEMM
+        pre = synth.WORKLOADS["q4_0_gemm_prefill"]
+        xp = torch.from_numpy(synth.activations(pre["M"], pre["K"])).to(dev)
+        yp = torch.empty((pre["M"], pre["N"]), device=dev)
+
+        tp = time_launches(lib.qmm_gemm_q4_0,
+                           gemv_args(xp, w_up, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
+        fp = 2 * pre["M"] * pre["N"] * pre["K"]
+        tfl = fp / (tp["mean_us"] * 1e-6) / 1e12
+        rows["q4_0_gemm_prefill"] = dict(tp, flops=fp, tflops=tfl,
+                                         frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
+                                         prefill_tokens_per_s=pre["M"] / (tp["mean_us"] * 1e-6))
+        log(f"[bench] prefill GEMM: {tp['mean_us']:.2f} us, {tfl:.1f} TFLOP/s")
+        # decode step model: 342 Q4_0 GEMVs (171 FFN pairs) + 1 Q8_0 GEMV
+        t_step = 171 * (t_up["mean_us"] + t_dn["mean_us"]) + tv["mean_us"]
+        rows["decode_tok_s_equiv"] = 1e6 / t_step
+
+    # ------------------------------------------------ counters, if current
+    traffic = None
+    if TRAFFIC_FILE.exists():
+        rec = json.loads(TRAFFIC_FILE.read_text())
+        if rec.get("source_sha256") == source_hash(DOMINANT_SOURCES):
+            traffic = rec.get("hbm_bytes_per_step")
+
+    # ------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.load()
+        reps, t_cpu = 0, 0.0
+        log(f"[bench] CPU oracle baseline for ~{args.cpu_seconds:.0f} s")
+        while t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            o.matmul("q4_0", x_up_h, w_up_h, up["N"], up["K"])
+            o.matmul("q4_0", x_dn_h, w_dn_h, down["N"], down["K"])
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": bytes_step * reps / t_cpu / 1e9, "unit": "GB/s",
+               "cores": o.threads(), "kind": "oracle",
+               "sample": f"{reps} full decode-pair steps (M=1, up K=2048->N=8192 and "
+                         f"down K=8192->N=2048), f64, {t_cpu:.1f} s"}
+
+    out = {
+        "metric": "Q4_0 GEMV HBM GB/s (% peak) + decode tok/s equiv; prefill GEMM TFLOP/s",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "q4_0_gemv_ffn_pair: M=1, K=2048->N=8192 (up) then "
+                               "K=8192->N=2048 (down), cold weights",
+                   "M": 1, "shapes": [[up["K"], up["N"]], [down["K"], down["N"]]],
+                   "bytes_per_step": bytes_step, "flops_per_step": flops_step,
+                   "weight_pool_copies": len(w_up), "seed": 0,
+                   "w_up_sha256": synth.sha256(w_up_h), "w_down_sha256": synth.sha256(w_dn_h)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gemv_m1_kernel (Q4_0), up + down launch per step",
+                     "mean_launch_us": pair_us},
+        "cpu_baseline": cpu,
+        "graph_step_bitwise_vs_eager": graph_ok,
+        "gpu_event_us_per_step": gpu_ms * 1e3 / args.steps,
+        "pct_hbm_peak": 100 * value / HBM_PEAK_GBS,
+        "rows": rows,
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+// C-ABI layer of libqmm: argument validation, status codes, the
+// thread-local error string, and dispatch to the gfx950 kernels.
+// Every check runs on the host before any HIP call, so a rejected call
+// leaves the device untouched.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool overlaps(uintptr_t a, uint64_t a_len, uintptr_t b, uint64_t b_len)
+{
+    return a < b + b_len && b < a + a_len;
+}
+
+// Shared checks. block_bytes is 18 (Q4_0) or 34 (Q8_0); max_m bounds M.
+int validate(const char *fn, const float *x, const void *w, const float *y,
+             int64_t M, int64_t N, int64_t K, int block_bytes, int64_t max_m)
+{
+    if (!x || !w || !y)
+        return fail(QMM_EINVAL, "%s: null pointer (x=%p w=%p y=%p)", fn,
+                    (const void *)x, w, (const void *)y);
+    if (M < 1 || N < 1 || K < 1)
+        return fail(QMM_EINVAL, "%s: M, N, K must be >= 1 (M=%lld N=%lld K=%lld)", fn,
+                    (long long)M, (long long)N, (long long)K);
+    if (M > max_m)
+        return fail(QMM_EINVAL, "%s: M=%lld exceeds %lld", fn, (long long)M,
+                    (long long)max_m);
+    if (K % 32)
+        return fail(QMM_EINVAL, "%s: K=%lld is not a multiple of 32 (the block size)", fn,
+                    (long long)K);
+    if (K % 256 || K > QMM_MAX_K)
+        return fail(QMM_EUNSUPPORTED,
+                    "%s: K=%lld unsupported (need K %% 256 == 0 and K <= %d)", fn,
+                    (long long)K, QMM_MAX_K);
+    // Sizes: every index the kernels form fits in int32 element counts for
+    // x and y rows, and byte offsets are 64-bit.
+    if (N > INT_MAX / 2 || M > INT_MAX / 2 || M > INT64_MAX / K / 4 ||
+        M > INT64_MAX / N / 4 || N > INT64_MAX / (K / 32) / block_bytes)
+        return fail(QMM_EINVAL, "%s: sizes overflow (M=%lld N=%lld K=%lld)", fn,
+                    (long long)M, (long long)N, (long long)K);
+    const uintptr_t xa = (uintptr_t)x, wa = (uintptr_t)w, ya = (uintptr_t)y;
+    if (xa % 16 || wa % 16 || ya % 4)
+        return fail(QMM_EALIGN,
+                    "%s: misaligned pointer (x and w need 16-byte, y 4-byte alignment)", fn);
+    const uint64_t x_len = (uint64_t)M * (uint64_t)K * 4u;
+    const uint64_t w_len = (uint64_t)N * (uint64_t)(K / 32) * (uint64_t)block_bytes;
+    const uint64_t y_len = (uint64_t)M * (uint64_t)N * 4u;
+    if (overlaps(ya, y_len, xa, x_len) || overlaps(ya, y_len, wa, w_len))
+        return fail(QMM_EINVAL, "%s: y overlaps x or w", fn);
+    return QMM_OK;
+}
+
+int finish(const char *fn, hipError_t err)
+{
+    if (err != hipSuccess)
+        return fail(QMM_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    const char *fn = "qmm_gemv_q4_0";
+    int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
+    if (st != QMM_OK) return st;
+    const uint8_t *wb = (const uint8_t *)w;
+    if (M == 1)
+        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)N, (int)K, stream));
+    return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
+                                               (int)K, stream));
+}
+
+QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    const char *fn = "qmm_gemv_q8_0";
+    int st = validate(fn, x, w, y, M, N, K, qmm::kQ8Bytes, QMM_GEMV_MAX_M);
+    if (st != QMM_OK) return st;
+    const uint8_t *wb = (const uint8_t *)w;
+    if (M == 1)
+        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)N, (int)K, stream));
+    return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
+                                               (int)K, stream));
+}
+
+QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    const char *fn = "qmm_gemm_q4_0";
+    int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, INT_MAX / 2);
+    if (st != QMM_OK) return st;
+    return finish(fn, qmm::launch_gemm_q4_0(x, (const uint8_t *)w, y, (int)M, (int)N,
+                                            (int)K, stream));
+}
+
+QMM_API const char *qmm_status_string(int status)
+{
+    switch (status) {
+    case QMM_OK: return "QMM_OK";
+    case QMM_EINVAL: return "QMM_EINVAL";
+    case QMM_EALIGN: return "QMM_EALIGN";
+    case QMM_EUNSUPPORTED: return "QMM_EUNSUPPORTED";
+    case QMM_EHIP: return "QMM_EHIP";
+    default: return "QMM_UNKNOWN_STATUS";
+    }
+}
+
+QMM_API const char *qmm_last_error(void) { return g_last_error; }
+
+QMM_API int qmm_version(void) { return 100; }
+
+}  // extern "C"

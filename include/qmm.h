@@ -1,0 +1,112 @@
+/*
+ * qmm.h -- block-quantized weight matmul on AMD Instinct MI355X (gfx950).
+ *
+ * y[m][n] = sum_k x[m][k] * w[n][k]   (y = x * W^T), with W stored as GGUF
+ * weight blocks of 32 consecutive k:
+ *   Q4_0 block, 18 bytes: fp16 scale d (little-endian), then 16 bytes qs;
+ *        element j < 16 is the low nibble of qs[j], element j + 16 its high
+ *        nibble; w = d * (q - 8).
+ *   Q8_0 block, 34 bytes: fp16 scale d, then 32 int8 q; w = d * q.
+ * The pages "Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3,
+ * and GLiNER2" (section Validation) count these two formats among the
+ * generated quant dispatches of one Gemma4 decode (Q4_0 for all but one
+ * projection, Q8_0 for the remaining one); the same pages' Benchmarks
+ * section measures decode and prefill (TTFT) of those models, the two
+ * regimes the entry points below serve.
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   x : float32 [M][K]
+ *   w : N rows of K/32 blocks; row n starts at byte n * (K/32) * block_bytes
+ *   y : float32 [M][N], overwritten (no accumulation into y, no bias)
+ *
+ * Ownership and execution: every pointer is a DEVICE pointer owned by the
+ * caller. The library allocates no memory, keeps no pointer after a call
+ * returns, and enqueues its work asynchronously on `stream` (NULL = the
+ * null stream); it never synchronizes. Calls are thread-safe.
+ *
+ * Errors: arguments are validated on the host before any HIP call, so a
+ * rejected call has no effect on the device. Every entry point returns a
+ * qmm_status; qmm_last_error() gives a thread-local description of the last
+ * non-OK status returned on the calling thread.
+ *   QMM_EINVAL       null pointer; M, N or K < 1; K not a multiple of 32;
+ *                    M > 16 for a GEMV entry point; y overlapping x or w;
+ *                    a byte size that overflows int64.
+ *   QMM_EALIGN       x or w not 16-byte aligned, y not 4-byte aligned.
+ *   QMM_EUNSUPPORTED K not a multiple of 256 (keeps every weight row
+ *                    16-byte aligned), or K > QMM_MAX_K.
+ *   QMM_EHIP         the HIP runtime reported an error at launch.
+ *
+ * Accuracy contract, with s[m][n] = sum_k |x[m][k] * w[n][k]|:
+ *   GEMV entry points (f32 arithmetic):  |y - y_exact| <= 1e-4 * s
+ *   qmm_gemm_q4_0 (bf16 MFMA, f32 acc):   |y - y_exact| <= 8e-3 * s
+ * for finite inputs whose f32 products do not underflow. Results are
+ * bitwise reproducible from call to call (no atomics, fixed reduction order).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define QMM_API __attribute__((visibility("default")))
+#else
+#define QMM_API
+#endif
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_EINVAL = 1,
+    QMM_EALIGN = 2,
+    QMM_EUNSUPPORTED = 3,
+    QMM_EHIP = 4
+} qmm_status;
+
+/* Largest K accepted by any entry point. */
+#define QMM_MAX_K 65536
+/* Largest M accepted by the GEMV entry points. */
+#define QMM_GEMV_MAX_M 16
+
+/*
+ * Decode GEMV over Q4_0 weights, 1 <= M <= 16 activation rows (M = 1 for
+ * one decoded token, M = 2..16 for batched or speculative decode, where
+ * several tokens share one pass over the weights). f32 accumulation; the
+ * weights stream from HBM once per call.
+ */
+QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Decode GEMV over Q8_0 weights (the one Q8_0 projection of a decode step,
+ * typically the vocabulary head), 1 <= M <= 16. Same contract as
+ * qmm_gemv_q4_0.
+ */
+QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Prefill GEMM over Q4_0 weights, any M >= 1 (M = prompt tokens). x is
+ * rounded to bf16 (round-to-nearest-even) and each weight d * (q - 8) to
+ * bf16 inside the kernel; products accumulate in f32 on the matrix cores.
+ */
+QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
+/* Static English name of a status code ("QMM_OK", ...). */
+QMM_API const char *qmm_status_string(int status);
+
+/* Thread-local detail for the last non-OK status on this thread ("" if none). */
+QMM_API const char *qmm_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+QMM_API int qmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

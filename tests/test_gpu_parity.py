@@ -1,0 +1,329 @@
+"""GPU parity: the HIP kernels (through the C-ABI binding) against the f64
+CPU oracle, element by element, on seeded inputs.
+
+Acceptance per output, with s = sum_k |x_k w_k| from the oracle:
+    |y - y_ref| <= tau * s,   tau = 1e-4 (GEMV paths) or 8e-3 (bf16 GEMM);
+no NaN/Inf where y_ref is finite; exact cases must match bitwise.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_matmul_q4_amd as qmm
+import oracle
+import pins
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TAU_GEMV = 1e-4
+TAU_GEMM = 8e-3
+BYTES = {"q4_0": 18, "q8_0": 34}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def weights(fmt, n, k, seed=0):
+    return synth.q4_0_weights(n, k, seed) if fmt == "q4_0" else synth.q8_0_weights(n, k, seed)
+
+
+def run(entry, fmt, x, w, n, k):
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    wt = torch.from_numpy(np.ascontiguousarray(w).reshape(-1)).cuda()
+    fn = {"gemv_q4_0": qmm.gemv_q4_0, "gemv_q8_0": qmm.gemv_q8_0,
+          "gemm_q4_0": qmm.gemm_q4_0}[f"{entry}_{fmt}"]
+    y = fn(xt, wt, n, k)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_parity(y, yref, s, tau, what):
+    assert y.shape == yref.shape, what
+    finite = np.isfinite(yref)
+    assert np.all(np.isfinite(y[finite])), f"{what}: non-finite output"
+    err = np.abs(y.astype(np.float64) - yref)
+    bound = tau * s
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err / np.maximum(bound, 1e-300), 0)), y.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} outputs out of bound; worst at {i}: "
+                             f"y={y[i]!r} ref={yref[i]!r} err={err[i]:.3e} bound={bound[i]:.3e}")
+    return float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
+
+
+def check(orc, entry, fmt, m, n, k, seed=0, x=None, w=None):
+    tau = TAU_GEMM if entry == "gemm" else TAU_GEMV
+    what = f"{entry}_{fmt} M={m} N={n} K={k} seed={seed}"
+    note(f"[parity] {what}")
+    if x is None:
+        x = synth.activations(m, k, seed)
+    if w is None:
+        w = weights(fmt, n, k, seed)
+    y = run(entry, fmt, x, w, n, k)
+    yref, s = orc.matmul(fmt, x, w, n, k)
+    return assert_parity(y, yref, s, tau, what)
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_gemv_tiny(orc):
+    check(orc, "gemv", "q4_0", 1, 256, 512)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 2048), (2048, 8192)], ids=["ffn_up", "ffn_down"])
+def test_gemv_decode_pair(orc, n, k):
+    check(orc, "gemv", "q4_0", 1, n, k)
+
+
+@pytest.mark.parametrize("m", [2, 4, 8, 16])
+def test_gemv_small_m(orc, m):
+    check(orc, "gemv", "q4_0", m, 8192, 2048)
+
+
+def test_gemv_q8_vocab(orc):
+    check(orc, "gemv", "q8_0", 1, 262144, 2048)
+
+
+def test_gemm_prefill(orc):
+    check(orc, "gemm", "q4_0", 2048, 8192, 2048)
+
+
+# ---------------------------------------------------------------------------
+# Ragged and odd shapes (several tiles plus a tail)
+# ---------------------------------------------------------------------------
+
+GEMV_SHAPES = [
+    (1, 1, 256), (1, 3, 512), (1, 17, 768), (1, 257, 2304), (1, 1000, 8192),
+    (1, 333, 4096), (1, 65, 16384), (1, 50, 65536), (1, 4097, 1280),
+    (2, 1, 256), (3, 257, 768), (5, 1000, 2048), (7, 17, 2304), (11, 130, 512),
+    (16, 33, 8192), (16, 1, 256), (13, 4100, 1024),
+]
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("m,n,k", GEMV_SHAPES)
+def test_gemv_shapes(orc, fmt, m, n, k):
+    check(orc, "gemv", fmt, m, n, k, seed=m * 7 + n)
+
+
+GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
+               (300, 17, 512), (256, 256, 4096), (1000, 520, 1280), (17, 2049, 256)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_shapes(orc, m, n, k):
+    check(orc, "gemm", "q4_0", m, n, k, seed=m + n)
+
+
+def test_q4_0_vs_q8_0_scale_distributions(orc):
+    # the Q4_0 scale recipe on Q8_0 bytes and vice versa (wider/narrower d)
+    w = synth.q8_0_weights(512, 2048, seed=5, sigma=0.02)
+    check(orc, "gemv", "q8_0", 1, 512, 2048, w=w)
+    w = synth.q4_0_weights(512, 2048, seed=5, sigma=0.005)
+    check(orc, "gemv", "q4_0", 3, 512, 2048, w=w)
+
+
+# ---------------------------------------------------------------------------
+# Exact cases: the GPU must reproduce the oracle bitwise
+# ---------------------------------------------------------------------------
+
+def pad_golden(g, k=256):
+    """Embed a golden case in K=256 (zero blocks, zero activations)."""
+    bs = BYTES[g["fmt"]]
+    n, k0 = g["N"], g["K"]
+    w = np.zeros((n, k // 32 * bs), np.uint8)
+    w[:, : k0 // 32 * bs] = g["w"].reshape(n, -1)
+    x = np.zeros((g["M"], k), np.float32)
+    x[:, :k0] = g["x"]
+    return x, w
+
+
+@pytest.mark.parametrize("path", pins.golden_cases(), ids=lambda p: p.name)
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_golden_on_gpu(orc, path, entry):
+    """Hand-derived blocks (embedded in K=256 with zero padding) against their
+    exact values: within the contract bound, and bitwise where the exact value
+    is an integer (every partial sum is then exact in f32)."""
+    g = pins.load_golden(path)
+    if entry == "gemm" and g["fmt"] != "q4_0":
+        pytest.skip("the GEMM entry point is Q4_0 only")
+    x, w = pad_golden(g)
+    note(f"[golden] {path.name} {entry}")
+    y = run(entry, g["fmt"], x, w, g["N"], 256)
+    exact = np.array([[float(v) for v in g["y"]]])
+    _, s = orc.matmul(g["fmt"], x, w, g["N"], 256)
+    assert_parity(y, exact, s, TAU_GEMM if entry == "gemm" else TAU_GEMV, path.name)
+    integral = np.array([v.denominator == 1 for v in g["y"]])
+    assert np.array_equal(y[0][integral], exact[0][integral])
+
+
+@pytest.mark.parametrize("entry,fmt,m", [("gemv", "q4_0", 1), ("gemv", "q4_0", 4),
+                                         ("gemv", "q8_0", 1), ("gemv", "q8_0", 16),
+                                         ("gemm", "q4_0", 64)])
+def test_one_hot_exact(orc, entry, fmt, m):
+    n, k = 96, 512
+    rng = np.random.default_rng(11)
+    d = pins.random_fp16(rng, (n, k // 32))
+    d = np.clip(d.astype(np.float32), -60000, 60000).astype(np.float16)
+    q = (rng.integers(0, 16, (n, k), dtype=np.uint8) if fmt == "q4_0"
+         else rng.integers(-128, 128, (n, k), dtype=np.int8))
+    w = pins.pack(fmt, d, q)
+    ks = rng.integers(0, k, m)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), ks] = 1.0
+    note(f"[exact] one-hot {entry} {fmt} M={m}")
+    y = run(entry, fmt, x, w, n, k).astype(np.float64)
+    yref, _ = orc.matmul(fmt, x, w, n, k)
+    if entry == "gemv":
+        assert np.array_equal(y, yref.astype(np.float32).astype(np.float64))
+    else:  # bf16(d * (q - 8)) exactly
+        want = torch.from_numpy(yref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(y, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("entry,fmt,m", [("gemv", "q4_0", 1), ("gemv", "q4_0", 9),
+                                         ("gemv", "q8_0", 1), ("gemv", "q8_0", 5),
+                                         ("gemm", "q4_0", 33)])
+def test_integer_exact(orc, entry, fmt, m):
+    n, k = 200, 2048
+    rng = np.random.default_rng(12)
+    d = np.ones((n, k // 32), np.float16)
+    q = (rng.integers(0, 16, (n, k), dtype=np.uint8) if fmt == "q4_0"
+         else rng.integers(-128, 128, (n, k), dtype=np.int8))
+    x = rng.integers(-8, 9, (m, k)).astype(np.float32)
+    w = pins.pack(fmt, d, q)
+    note(f"[exact] integer {entry} {fmt} M={m}")
+    y = run(entry, fmt, x, w, n, k)
+    yref, _ = orc.matmul(fmt, x, w, n, k)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+@pytest.mark.parametrize("entry,m", [("gemv", 1), ("gemv", 6), ("gemm", 40)])
+def test_zero_point_exact(entry, m):
+    n, k = 100, 1024
+    rng = np.random.default_rng(13)
+    d = pins.random_fp16(rng, (n, k // 32))
+    w = synth.pack_q4_0(d, np.full((n, k), 8, np.uint8))
+    x = (rng.standard_normal((m, k)) * 100).astype(np.float32)
+    note(f"[exact] all-8 nibbles {entry} M={m}")
+    y = run(entry, "q4_0", x, w, n, k)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("entry,m", [("gemv", 1), ("gemv", 2), ("gemm", 3)])
+def test_subnormal_scale_exact(entry, m):
+    n, k = 4, 256
+    bits = np.array([0x0001, 0x03FF, 0x8001, 0x0200], np.uint16)
+    d = np.repeat(bits[:, None], k // 32, axis=1).view(np.float16)
+    w = synth.pack_q4_0(d, np.full((n, k), 15, np.uint8))
+    x = np.ones((m, k), np.float32)
+    note(f"[exact] subnormal d {entry} M={m}")
+    y = run(entry, "q4_0", x, w, n, k)
+    f = (bits & 0x3FF).astype(np.float64) * np.where(bits & 0x8000, -1, 1)
+    want = 7 * k * f * 2.0 ** -24
+    if entry == "gemm":
+        want = torch.from_numpy((7 * f * 2.0 ** -24).astype(np.float32)).to(
+            torch.bfloat16).double().numpy() * k
+    assert np.array_equal(y, np.broadcast_to(want, (m, n)).astype(np.float32))
+
+
+def test_linear_in_d_bitwise():
+    n, k = 300, 2048
+    d, q = synth.q4_0_fields(n, k, seed=3)
+    d2 = (d.astype(np.float64) * 2).astype(np.float16)
+    x = synth.activations(4, k, seed=3)
+    for m in (1, 4):
+        note(f"[exact] linear in d M={m}")
+        y1 = run("gemv", "q4_0", x[:m], synth.pack_q4_0(d, q), n, k)
+        y2 = run("gemv", "q4_0", x[:m], synth.pack_q4_0(d2, q), n, k)
+        assert np.array_equal(y2, 2 * y1)
+
+
+# ---------------------------------------------------------------------------
+# Determinism, streams, errors
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("entry,fmt,m,n,k", [("gemv", "q4_0", 1, 8192, 2048),
+                                             ("gemv", "q4_0", 8, 8192, 2048),
+                                             ("gemv", "q8_0", 1, 4096, 2048),
+                                             ("gemm", "q4_0", 512, 1024, 2048)])
+def test_bitwise_repeatable(entry, fmt, m, n, k):
+    x = synth.activations(m, k, seed=21)
+    w = weights(fmt, n, k, seed=21)
+    note(f"[determinism] {entry}_{fmt} M={m}")
+    ys = [run(entry, fmt, x, w, n, k) for _ in range(3)]
+    assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
+
+
+def test_side_stream(orc):
+    n, k = 1000, 2048
+    x = synth.activations(2, k, seed=4)
+    w = synth.q4_0_weights(n, k, seed=4)
+    xt = torch.from_numpy(x).cuda()
+    wt = torch.from_numpy(w.reshape(-1)).cuda()
+    s = torch.cuda.Stream()
+    note("[stream] side stream")
+    with torch.cuda.stream(s):
+        y1 = qmm.gemv_q4_0(xt[:1], wt, n, k)
+        y2 = qmm.gemv_q4_0(xt, wt, n, k)
+        y3 = qmm.gemm_q4_0(xt, wt, n, k)
+    s.synchronize()
+    yref, sref = orc.matmul("q4_0", x, w, n, k)
+    assert_parity(y1.cpu().numpy(), yref[:1], sref[:1], TAU_GEMV, "side stream M=1")
+    assert_parity(y2.cpu().numpy(), yref, sref, TAU_GEMV, "side stream M=2")
+    assert_parity(y3.cpu().numpy(), yref, sref, TAU_GEMM, "side stream gemm")
+
+
+def test_out_argument_overwrites():
+    n, k = 64, 256
+    x = torch.from_numpy(synth.activations(1, k)).cuda()
+    w = torch.from_numpy(synth.q4_0_weights(n, k).reshape(-1)).cuda()
+    out = torch.full((1, n), float("nan"), device="cuda")
+    y = qmm.gemv_q4_0(x, w, n, k, out=out)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == out.data_ptr() and torch.isfinite(out).all()
+
+
+def test_errors_raise_on_gpu():
+    x = torch.zeros(1, 96, device="cuda")
+    w = torch.zeros(8 * 3 * 18, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.gemv_q4_0(x, w, 8, 96)
+    assert e.value.status == qmm.QMM_EUNSUPPORTED
+    x = torch.zeros(17, 256, device="cuda")
+    w = torch.zeros(8 * 8 * 18, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.gemv_q4_0(x, w, 8, 256)
+    assert e.value.status == qmm.QMM_EINVAL
+
+
+def test_randomized_small_shapes(orc):
+    """Seeded randomized differential test over many small shapes."""
+    rng = np.random.default_rng(2024)
+    for case in range(120):
+        entry = ["gemv", "gemv", "gemm"][case % 3]
+        fmt = "q8_0" if (entry == "gemv" and case % 2) else "q4_0"
+        m = int(rng.integers(1, 17)) if entry == "gemv" else int(rng.integers(1, 200))
+        n = int(rng.integers(1, 600))
+        k = 256 * int(rng.integers(1, 13))
+        check(orc, entry, fmt, m, n, k, seed=1000 + case)
