@@ -25,6 +25,8 @@ FLAGS = [
     "-Wall", "-Werror", "-Wno-unused-function",
     # never let the compiler form v_pk_{add,mul,fma}_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # private arrays stay in registers; never silently moved into LDS
+    "-mllvm", "-disable-promote-alloca-to-lds",
     f"-I{INCLUDE}",
 ]
 

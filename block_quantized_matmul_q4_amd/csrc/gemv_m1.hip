@@ -7,8 +7,9 @@
 //    for Q4_0, 68 for Q8_0) at the same K position in RPT different rows.
 //    A pair always starts on a dword boundary, so it is fetched with
 //    dwordx4 loads; the lanes of a row cover the row's bytes contiguously.
-//  * The 64 activations of the thread's pair are loaded once into VGPRs and
-//    reused for all RPT rows (x is tiny and cache-resident).
+//  * The activations are staged once per workgroup into LDS with coalesced
+//    loads; each thread reads the 64 of its pair into VGPRs and reuses them
+//    for all RPT rows.
 //  * All weight loads of a chunk are issued before any arithmetic, so each
 //    thread keeps RPT * pair bytes in flight.
 //  * Decode: Q4_0 nibbles become 16*(q-8) as signed bytes with two logic
@@ -22,6 +23,21 @@
 namespace qmm {
 namespace {
 
+// Weight loads; NT marks them non-temporal (streamed once, not worth caching).
+template <bool NT>
+__device__ __forceinline__ u32x4_a4 ld(const u32x4_a4 *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ uint32_t ld(const uint32_t *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 template <int FMT> struct Pair;
 
 template <> struct Pair<FMT_Q4_0> {
@@ -29,13 +45,14 @@ template <> struct Pair<FMT_Q4_0> {
     static constexpr int kBytes = 36;
     static constexpr float kOutScale = 1.0f / 16.0f;
 
+    template <bool NT>
     __device__ static void load(const uint8_t *p, uint32_t (&D)[kDwords])
     {
-        const u32x4_a4 a = *(const u32x4_a4 *)p;
-        const u32x4_a4 b = *(const u32x4_a4 *)(p + 16);
+        const u32x4_a4 a = ld<NT>((const u32x4_a4 *)p);
+        const u32x4_a4 b = ld<NT>((const u32x4_a4 *)(p + 16));
         D[0] = a.x; D[1] = a.y; D[2] = a.z; D[3] = a.w;
         D[4] = b.x; D[5] = b.y; D[6] = b.z; D[7] = b.w;
-        D[8] = *(const uint32_t *)(p + 32);
+        D[8] = ld<NT>((const uint32_t *)(p + 32));
     }
 
     // Pair bytes: [0,2) d0, [2,18) qs of block 0, [18,20) d1, [20,36) qs of
@@ -69,15 +86,16 @@ template <> struct Pair<FMT_Q8_0> {
     static constexpr int kBytes = 68;
     static constexpr float kOutScale = 1.0f;
 
+    template <bool NT>
     __device__ static void load(const uint8_t *p, uint32_t (&D)[kDwords])
     {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const u32x4_a4 a = *(const u32x4_a4 *)(p + 16 * i);
+            const u32x4_a4 a = ld<NT>((const u32x4_a4 *)(p + 16 * i));
             D[4 * i + 0] = a.x; D[4 * i + 1] = a.y;
             D[4 * i + 2] = a.z; D[4 * i + 3] = a.w;
         }
-        D[16] = *(const uint32_t *)(p + 64);
+        D[16] = ld<NT>((const uint32_t *)(p + 64));
     }
 
     // Pair bytes: [0,2) d0, [2,34) q of block 0, [34,36) d1, [36,68) q of
@@ -98,62 +116,113 @@ template <> struct Pair<FMT_Q8_0> {
     }
 };
 
-constexpr int kThreads = 256;
-
-// T threads per row (power of two, 4..256), RPT rows per thread.
-// Grid: ceil(N / (256 / T * RPT)) workgroups of 256 threads.
-template <int FMT, int T, int RPT>
-__global__ __launch_bounds__(kThreads) void gemv_m1_kernel(
+// T threads per row (power of two, 4..WG), RPT rows per thread, CH chunks
+// of T pairs per pass along K, WG threads per workgroup, NT non-temporal
+// weight loads. Grid: ceil(N / (WG / T * RPT)) workgroups.
+//
+// A wave owns TW = min(T, 64) consecutive pairs of each chunk for its rows
+// (a row wider than one wave is split over T / 64 waves). Per pass of CH
+// chunks along K:
+//  1. the wave loads the activations of its pairs (64 floats each) with
+//     coalesced 16-byte loads (L2-resident after the first workgroup);
+//  2. each thread issues the loads of all its CH * RPT weight pairs (HBM);
+//  3. the wave writes the activations to its own LDS region, in rows of 64
+//     floats padded by 4 so that consecutive lanes' 16-byte reads fall in
+//     distinct banks; no workgroup barrier is involved;
+//  4. per chunk, each thread reads its 64 activations back and runs the
+//     FMAs for its RPT rows.
+// Every load is unconditional from a clamped in-bounds address: rows past N
+// are computed and dropped, pairs past P are masked by a select.
+template <int FMT, int T, int RPT, int CH, int WG, bool NT>
+__global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int N, int P)
 {
     using L = Pair<FMT>;
-    constexpr int RPAR = kThreads / T;          // rows in flight per workgroup
-    constexpr int G = T < 64 ? T : 64;          // lanes of a row inside one wave
-    constexpr int WPR = T > 64 ? T / 64 : 1;    // waves per row
+    constexpr int RPAR = WG / T;                // rows in flight per workgroup
+    constexpr int TW = T < 64 ? T : 64;         // pairs per wave per chunk
+    constexpr int WPR = T / TW;                 // waves per row
+    constexpr int XS = 68;                      // padded LDS row (floats)
+    constexpr int XF4 = 16 * TW / 64;           // float4s per lane per chunk
+    constexpr int REGION = CH * TW * XS;        // floats per wave
+    __shared__ __attribute__((aligned(16))) float xs_all[WG / 64 * REGION];
+
     const int tid = threadIdx.x;
+    const int lane = tid % 64, wave = tid / 64;
     const int t = tid % T;
     const int r = tid / T;
+    const int tw0 = t - lane % TW;              // first pair index of this wave
+    float *xs = xs_all + wave * REGION;
     const int64_t row_bytes = (int64_t)P * L::kBytes;
     const int n_first = blockIdx.x * (RPAR * RPT) + r;
+
+    const uint8_t *wrow[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        wrow[j] = w + (int64_t)min(n_first + RPAR * j, N - 1) * row_bytes;
 
     float acc[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j) acc[j] = 0.f;
 
-    for (int c = 0; c < P; c += T) {
-        const int p = c + t;
-        const bool pv = p < P;
-        uint32_t D[RPT][L::kDwords];
+    for (int c0 = 0; c0 < P; c0 += CH * T) {
+        // 1. activations of this wave's pairs in CH chunks; float4 i of a
+        //    chunk belongs to the wave's pair i / 16 (pairs clamped to P-1)
+        float4 xst[CH][XF4];
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-            const int n = n_first + RPAR * j;
-            if (pv && n < N) {
-                L::load(w + n * row_bytes + (int64_t)p * L::kBytes, D[j]);
-            } else {
+        for (int h = 0; h < CH; ++h) {
 #pragma unroll
-                for (int i = 0; i < L::kDwords; ++i) D[j][i] = 0u;
+            for (int u = 0; u < XF4; ++u) {
+                const int i = lane + 64 * u;
+                const int pp = min(c0 + h * T + tw0 + i / 16, P - 1);
+                xst[h][u] = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
             }
         }
-        float xv[64];
-        if (pv) {
-            const float4 *xp = reinterpret_cast<const float4 *>(x + 64 * p);
+        __builtin_amdgcn_sched_barrier(0);
+        // 2. weight pairs
+        uint32_t D[CH][RPT][L::kDwords];
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+            const int pc = min(c0 + h * T + t, P - 1);
+#pragma unroll
+            for (int j = 0; j < RPT; ++j)
+                L::template load<NT>(wrow[j] + (int64_t)pc * L::kBytes, D[h][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 3. activations to this wave's LDS region
+        __builtin_amdgcn_wave_barrier();        // previous pass's reads done
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+#pragma unroll
+            for (int u = 0; u < XF4; ++u) {
+                const int i = lane + 64 * u;
+                *reinterpret_cast<float4 *>(&xs[(h * TW + i / 16) * XS + 4 * (i % 16)]) =
+                    xst[h][u];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // 4. per chunk: activations back to VGPRs, FMAs
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+            float xv[64];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float4 v = xp[i];
+                const float4 v = *reinterpret_cast<const float4 *>(
+                    &xs[(h * TW + lane % TW) * XS + 4 * i]);
                 xv[4 * i + 0] = v.x; xv[4 * i + 1] = v.y;
                 xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
             }
-        } else {
+            const bool pv = c0 + h * T + t < P;
 #pragma unroll
-            for (int i = 0; i < 64; ++i) xv[i] = 0.f;
+            for (int j = 0; j < RPT; ++j) {
+                const float part = L::dot(D[h][j], xv, 0.f);
+                acc[j] += pv ? part : 0.f;
+            }
         }
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) acc[j] = L::dot(D[j], xv, acc[j]);
     }
 
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) acc[j] = group_sum<G>(acc[j]);
+    for (int j = 0; j < RPT; ++j) acc[j] = group_sum<TW>(acc[j]);
 
     if constexpr (WPR == 1) {
         if (t == T - 1) {
@@ -164,60 +233,64 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_kernel(
             }
         }
     } else {
-        __shared__ float red[kThreads / 64][RPT];
-        const int wave = tid / 64, lane = tid % 64;
+        __syncthreads();                        // every wave is done with xs
+        float *red = xs_all;                    // [WG / 64][RPT]
         if (lane == 63) {
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) red[wave][j] = acc[j];
+            for (int j = 0; j < RPT; ++j) red[wave * RPT + j] = acc[j];
         }
         __syncthreads();
         if (tid < RPAR * RPT) {
             const int rr = tid % RPAR, j = tid / RPAR;
             float s = 0.f;
 #pragma unroll
-            for (int q = 0; q < WPR; ++q) s += red[rr * WPR + q][j];
+            for (int q = 0; q < WPR; ++q) s += red[(rr * WPR + q) * RPT + j];
             const int n = blockIdx.x * (RPAR * RPT) + rr + RPAR * j;
             if (n < N) y[n] = s * L::kOutScale;
         }
     }
 }
 
-template <int FMT, int T, int RPT>
+constexpr int kThreads = 256;
+
+template <int FMT, int T, int RPT, int WG = kThreads, int CH = 1, bool NT = false>
 hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
                   hipStream_t stream)
 {
-    constexpr int rows_per_wg = kThreads / T * RPT;
+    constexpr int rows_per_wg = WG / T * RPT;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, NT>), dim3(grid), dim3(WG), 0,
                        stream, x, w, y, N, P);
     return hipGetLastError();
 }
 
-// Rows per thread: as many as keep at least ~2 workgroups per compute unit
-// (256 CUs) busy, so every thread streams several rows' pairs at once.
-template <int FMT, int T>
-hipError_t launch_t(const float *x, const uint8_t *w, float *y, int N, int P,
-                    hipStream_t stream)
-{
-    constexpr int rpar = kThreads / T;
-    const int64_t groups = (N + rpar - 1) / rpar;   // row groups of RPAR rows
-    if (groups >= 4 * 512) return launch<FMT, T, 4>(x, w, y, N, P, stream);
-    if (groups >= 2 * 512) return launch<FMT, T, 2>(x, w, y, N, P, stream);
-    return launch<FMT, T, 1>(x, w, y, N, P, stream);
-}
-
+// Launch shapes, from timing sweeps on MI355X (cold weights, 9 MB to
+// 570 MB per call). P = pairs per row = K / 64.
+//   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
+//   P <= 32 : T = 16 x 2 chunks (Q4_0) or T = 32 (Q8_0); 1-2 rows per thread
+//   P <= 64 : T = 32 x 2 chunks
+//   P > 64  : T = 128 (a row spans two waves), looping over K in chunks of
+//             128 pairs; 4 rows per thread once N allows
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
                       hipStream_t stream)
 {
-    const int P = K / 64;  // pairs per row (K % 256 == 0, so P % 4 == 0)
-    if (P <= 4) return launch_t<FMT, 4>(x, w, y, N, P, stream);
-    if (P <= 8) return launch_t<FMT, 8>(x, w, y, N, P, stream);
-    if (P <= 16) return launch_t<FMT, 16>(x, w, y, N, P, stream);
-    if (P <= 32) return launch_t<FMT, 32>(x, w, y, N, P, stream);
-    if (P <= 64) return launch_t<FMT, 64>(x, w, y, N, P, stream);
-    if (P <= 128) return launch_t<FMT, 128>(x, w, y, N, P, stream);
-    return launch_t<FMT, 256>(x, w, y, N, P, stream);
+    const int P = K / 64;  // K % 256 == 0, so P % 4 == 0
+    if (P <= 4) return launch<FMT, 4, 2, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 8) return launch<FMT, 8, 2, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 16) return launch<FMT, 16, 2, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 32) {
+        if constexpr (FMT == FMT_Q8_0) {
+            if (N >= 65536) return launch<FMT, 32, 4, 128, 1>(x, w, y, N, P, stream);
+            return launch<FMT, 32, 2, 256, 1>(x, w, y, N, P, stream);
+        } else {
+            if (N >= 65536) return launch<FMT, 16, 2, 128, 2>(x, w, y, N, P, stream);
+            return launch<FMT, 16, 1, 256, 2>(x, w, y, N, P, stream);
+        }
+    }
+    if (P <= 64) return launch<FMT, 32, 2, 256, 2>(x, w, y, N, P, stream);
+    if (N >= 2048) return launch<FMT, 128, 4, 256, 1>(x, w, y, N, P, stream);
+    return launch<FMT, 128, 2, 256, 1>(x, w, y, N, P, stream);
 }
 
 }  // namespace
