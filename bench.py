@@ -13,9 +13,10 @@ Timing:
 * ms_per_step / value: K steps captured in one HIP graph and replayed
   between two device synchronizations (wall clock); the GPU runs the steps
   back to back.
-* per-kernel durations: an event pair recorded natively on the launch
-  stream around every launch, with the stream kept backlogged so that host
-  overhead never shows in the interval; mean / median / p10 / p90.
+* per-kernel durations: --samples launches of one kernel (cycling through
+  the cold pool) captured back to back in a HIP graph; each of 5 replays is
+  bracketed by HIP events on the launch stream; the per-launch mean
+  includes the dispatch gap between consecutive kernels.
 * the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
   vocabulary GEMV and the Q4_0 prefill GEMM, reported under "rows".
 
@@ -59,8 +60,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--samples", type=int, default=200,
-                    help="event-timed launches per kernel and shape")
+    ap.add_argument("--samples", type=int, default=100,
+                    help="back-to-back launches per timed graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bounded wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,29 +175,32 @@ def main():
         ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[i % len(w_dn)].data_ptr(),
                              y_dn.data_ptr(), 1, down["N"], down["K"], s))
 
-    filler = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
-    def backlog(ms_of_work):
-        # ~0.1 ms per pass; keeps the stream busy while the host enqueues
-        for _ in range(max(1, int(ms_of_work / 0.1))):
-            filler.zero_()
-
-    def time_launches(fn, arglists, est_us=5.0):
-        """Event pair around each launch of fn(*arglists[i], stream)."""
-        count = len(arglists)
-        ev = hip.events(2 * count)
+    def time_launches(fn, arglists, replays=5):
+        """Mean duration per launch of fn(*arglists[i], stream): the launches
+        are captured back to back in one HIP graph, and each replay is
+        bracketed by HIP events on the stream it runs on."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for a in arglists:
+                ok(fn(*a, cs))
+        g.replay()                       # warm: code objects, TLB, clocks
+        torch.cuda.synchronize()
+        ev = hip.events(2 * replays)
         rec = hip.lib.hipEventRecord
+        for r in range(replays):
+            rec(ev[2 * r], sh)
+            g.replay()
+            rec(ev[2 * r + 1], sh)
         torch.cuda.synchronize()
-        backlog(count * 0.006 + 1.0)   # host needs < 6 us per launch
-        for i in range(count):
-            rec(ev[2 * i], sh)
-            ok(fn(*arglists[i], sh))
-            rec(ev[2 * i + 1], sh)
-        torch.cuda.synchronize()
-        us = [1e3 * hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(count)]
+        per = [1e3 * hip.elapsed_ms(ev[2 * r], ev[2 * r + 1]) / len(arglists)
+               for r in range(replays)]
         for e in ev:
             hip.lib.hipEventDestroy(e)
-        return summarize(us)
+        del g
+        out = summarize(per)
+        out["launches_per_replay"] = len(arglists)
+        return out
 
     def gemv_args(x, pool_, y, m, n_, k, count):
         return [(x.data_ptr(), pool_[i % len(pool_)].data_ptr(), y.data_ptr(), m, n_, k)

@@ -3,171 +3,274 @@
 //
 // With several activation rows the f32 FMA count (M per weight) outgrows
 // the weight stream, so the contraction moves to v_mfma_f32_16x16x32_bf16:
-// one instruction covers 16 activation rows x 16 weight rows x one 32-wide
-// block. Exactness is kept where it matters:
+// one instruction covers 16 A rows x 16 weight rows x one 32-wide block.
+// Exactness is kept where it matters:
 //  * B operand (weights): the integer codes 16*(q-8) (Q4_0) or q (Q8_0),
 //    exact in bf16. The fp16 scale d is applied in f32 to the block's
-//    16x16 result, so no weight is rounded.
+//    result, so no weight is rounded.
 //  * A operand (activations): x = hi + lo with hi = bf16(x) and
-//    lo = bf16(x - hi), both round-to-nearest-even; the two products are
-//    exact and accumulate in f32. The representation error is at most
-//    2^-17 |x| per term, far inside the 1e-4 relative bound.
+//    lo = bf16(x - hi), both round-to-nearest-even; both products are exact
+//    and accumulate in f32. The representation error is at most 2^-17 |x|
+//    per term, far inside the 1e-4 relative bound. For M <= 8 (PACK) the hi
+//    rows and lo rows share one instruction (A rows m and M + m); for M > 8
+//    they take one instruction each.
 // Within a block the k order is permuted identically in A and B so that
 // each lane's eight weights come from one qs dword (Q4_0: bytes 4g..4g+3,
 // i.e. elements 4g..4g+3 and 4g+16..4g+19; Q8_0: elements 8g..8g+7).
 //
-// Work split: a workgroup owns 16 weight rows; its four waves take
-// interleaved pairs of blocks along K and are summed through LDS in a fixed
-// order (bitwise reproducible).
+// Work split: a workgroup of WAVES waves owns NT x 16 weight rows; each wave
+// takes a 256-wide slice of K (8 blocks) per pass. A wave
+//  1. loads its activation slice (M rows x 256, one float4 per lane and
+//     row, coalesced) and its weight pairs (whole 36/68-byte pairs with
+//     16-byte loads);
+//  2. writes both to its own LDS region: activations already split into
+//     hi/lo bf16 and laid out as MFMA A fragments, weight pairs re-aligned
+//     so that every qs dword is dword-aligned;
+//  3. runs, per block, one A-fragment read, one B dword and scale read per
+//     weight tile, the MFMA(s), and the f32 scale-and-accumulate.
+// No workgroup barrier is needed until the final reduction, where the
+// waves' partial sums meet in LDS in a fixed order (bitwise reproducible).
 #include "qmm_internal.h"
 
 namespace qmm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int KW = 256;             // K per wave per pass
+constexpr int BPW = KW / 32;        // blocks per wave per pass (8)
+constexpr int PPW = KW / 64;        // pairs per wave per pass (4)
 
-__device__ __forceinline__ void split8(const float4 a, const float4 b, bf16x8 &hi,
-                                       bf16x8 &lo)
-{
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)v[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(v[i] - (float)h);
-    }
-}
+template <int FMT> struct Fmt;
 
-__device__ __forceinline__ uint32_t ld32(const uint8_t *p)
-{
-    return *(const uint32_t *)p;
-}
-
-template <int FMT> struct SmallM;
-
-template <> struct SmallM<FMT_Q4_0> {
+template <> struct Fmt<FMT_Q4_0> {
     static constexpr int kPairBytes = 36;
+    static constexpr int kPairDwords = 9;     // global and LDS
     static constexpr float kOutScale = 1.0f / 16.0f;
 
-    // Lane group g of the pair starting at p: codes of block 0 and 1, scales.
-    __device__ static void load(const uint8_t *p, int g, bf16x8 &b0, bf16x8 &b1,
-                                float &d0, float &d1)
+    // global pair (9 dwords: d0 at byte 0, qs0 at 2..17, d1 at 18, qs1 at
+    // 20..35) -> LDS pair: qs0[4], qs1[4], (d0 | d1 << 16)
+    __device__ static void relayout(const uint32_t *D, uint32_t *o)
     {
-        const uint32_t q0 = __builtin_amdgcn_alignbyte(ld32(p + 4 * g + 4),
-                                                       ld32(p + 4 * g), 2);
-        const uint32_t q1 = ld32(p + 20 + 4 * g);
-        d0 = half_lo(ld32(p));
-        d1 = half_hi(ld32(p + 16));
-        const uint32_t l0 = lo16(q0), h0 = hi16(q0), l1 = lo16(q1), h1 = hi16(q1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(D[i + 1], D[i], 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 + i] = D[5 + i];
+        o[8] = (D[0] & 0xFFFFu) | (D[4] & 0xFFFF0000u);
+    }
+
+    // lane group g's eight codes of block h of an LDS pair, and the scale
+    __device__ static void b_operand(const uint32_t *pair, int h, int g, bf16x8 &b, float &d)
+    {
+        const uint32_t q = pair[4 * h + g];
+        const uint32_t dd = pair[8];
+        d = h ? half_hi(dd) : half_lo(dd);
+        const uint32_t lo = lo16(q), hi = hi16(q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            b0[e] = (__bf16)sbyte(l0, e);
-            b0[4 + e] = (__bf16)sbyte(h0, e);
-            b1[e] = (__bf16)sbyte(l1, e);
-            b1[4 + e] = (__bf16)sbyte(h1, e);
+            b[e] = (__bf16)sbyte(lo, e);
+            b[4 + e] = (__bf16)sbyte(hi, e);
         }
     }
 
-    // Element offsets (within the pair's 64 k) of lane group g's first and
-    // second four activations for block 0; block 1 adds 32.
-    __device__ static int xoff_a(int g) { return 4 * g; }
-    __device__ static int xoff_b(int g) { return 16 + 4 * g; }
+    // A-fragment position of block element kk (a multiple of 4): lane
+    // group and first of the four slots
+    __device__ static void slot(int kk, int &g, int &e0)
+    {
+        g = (kk & 15) >> 2;
+        e0 = kk < 16 ? 0 : 4;
+    }
 };
 
-template <> struct SmallM<FMT_Q8_0> {
+template <> struct Fmt<FMT_Q8_0> {
     static constexpr int kPairBytes = 68;
+    static constexpr int kPairDwords = 17;
     static constexpr float kOutScale = 1.0f;
 
-    __device__ static void load(const uint8_t *p, int g, bf16x8 &b0, bf16x8 &b1,
-                                float &d0, float &d1)
+    // global pair (17 dwords: d0 at 0, q0 at 2..33, d1 at 34, q1 at 36..67)
+    // -> LDS pair: q0[8], q1[8], (d0 | d1 << 16)
+    __device__ static void relayout(const uint32_t *D, uint32_t *o)
     {
-        const uint32_t a0 = ld32(p + 8 * g), a1 = ld32(p + 8 * g + 4),
-                       a2 = ld32(p + 8 * g + 8);
-        const uint32_t q00 = __builtin_amdgcn_alignbyte(a1, a0, 2);
-        const uint32_t q01 = __builtin_amdgcn_alignbyte(a2, a1, 2);
-        const uint32_t q10 = ld32(p + 36 + 8 * g), q11 = ld32(p + 40 + 8 * g);
-        d0 = half_lo(ld32(p));
-        d1 = half_hi(ld32(p + 32));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_alignbyte(D[i + 1], D[i], 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[8 + i] = D[9 + i];
+        o[16] = (D[0] & 0xFFFFu) | (D[8] & 0xFFFF0000u);
+    }
+
+    __device__ static void b_operand(const uint32_t *pair, int h, int g, bf16x8 &b, float &d)
+    {
+        // two dword reads: an LDS pair of 17 dwords is only dword aligned
+        const uint32_t q0 = pair[8 * h + 2 * g], q1 = pair[8 * h + 2 * g + 1];
+        const uint32_t dd = pair[16];
+        d = h ? half_hi(dd) : half_lo(dd);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            b0[e] = (__bf16)sbyte(q00, e);
-            b0[4 + e] = (__bf16)sbyte(q01, e);
-            b1[e] = (__bf16)sbyte(q10, e);
-            b1[4 + e] = (__bf16)sbyte(q11, e);
+            b[e] = (__bf16)sbyte(q0, e);
+            b[4 + e] = (__bf16)sbyte(q1, e);
         }
     }
 
-    __device__ static int xoff_a(int g) { return 8 * g; }
-    __device__ static int xoff_b(int g) { return 8 * g + 4; }
+    __device__ static void slot(int kk, int &g, int &e0)
+    {
+        g = kk >> 3;
+        e0 = kk & 7;
+    }
 };
 
-template <int FMT>
-__global__ __launch_bounds__(64 * kWaves) void gemv_small_m_kernel(
+// hi = bf16(v), lo = bf16(v - hi), both round to nearest even
+__device__ __forceinline__ void split4(const float4 v, bf16x4 &hi, bf16x4 &lo)
+{
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)f[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(f[i] - (float)h);
+    }
+}
+
+template <int FMT, bool PACK, int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int M, int N, int K)
 {
-    using L = SmallM<FMT>;
+    using L = Fmt<FMT>;
+    constexpr int TERMS = PACK ? 1 : 2;             // A operands per block
+    constexpr int MMAX = PACK ? 8 : 16;
+    constexpr int AF = BPW * TERMS * 64 * 4;        // A-fragment dwords per wave
+    constexpr int WROWS = 16 * NT;                  // weight rows per workgroup
+    constexpr int PPL = WROWS * PPW / 64;           // pairs loaded per lane
+    constexpr int WD = WROWS * PPW * L::kPairDwords;  // weight dwords per wave
+    constexpr int REGION = AF + WD;
+    static_assert(PPL * 64 == WROWS * PPW, "pairs must tile the wave");
+    static_assert(WAVES * NT * 64 * 4 <= WAVES * REGION, "reduction fits in LDS");
+    __shared__ __attribute__((aligned(16))) uint32_t lds[WAVES * REGION];
+
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int col = lane % 16, g = lane / 16;
-    const int n = blockIdx.x * 16 + col;
+    uint32_t *af = lds + wave * REGION;
+    uint32_t *wl = af + AF;
     const int P = K / 64;
     const int64_t row_bytes = (int64_t)P * L::kPairBytes;
-    // Rows past N / M read row 0 (always valid) and are never stored.
-    const uint8_t *wrow = w + (n < N ? n : 0) * row_bytes;
-    const bool mv = col < M;
-    const float *xrow = x + (int64_t)(mv ? col : 0) * K;
+    const int n0 = blockIdx.x * WROWS;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // A rows without an activation row stay zero for the whole kernel
+    for (int i = lane; i < AF; i += 64) af[i] = 0u;
+
+    // this lane's weight pairs: row lrow of the tile, local pairs lp0 + u
+    const int lrow = lane / (PPW / PPL);
+    const int lp0 = (lane % (PPW / PPL)) * PPL;
+    const uint8_t *wsrc = w + (int64_t)min(n0 + lrow, N - 1) * row_bytes;
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int p = wave; p < P; p += kWaves) {
-        bf16x8 b0, b1;
-        float d0, d1;
-        L::load(wrow + (int64_t)p * L::kPairBytes, g, b0, b1, d0, d1);
-        const float *xp = xrow + 64 * p;
-        float4 xa0 = *(const float4 *)(xp + L::xoff_a(g));
-        float4 xb0 = *(const float4 *)(xp + L::xoff_b(g));
-        float4 xa1 = *(const float4 *)(xp + 32 + L::xoff_a(g));
-        float4 xb1 = *(const float4 *)(xp + 32 + L::xoff_b(g));
-        if (!mv) {
-            xa0 = xb0 = xa1 = xb1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        bf16x8 h0, l0, h1, l1;
-        split8(xa0, xb0, h0, l0);
-        split8(xa1, xb1, h1, l1);
-        f32x4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, b0, zero, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l0, b0, c0, 0, 0, 0);
-        f32x4 c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, b1, zero, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l1, b1, c1, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] = fmaf(d0, c0[i], acc[i]);
-            acc[i] = fmaf(d1, c1[i], acc[i]);
-        }
-    }
 
-    // acc[i] is C[m = 4g + i][n]; sum the four waves in a fixed order.
-    __shared__ f32x4 red[kWaves][64];
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        f32x4 s = red[0][lane];
+    for (int k0 = wave * KW; k0 < K; k0 += WAVES * KW) {
+        // ---- 1. loads
+        float4 xv[MMAX];
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q) {
-            const f32x4 v = red[q][lane];
+        for (int m = 0; m < MMAX; ++m)
+            if (m < M) xv[m] = *reinterpret_cast<const float4 *>(x + (int64_t)m * K + k0 + 4 * lane);
+        uint32_t D[PPL][L::kPairDwords];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] += v[i];
+        for (int u = 0; u < PPL; ++u) {
+            const uint8_t *src = wsrc + (int64_t)(k0 / 64 + lp0 + u) * L::kPairBytes;
+#pragma unroll
+            for (int i = 0; i + 4 <= L::kPairDwords; i += 4) {
+                const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * i);
+                D[u][i] = v.x; D[u][i + 1] = v.y; D[u][i + 2] = v.z; D[u][i + 3] = v.w;
+            }
+            D[u][L::kPairDwords - 1] =
+                *reinterpret_cast<const uint32_t *>(src + 4 * (L::kPairDwords - 1));
         }
-        if (n < N) {
+        // ---- 2. to LDS
+        __builtin_amdgcn_wave_barrier();            // previous pass's reads done
+        {
+            const int b = lane / 8, kk = 4 * (lane % 8);
+            int g, e0;
+            L::slot(kk, g, e0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * g + i;
-                if (m < M) y[(int64_t)m * N + n] = s[i] * L::kOutScale;
+            for (int m = 0; m < MMAX; ++m) {
+                if (m < M) {
+                    bf16x4 hi, lo;
+                    split4(xv[m], hi, lo);
+                    const int rl = PACK ? M + m : m;  // A row of the lo part
+                    const int tl = PACK ? 0 : 1;      // A operand of the lo part
+                    *reinterpret_cast<bf16x4 *>(
+                        &af[((b * TERMS + 0) * 64 + 16 * g + m) * 4 + e0 / 2]) = hi;
+                    *reinterpret_cast<bf16x4 *>(
+                        &af[((b * TERMS + tl) * 64 + 16 * g + rl) * 4 + e0 / 2]) = lo;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PPL; ++u)
+            L::relayout(D[u], wl + (lrow * PPW + lp0 + u) * L::kPairDwords);
+        __builtin_amdgcn_wave_barrier();
+        // ---- 3. matrix cores
+        const int col = lane % 16, g = lane / 16;
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            bf16x8 a[TERMS];
+#pragma unroll
+            for (int tt = 0; tt < TERMS; ++tt)
+                a[tt] = *reinterpret_cast<const bf16x8 *>(&af[((b * TERMS + tt) * 64 + lane) * 4]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t *pair = wl + ((16 * t + col) * PPW + b / 2) * L::kPairDwords;
+                bf16x8 bq;
+                float d;
+                L::b_operand(pair, b & 1, g, bq, d);
+                f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], bq, zero, 0, 0, 0);
+                if constexpr (!PACK)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[TERMS - 1], bq, c, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(d, c[e], acc[t][e]);
             }
         }
     }
+
+    // acc[t][e] is C[A row 4g + e][weight row 16 t + col] of this wave; sum
+    // the waves (and, packed, A rows m and M + m) in a fixed order.
+    __syncthreads();
+    f32x4 *red = reinterpret_cast<f32x4 *>(lds);    // [WAVES][NT][64]
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 16 * WROWS; o += 64 * WAVES) {
+        const int m = o / WROWS, nl = o % WROWS;
+        const int t = nl / 16, c = nl % 16;
+        const int n = n0 + nl;
+        if (m >= M || n >= N) continue;
+        float s = 0.f;
+        for (int q = 0; q < WAVES; ++q) {
+            s += red[(q * NT + t) * 64 + 16 * (m / 4) + c][m % 4];
+            if constexpr (PACK) s += red[(q * NT + t) * 64 + 16 * ((M + m) / 4) + c][(M + m) % 4];
+        }
+        y[(int64_t)m * N + n] = s * L::kOutScale;
+    }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                      hipStream_t stream)
+{
+    if (M <= 8) {
+        constexpr int NT = 2, WAVES = 8;
+        const int grid = (N + 16 * NT - 1) / (16 * NT);
+        hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, WAVES>), dim3(grid),
+                           dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
+    } else {
+        constexpr int NT = 1, WAVES = 4;
+        const int grid = (N + 16 * NT - 1) / (16 * NT);
+        hipLaunchKernelGGL((gemv_small_m_kernel<FMT, false, NT, WAVES>), dim3(grid),
+                           dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -175,14 +278,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_m_kernel(
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream)
 {
-    const int grid = (N + 15) / 16;
-    if (fmt == FMT_Q4_0)
-        hipLaunchKernelGGL((gemv_small_m_kernel<FMT_Q4_0>), dim3(grid),
-                           dim3(64 * kWaves), 0, stream, x, w, y, M, N, K);
-    else
-        hipLaunchKernelGGL((gemv_small_m_kernel<FMT_Q8_0>), dim3(grid),
-                           dim3(64 * kWaves), 0, stream, x, w, y, M, N, K);
-    return hipGetLastError();
+    return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
+                           : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }
 
 }  // namespace qmm
