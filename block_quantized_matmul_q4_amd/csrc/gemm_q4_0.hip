@@ -11,8 +11,9 @@
 //  * dequantizes one Q4_0 block of one weight row: d * (q - 8) is exact in
 //    f32 and is rounded once to bf16 (nearest even) into LDS.
 // LDS is double buffered: the global loads of step s+1 are issued before the
-// matrix-core work of step s and land in the other buffer after it, so one
-// barrier per step suffices.
+// matrix-core work of step s, and their conversion into the other buffer is
+// placed between the later substeps' matrix-core instructions; LDS
+// fragments are prefetched one 16-wide substep ahead. One barrier per step.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the
 // eight XCDs, and consecutive tiles in band-major order (one 256-row band
@@ -94,15 +95,21 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
         b_reg[4] = *reinterpret_cast<const uint32_t *>(src + 16);
     };
 
-    auto store_step = [&](int buf) {
-        // A: f32 -> bf16 (RNE)
+    // Writes the prefetched step into LDS buffer buf, in two halves (part 0:
+    // activations, part 1: weights) so that each half can be interleaved
+    // with matrix-core work.
+    auto store_part = [&](int buf, int part) {
+        if (part == 0) {
+            // A: f32 -> bf16 (RNE)
 #pragma unroll
-        for (int u = 0; u < A_F4; ++u) {
-            const float4 v = a_reg[u];
-            uint2 pk;
-            pk.x = pack_bf16x2(v.x, v.y);
-            pk.y = pack_bf16x2(v.z, v.w);
-            *reinterpret_cast<uint2 *>(&As[buf][(tid / 16 + 32 * u) * LDK + a_col]) = pk;
+            for (int u = 0; u < A_F4; ++u) {
+                const float4 v = a_reg[u];
+                uint2 pk;
+                pk.x = pack_bf16x2(v.x, v.y);
+                pk.y = pack_bf16x2(v.z, v.w);
+                *reinterpret_cast<uint2 *>(&As[buf][(tid / 16 + 32 * u) * LDK + a_col]) = pk;
+            }
+            return;
         }
         // B: block b_blk of the pair -> bf16(d * (q - 8)) (RNE)
         uint32_t qs[4];
@@ -143,31 +150,47 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
     const int frow = lane % 32, fk = 8 * (lane / 32);
 
     load_step(0);
-    store_step(0);
+    store_part(0, 0);
+    store_part(0, 1);
     __syncthreads();
 
     for (int p = 0; p < P; ++p) {
         const int buf = p & 1;
-        if (p + 1 < P) load_step(p + 1);
+        const bool more = p + 1 < P;
+        if (more) load_step(p + 1);
         const __bf16 *as = &As[buf][(wm * WTM + frow) * LDK + fk];
         const __bf16 *bs = &Bs[buf][(wn * WTN + frow) * LDK + fk];
+        // fragments double-buffered across the four 16-wide substeps
+        bf16x8 a[2][TM], b[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            a[0][i] = *reinterpret_cast<const bf16x8 *>(as + 32 * i * LDK);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            b[0][j] = *reinterpret_cast<const bf16x8 *>(bs + 32 * j * LDK);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            bf16x8 a[TM], b[TN];
+            const int cur = s & 1;
+            if (s + 1 < BK / 16) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(as + 32 * i * LDK + 16 * s);
+                for (int i = 0; i < TM; ++i)
+                    a[cur ^ 1][i] =
+                        *reinterpret_cast<const bf16x8 *>(as + 32 * i * LDK + 16 * (s + 1));
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                b[j] = *reinterpret_cast<const bf16x8 *>(bs + 32 * j * LDK + 16 * s);
+                for (int j = 0; j < TN; ++j)
+                    b[cur ^ 1][j] =
+                        *reinterpret_cast<const bf16x8 *>(bs + 32 * j * LDK + 16 * (s + 1));
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j],
-                                                                       0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j],
+                                                                       acc[i][j], 0, 0, 0);
+            // the next step's conversions ride along the later substeps'
+            // matrix-core work (its loads have had time to land)
+            if (more && s >= 2) store_part(buf ^ 1, s - 2);
         }
-        if (p + 1 < P) store_step(buf ^ 1);
         __syncthreads();
     }
 
