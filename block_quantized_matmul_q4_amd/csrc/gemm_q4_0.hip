@@ -10,10 +10,18 @@
 //    nearest even, v_cvt_pk_bf16_f32) on their way into LDS, and
 //  * dequantizes one Q4_0 block of one weight row: d * (q - 8) is exact in
 //    f32 and is rounded once to bf16 (nearest even) into LDS.
-// LDS is double buffered: the global loads of step s+1 are issued before the
-// matrix-core work of step s, and their conversion into the other buffer is
-// placed between the later substeps' matrix-core instructions; LDS
-// fragments are prefetched one 16-wide substep ahead. One barrier per step.
+// LDS is double buffered. During step s the registers hold step s+1, which
+// is converted into the other buffer a quarter per 16-wide substep,
+// interleaved with that substep's matrix-core instructions; as soon as a
+// half (activations, weights) is written, its registers are reloaded with
+// step s+2, so each global load has most of a K step to land. LDS fragments
+// are prefetched one substep ahead. One barrier per step.
+//
+// Global traffic goes through buffer resources based at the tile's first
+// row, with the whole byte offset in the lane's offset register (the part
+// the hardware range-checks): rows past M or N fall outside the resource,
+// so they load zeros and their stores are dropped. 32-bit offsets replace
+// the 64-bit pointers a thread would otherwise keep per activation row.
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the
 // eight XCDs, and consecutive tiles in band-major order (one 256-row band
@@ -25,8 +33,8 @@ namespace qmm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WAVES_M = 2, WAVES_N = 4;
@@ -36,6 +44,8 @@ constexpr int TM = WTM / 32, TN = WTN / 32;            // 4 x 2 MFMA tiles
 constexpr int LDK = BK + 8;                            // padded LDS row (bf16)
 constexpr int kXcds = 8;
 constexpr int A_F4 = BM * BK / 4 / kThreads;           // 8 float4 per thread
+// word 3 of a raw (stride 0) buffer resource on gfx9: 32-bit data format
+constexpr int kBufferWord3 = 0x00020000;
 
 static_assert(BN * 2 == kThreads, "one Q4_0 block per thread per K step");
 
@@ -66,43 +76,57 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
     const int wave = tid / 64, lane = tid % 64;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int P = K / 64;
-    const int64_t row_bytes = (int64_t)P * 36;
+    const int row_bytes = P * 36;
 
-    // A staging: 16 threads per row (one float4 each), 32 rows per pass.
-    // Rows past M read row M-1: their outputs are never stored.
+    // Resources over the tile's rows (all sizes fit 32 bits: K <= 65536).
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + (int64_t)m0 * K), 0, a_rows * K * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, b_rows * row_bytes,
+        kBufferWord3);
+
+    // A staging: 16 threads per row (one float4 each), rows tid/16 + 32u.
+    // The row lives in the lane offset (the part of the address the
+    // hardware range-checks, whether or not it includes the uniform
+    // offset); the step's column offset goes into the uniform offset and
+    // never carries a valid row past its end.
     const int a_col = (tid % 16) * 4;
-    const float *a_src[A_F4];
+    int a_voff[A_F4];
 #pragma unroll
-    for (int u = 0; u < A_F4; ++u) {
-        const int m = min(m0 + tid / 16 + 32 * u, M - 1);
-        a_src[u] = x + (int64_t)m * K + a_col;
-    }
+    for (int u = 0; u < A_F4; ++u) a_voff[u] = ((tid / 16 + 32 * u) * K + a_col) * 4;
     // B staging: thread -> (row tid / 2, block tid % 2) of the tile; the
     // block's 18 bytes lie in the 20 bytes at pair offset 16 * blk.
     const int b_row = tid / 2, b_blk = tid % 2;
-    const uint8_t *b_src = w + (int64_t)min(n0 + b_row, N - 1) * row_bytes + 16 * b_blk;
+    const int b_voff = b_row * row_bytes + 16 * b_blk;
 
     float4 a_reg[A_F4];
     uint32_t b_reg[5];
 
-    auto load_step = [&](int p) {
+    // global -> registers for K step p: activations, weights
+    auto load_a = [&](int p) {
 #pragma unroll
-        for (int u = 0; u < A_F4; ++u)
-            a_reg[u] = *reinterpret_cast<const float4 *>(a_src[u] + 64 * p);
-        const uint8_t *src = b_src + (int64_t)p * 36;
-        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src);
+        for (int u = 0; u < A_F4; ++u) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[u], p * 256, 0);
+            a_reg[u] = __builtin_bit_cast(float4, v);
+        }
+    };
+    auto load_b = [&](int p) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_voff, p * 36, 0);
         b_reg[0] = v.x; b_reg[1] = v.y; b_reg[2] = v.z; b_reg[3] = v.w;
-        b_reg[4] = *reinterpret_cast<const uint32_t *>(src + 16);
+        b_reg[4] = __builtin_amdgcn_raw_buffer_load_b32(b_rsrc, b_voff + 16, p * 36, 0);
     };
 
-    // Writes the prefetched step into LDS buffer buf, in two halves (part 0:
-    // activations, part 1: weights) so that each half can be interleaved
-    // with matrix-core work.
-    auto store_part = [&](int buf, int part) {
-        if (part == 0) {
-            // A: f32 -> bf16 (RNE)
+    // Converts a quarter of the registers' step into LDS buffer buf, so the
+    // conversion spreads over the four substeps' matrix-core work:
+    // quarters 0, 1 are activation float4s 0-3 and 4-7 (f32 -> bf16, RNE),
+    // quarters 2, 3 are qs dwords 0-1 and 2-3 of block b_blk of the pair
+    // (-> bf16(d * (q - 8)), RNE). Selects, not branches: the loop body stays
+    // one basic block, so the waits for these registers' loads stay exact.
+    auto convert = [&](int buf, int quarter) {
+        if (quarter < 2) {
 #pragma unroll
-            for (int u = 0; u < A_F4; ++u) {
+            for (int u = 4 * quarter; u < 4 * quarter + 4; ++u) {
                 const float4 v = a_reg[u];
                 uint2 pk;
                 pk.x = pack_bf16x2(v.x, v.y);
@@ -111,24 +135,14 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
             }
             return;
         }
-        // B: block b_blk of the pair -> bf16(d * (q - 8)) (RNE)
-        uint32_t qs[4];
-        float d;
-        if (b_blk == 0) {
-            d = half_lo(b_reg[0]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qs[i] = __builtin_amdgcn_alignbyte(b_reg[i + 1], b_reg[i], 2);
-        } else {
-            d = half_hi(b_reg[0]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qs[i] = b_reg[i + 1];
-        }
+        const float d = half_lo(b_reg[0] >> (16 * b_blk));
         const float dq = d * (1.0f / 16.0f);
         __bf16 *dst = &Bs[buf][b_row * LDK + 32 * b_blk];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = lo16(qs[i]), hi = hi16(qs[i]);
+        for (int i = 2 * (quarter - 2); i < 2 * (quarter - 2) + 2; ++i) {
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b_reg[i + 1], b_reg[i], 2);
+            const uint32_t qs = b_blk ? b_reg[i + 1] : realigned;
+            const uint32_t lo = lo16(qs), hi = hi16(qs);
             uint2 l, h;
             l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
             l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
@@ -149,15 +163,18 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
 
     const int frow = lane % 32, fk = 8 * (lane / 32);
 
-    load_step(0);
-    store_part(0, 0);
-    store_part(0, 1);
+    // Steps past the last one reload (and convert) the last step, into the
+    // buffer nobody reads any more: the loop body has no branches.
+    load_a(0);
+    load_b(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) convert(0, q);
+    load_a(min(1, P - 1));
+    load_b(min(1, P - 1));
     __syncthreads();
 
     for (int p = 0; p < P; ++p) {
         const int buf = p & 1;
-        const bool more = p + 1 < P;
-        if (more) load_step(p + 1);
         const __bf16 *as = &As[buf][(wm * WTM + frow) * LDK + fk];
         const __bf16 *bs = &Bs[buf][(wn * WTN + frow) * LDK + fk];
         // fragments double-buffered across the four 16-wide substeps
@@ -168,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             b[0][j] = *reinterpret_cast<const bf16x8 *>(bs + 32 * j * LDK);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             const int cur = s & 1;
@@ -187,23 +205,47 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j],
                                                                        acc[i][j], 0, 0, 0);
-            // the next step's conversions ride along the later substeps'
-            // matrix-core work (its loads have had time to land)
-            if (more && s >= 2) store_part(buf ^ 1, s - 2);
+            // a quarter of step p+1 (in registers since most of a step ago)
+            // goes into the other buffer; once a half is written, its
+            // registers are refilled with step p+2
+            convert(buf ^ 1, s);
+            if (s == 1) load_a(min(p + 2, P - 1));
+            if (s == 3) load_b(min(p + 2, P - 1));
+            // interleave: each matrix-core instruction is followed by a few
+            // VALU instructions of the conversion and one LDS access
+#pragma unroll
+            for (int k = 0; k < TM * TN; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+                __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);       // VMEM reads
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
 
     // ---- epilogue: acc[i][j][e] = C[32i + 8(e/4) + 4(lane/32) + e%4][32j + lane%32]
+    // Columns past N get bit 31 set in their offset, which puts them outside
+    // the resource (its size, BM * N * 4 at most, is below 2^31 by the
+    // entry point's bound on N); rows past M lie outside it already. The
+    // hardware drops stores outside the resource.
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (int64_t)m0 * N, 0, a_rows * N * 4, kBufferWord3);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = n0 + wn * WTN + 32 * j + lane % 32;
+            const int r0 = wm * WTM + 32 * i + 4 * (lane / 32);
+            const uint32_t outside = n < N ? 0u : 0x80000000u;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm * WTM + 32 * i + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
-                if (m < M && n < N) y[(int64_t)m * N + n] = acc[i][j][e];
+                const int r = r0 + 8 * (e / 4) + e % 4;
+                const float v = acc[i][j][e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), y_rsrc,
+                                                      int(uint32_t((r * N + n) * 4) | outside),
+                                                      0, 0);
             }
         }
     }

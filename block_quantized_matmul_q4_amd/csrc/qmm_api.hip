@@ -108,6 +108,11 @@ QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
     const char *fn = "qmm_gemm_q4_0";
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, INT_MAX / 2);
     if (st != QMM_OK) return st;
+    // the kernel addresses a 256-row band of y with 32-bit byte offsets
+    if (N > QMM_GEMM_MAX_N || ((M + 255) / 256) * ((N + 255) / 256) > INT_MAX)
+        return fail(QMM_EUNSUPPORTED,
+                    "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
+                    (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX);
     return finish(fn, qmm::launch_gemm_q4_0(x, (const uint8_t *)w, y, (int)M, (int)N,
                                             (int)K, stream));
 }

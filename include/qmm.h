@@ -33,7 +33,9 @@
  *                    a byte size that overflows int64.
  *   QMM_EALIGN       x or w not 16-byte aligned, y not 4-byte aligned.
  *   QMM_EUNSUPPORTED K not a multiple of 256 (keeps every weight row
- *                    16-byte aligned), or K > QMM_MAX_K.
+ *                    16-byte aligned), or K > QMM_MAX_K; for qmm_gemm_q4_0
+ *                    also N > QMM_GEMM_MAX_N or more than INT32_MAX output
+ *                    tiles of 256 x 256.
  *   QMM_EHIP         the HIP runtime reported an error at launch.
  *
  * Accuracy contract, with s[m][n] = sum_k |x[m][k] * w[n][k]|:
@@ -70,6 +72,8 @@ typedef enum qmm_status {
 #define QMM_MAX_K 65536
 /* Largest M accepted by the GEMV entry points. */
 #define QMM_GEMV_MAX_M 16
+/* Largest N accepted by qmm_gemm_q4_0 (a 256-row band of y stays below 2 GiB). */
+#define QMM_GEMM_MAX_N 2097151
 
 /*
  * Decode GEMV over Q4_0 weights, 1 <= M <= 16 activation rows (M = 1 for
