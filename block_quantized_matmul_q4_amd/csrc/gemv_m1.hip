@@ -117,23 +117,26 @@ template <> struct Pair<FMT_Q8_0> {
 };
 
 // T threads per row (power of two, 4..WG), RPT rows per thread, CH chunks
-// of T pairs per pass along K, WG threads per workgroup, NT non-temporal
-// weight loads. Grid: ceil(N / (WG / T * RPT)) workgroups.
+// of T pairs per pass along K, WG threads per workgroup, SX activations
+// staged once per workgroup (else once per wave), NT non-temporal weight
+// loads. Grid: ceil(N / (WG / T * RPT)) workgroups.
 //
 // A wave owns TW = min(T, 64) consecutive pairs of each chunk for its rows
 // (a row wider than one wave is split over T / 64 waves). Per pass of CH
 // chunks along K:
-//  1. the wave loads the activations of its pairs (64 floats each) with
-//     coalesced 16-byte loads (L2-resident after the first workgroup);
+//  1. the activations of the pass's pairs (64 floats each) are loaded with
+//     coalesced 16-byte loads (L2-resident after the first workgroup): by
+//     the whole workgroup (SX) or by each wave for its own pairs;
 //  2. each thread issues the loads of all its CH * RPT weight pairs (HBM);
-//  3. the wave writes the activations to its own LDS region, in rows of 64
-//     floats padded by 4 so that consecutive lanes' 16-byte reads fall in
-//     distinct banks; no workgroup barrier is involved;
+//  3. the activations go to LDS, in rows of 64 floats padded by 4 so that
+//     consecutive lanes' 16-byte reads fall in distinct banks; SX needs one
+//     workgroup barrier here (the weights are already in flight), per-wave
+//     staging none;
 //  4. per chunk, each thread reads its 64 activations back and runs the
 //     FMAs for its RPT rows.
 // Every load is unconditional from a clamped in-bounds address: rows past N
 // are computed and dropped, pairs past P are masked by a select.
-template <int FMT, int T, int RPT, int CH, int WG, bool NT>
+template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT>
 __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int N, int P)
@@ -143,16 +146,25 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     constexpr int TW = T < 64 ? T : 64;         // pairs per wave per chunk
     constexpr int WPR = T / TW;                 // waves per row
     constexpr int XS = 68;                      // padded LDS row (floats)
-    constexpr int XF4 = 16 * TW / 64;           // float4s per lane per chunk
-    constexpr int REGION = CH * TW * XS;        // floats per wave
-    __shared__ __attribute__((aligned(16))) float xs_all[WG / 64 * REGION];
+    // staging unit: the whole workgroup for all T pairs of a chunk (SX), or
+    // one wave for its TW pairs
+    constexpr int SP = SX ? T : TW;             // pairs staged per unit and chunk
+    constexpr int ST = SX ? WG : 64;            // threads per staging unit
+    constexpr int XF4 = 16 * SP * CH / ST;      // float4s per thread per pass
+    static_assert(16 * SP * CH % ST == 0, "staging must tile the pass exactly");
+    constexpr int REGION = CH * SP * XS;        // floats per staging unit
+    constexpr int UNITS = SX ? 1 : WG / 64;
+    __shared__ __attribute__((aligned(16))) float xs_all[UNITS * REGION];
 
     const int tid = threadIdx.x;
     const int lane = tid % 64, wave = tid / 64;
     const int t = tid % T;
     const int r = tid / T;
     const int tw0 = t - lane % TW;              // first pair index of this wave
-    float *xs = xs_all + wave * REGION;
+    const int sid = SX ? tid : lane;            // thread index in its unit
+    const int sp0 = SX ? 0 : tw0;               // first pair staged by the unit
+    const int lp = SX ? t : lane % TW;          // this thread's pair in the unit
+    float *xs = xs_all + (SX ? 0 : wave * REGION);
     const int64_t row_bytes = (int64_t)P * L::kBytes;
     const int n_first = blockIdx.x * (RPAR * RPT) + r;
 
@@ -166,17 +178,15 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     for (int j = 0; j < RPT; ++j) acc[j] = 0.f;
 
     for (int c0 = 0; c0 < P; c0 += CH * T) {
-        // 1. activations of this wave's pairs in CH chunks; float4 i of a
-        //    chunk belongs to the wave's pair i / 16 (pairs clamped to P-1)
-        float4 xst[CH][XF4];
+        // 1. activations: float4 i of the unit's pass belongs to chunk
+        //    i / (16 SP), pair (i / 16) % SP of that chunk (clamped to P-1)
+        float4 xst[XF4];
 #pragma unroll
-        for (int h = 0; h < CH; ++h) {
-#pragma unroll
-            for (int u = 0; u < XF4; ++u) {
-                const int i = lane + 64 * u;
-                const int pp = min(c0 + h * T + tw0 + i / 16, P - 1);
-                xst[h][u] = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
-            }
+        for (int u = 0; u < XF4; ++u) {
+            const int i = sid + ST * u;
+            const int h = i / (16 * SP), q = (i / 16) % SP;
+            const int pp = min(c0 + h * T + sp0 + q, P - 1);
+            xst[u] = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
         }
         __builtin_amdgcn_sched_barrier(0);
         // 2. weight pairs
@@ -189,18 +199,16 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
                 L::template load<NT>(wrow[j] + (int64_t)pc * L::kBytes, D[h][j]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // 3. activations to this wave's LDS region
-        __builtin_amdgcn_wave_barrier();        // previous pass's reads done
+        // 3. activations to LDS
+        if constexpr (SX) __syncthreads();      // previous pass's readers done
+        else __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int h = 0; h < CH; ++h) {
-#pragma unroll
-            for (int u = 0; u < XF4; ++u) {
-                const int i = lane + 64 * u;
-                *reinterpret_cast<float4 *>(&xs[(h * TW + i / 16) * XS + 4 * (i % 16)]) =
-                    xst[h][u];
-            }
+        for (int u = 0; u < XF4; ++u) {
+            const int i = sid + ST * u;
+            *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) = xst[u];
         }
-        __builtin_amdgcn_wave_barrier();
+        if constexpr (SX) __syncthreads();
+        else __builtin_amdgcn_wave_barrier();
         // 4. per chunk: activations back to VGPRs, FMAs
 #pragma unroll
         for (int h = 0; h < CH; ++h) {
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float4 v = *reinterpret_cast<const float4 *>(
-                    &xs[(h * TW + lane % TW) * XS + 4 * i]);
+                    &xs[(h * SP + lp) * XS + 4 * i]);
                 xv[4 * i + 0] = v.x; xv[4 * i + 1] = v.y;
                 xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
             }
@@ -253,13 +261,14 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
 
 constexpr int kThreads = 256;
 
-template <int FMT, int T, int RPT, int WG = kThreads, int CH = 1, bool NT = false>
+template <int FMT, int T, int RPT, int WG = kThreads, int CH = 1, bool SX = false,
+          bool NT = false>
 hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
                   hipStream_t stream)
 {
     constexpr int rows_per_wg = WG / T * RPT;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, NT>), dim3(grid), dim3(WG), 0,
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, SX, NT>), dim3(grid), dim3(WG), 0,
                        stream, x, w, y, N, P);
     return hipGetLastError();
 }
@@ -267,7 +276,9 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
 // Launch shapes, from timing sweeps on MI355X (cold weights, 9 MB to
 // 570 MB per call). P = pairs per row = K / 64.
 //   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
-//   P <= 32 : T = 16 x 2 chunks (Q4_0) or T = 32 (Q8_0); 1-2 rows per thread
+//   P <= 32 : T = 16 x 2 chunks (Q4_0) or T = 32 (Q8_0); 1-2 rows per
+//             thread; the large Q8_0 case shares one activation copy per
+//             512-thread workgroup
 //   P <= 64 : T = 32 x 2 chunks
 //   P > 64  : T = 128 (a row spans two waves), looping over K in chunks of
 //             128 pairs; 4 rows per thread once N allows
@@ -281,7 +292,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
     if (P <= 16) return launch<FMT, 16, 2, 256, 1>(x, w, y, N, P, stream);
     if (P <= 32) {
         if constexpr (FMT == FMT_Q8_0) {
-            if (N >= 65536) return launch<FMT, 32, 4, 128, 1>(x, w, y, N, P, stream);
+            if (N >= 65536) return launch<FMT, 32, 2, 512, 1, true>(x, w, y, N, P, stream);
             return launch<FMT, 32, 2, 256, 1>(x, w, y, N, P, stream);
         } else {
             if (N >= 65536) return launch<FMT, 16, 2, 128, 2>(x, w, y, N, P, stream);

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     constexpr int WD = WROWS * PPW * L::kPairDwords;  // weight dwords per wave
     constexpr int REGION = AF + WD;
     static_assert(PPL * 64 == WROWS * PPW, "pairs must tile the wave");
+    static_assert(PPW % PPL == 0, "a lane's pairs lie in one weight row");
     static_assert(WAVES * NT * 64 * 4 <= WAVES * REGION, "reduction fits in LDS");
     __shared__ __attribute__((aligned(16))) uint32_t lds[WAVES * REGION];
 
@@ -265,7 +266,9 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
         hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, WAVES>), dim3(grid),
                            dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
     } else {
-        constexpr int NT = 1, WAVES = 4;
+        // 32 weight rows per workgroup, six waves over K (from a launch
+        // sweep at M = 12 and 16, K = 2048, N = 8192)
+        constexpr int NT = 2, WAVES = 6;
         const int grid = (N + 16 * NT - 1) / (16 * NT);
         hipLaunchKernelGGL((gemv_small_m_kernel<FMT, false, NT, WAVES>), dim3(grid),
                            dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);

@@ -88,6 +88,22 @@ def test_gemv_rejects_more_than_16_rows(name):
     assert "exceeds 16" in qmm.qmm_last_error()
 
 
+def header_constant(name):
+    m = re.search(rf"#define\s+{name}\s+(\d+)", HEADER.read_text())
+    return int(m.group(1))
+
+
+def test_gemm_rejects_n_past_its_bound():
+    # a 256-row band of y must stay below 2 GiB for the kernel's offsets
+    n_max = header_constant("QMM_GEMM_MAX_N")
+    assert 256 * n_max * 4 < 2**31 <= 256 * (n_max + 1) * 4
+    w_len = (n_max + 1) * (256 // 32) * 18
+    assert B + w_len < C                    # no overlap with the fake y
+    got = qmm.qmm_gemm_q4_0(A, B, C, 1, n_max + 1, 256, 0)
+    assert got == qmm.QMM_EUNSUPPORTED, qmm.qmm_last_error()
+    assert "unsupported" in qmm.qmm_last_error()
+
+
 
 
 def test_tensor_front_end_checks_types():
