@@ -273,15 +273,15 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
     return hipGetLastError();
 }
 
-// Launch shapes, from timing sweeps on MI355X (cold weights, 9 MB to
-// 570 MB per call). P = pairs per row = K / 64.
+// Launch shapes, from timing sweeps on MI355X over random weights (cold,
+// 9 MB to 570 MB per call; uniform bytes draw more power than constant
+// ones and change the ranking). P = pairs per row = K / 64.
 //   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
-//   P <= 32 : T = 16 x 2 chunks (Q4_0) or T = 32 (Q8_0); 1-2 rows per
-//             thread; the large Q8_0 case shares one activation copy per
-//             512-thread workgroup
-//   P <= 64 : T = 32 x 2 chunks
+//   P <= 32 : T = 32, one row per thread, 512-thread workgroups sharing
+//             one activation copy (Q4_0 with N >= 65536: T = 16 x 2 chunks)
+//   P <= 64 : T = 64 (Q4_0), T = 32 x 2 chunks (Q8_0)
 //   P > 64  : T = 128 (a row spans two waves), looping over K in chunks of
-//             128 pairs; 4 rows per thread once N allows
+//             128 pairs; 4 rows per thread from N = 4096, else 2
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
                       hipStream_t stream)
@@ -291,16 +291,15 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
     if (P <= 8) return launch<FMT, 8, 2, 256, 1>(x, w, y, N, P, stream);
     if (P <= 16) return launch<FMT, 16, 2, 256, 1>(x, w, y, N, P, stream);
     if (P <= 32) {
-        if constexpr (FMT == FMT_Q8_0) {
-            if (N >= 65536) return launch<FMT, 32, 2, 512, 1, true>(x, w, y, N, P, stream);
-            return launch<FMT, 32, 2, 256, 1>(x, w, y, N, P, stream);
-        } else {
-            if (N >= 65536) return launch<FMT, 16, 2, 128, 2>(x, w, y, N, P, stream);
-            return launch<FMT, 16, 1, 256, 2>(x, w, y, N, P, stream);
-        }
+        if (FMT == FMT_Q4_0 && N >= 65536)
+            return launch<FMT, 16, 1, 512, 2, true>(x, w, y, N, P, stream);
+        return launch<FMT, 32, 1, 512, 1, true>(x, w, y, N, P, stream);
     }
-    if (P <= 64) return launch<FMT, 32, 2, 256, 2>(x, w, y, N, P, stream);
-    if (N >= 2048) return launch<FMT, 128, 4, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 64) {
+        if constexpr (FMT == FMT_Q4_0) return launch<FMT, 64, 2, 256, 1>(x, w, y, N, P, stream);
+        else return launch<FMT, 32, 2, 256, 2>(x, w, y, N, P, stream);
+    }
+    if (N >= 4096) return launch<FMT, 128, 4, 256, 1>(x, w, y, N, P, stream);
     return launch<FMT, 128, 2, 256, 1>(x, w, y, N, P, stream);
 }
 

@@ -117,6 +117,7 @@ GEMV_SHAPES = [
     (1, 333, 4096), (1, 65, 16384), (1, 50, 65536), (1, 4097, 1280),
     (2, 1, 256), (3, 257, 768), (5, 1000, 2048), (7, 17, 2304), (11, 130, 512),
     (16, 33, 8192), (16, 1, 256), (13, 4100, 1024),
+    (1, 65539, 1280), (1, 4100, 8192),
 ]
 
 
