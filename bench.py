@@ -19,6 +19,10 @@ Timing:
   includes the dispatch gap between consecutive kernels.
 * the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
   vocabulary GEMV and the Q4_0 prefill GEMM, reported under "rows".
+* decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
+  at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
+  weight copy, captured in one HIP graph; 5 replays bracketed by HIP events
+  give the measured time per token (gaps between dispatches included).
 
 The CPU baseline times the f64 oracle (test infrastructure, plain C with
 OpenMP) on full decode steps for a bounded number of seconds.
@@ -286,6 +290,41 @@ def main():
         bv = wv_h.nbytes + xv_h.nbytes + yv.numel() * 4
         rows["q8_0_gemv_vocab"] = dict(tv, bytes=bv, gbs=bv / (tv["mean_us"] * 1e-6) / 1e9)
         log(f"[bench] q8 vocab: {tv['mean_us']:.2f} us")
+        # measured decode step: the 342 Q4_0 GEMVs as 171 FFN (up, down)
+        # pairs, then the Q8_0 vocabulary GEMV, back to back in one HIP graph;
+        # every GEMV reads its own pool copy (3.8 GB per step: cold HBM)
+        def decode_step(cs):
+            for layer in range(171):
+                ok(lib.qmm_gemv_q4_0(x_up.data_ptr(), w_up[layer % len(w_up)].data_ptr(),
+                                     y_up.data_ptr(), 1, up["N"], up["K"], cs))
+                ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[layer % len(w_dn)].data_ptr(),
+                                     y_dn.data_ptr(), 1, down["N"], down["K"], cs))
+            ok(lib.qmm_gemv_q8_0(xv.data_ptr(), wv[0].data_ptr(), yv.data_ptr(), 1,
+                                 voc["N"], voc["K"], cs))
+
+        g_dec = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_dec):
+            decode_step(torch.cuda.current_stream().cuda_stream)
+        g_dec.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        ev = hip.events(2 * reps)
+        for r in range(reps):
+            hip.lib.hipEventRecord(ev[2 * r], sh)
+            g_dec.replay()
+            hip.lib.hipEventRecord(ev[2 * r + 1], sh)
+        torch.cuda.synchronize()
+        per = [1e3 * hip.elapsed_ms(ev[2 * r], ev[2 * r + 1]) for r in range(reps)]
+        for e in ev:
+            hip.lib.hipEventDestroy(e)
+        del g_dec
+        td = summarize(per)
+        b_dec = 171 * bytes_step + bv
+        rows["decode_step_replay"] = dict(
+            td, dispatches=343, bytes=b_dec, gbs=b_dec / (td["mean_us"] * 1e-6) / 1e9,
+            tokens_per_s=1e6 / td["mean_us"])
+        log(f"[bench] decode step replay (343 GEMVs): {td['mean_us']:.1f} us, "
+            f"{1e6 / td['mean_us']:.0f} tok/s")
         del wv
         # Q4_0 prefill GEMM
         pre = synth.WORKLOADS["q4_0_gemm_prefill"]
