@@ -290,6 +290,19 @@ def main():
         bv = wv_h.nbytes + xv_h.nbytes + yv.numel() * 4
         rows["q8_0_gemv_vocab"] = dict(tv, bytes=bv, gbs=bv / (tv["mean_us"] * 1e-6) / 1e9)
         log(f"[bench] q8 vocab: {tv['mean_us']:.2f} us")
+        # the vocabulary head over k + 1 tokens (multi-token prediction
+        # verification, k = 1 and 3): one pass over the 570 MB for all rows
+        for m in (2, 4):
+            xm = torch.from_numpy(synth.activations(m, voc["K"])).to(dev)
+            ym = torch.empty((m, voc["N"]), device=dev)
+            t = time_launches(lib.qmm_gemv_q8_0,
+                              gemv_args(xm, wv, ym, m, voc["N"], voc["K"], max(20, n // 4)))
+            b = wv_h.nbytes + xm.numel() * 4 + ym.numel() * 4
+            rows[f"q8_0_gemv_vocab_m{m}"] = dict(
+                t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
+                tokens_per_s=m / (t["mean_us"] * 1e-6))
+            log(f"[bench] q8 vocab M={m}: {t['mean_us']:.2f} us")
+            del xm, ym
         # measured decode step: the 342 Q4_0 GEMVs as 171 FFN (up, down)
         # pairs, then the Q8_0 vocabulary GEMV, back to back in one HIP graph;
         # every GEMV reads its own pool copy (3.8 GB per step: cold HBM)

@@ -104,6 +104,13 @@ def test_gemv_q8_vocab(orc):
     check(orc, "gemv", "q8_0", 1, 262144, 2048)
 
 
+@pytest.mark.parametrize("m", [2, 4])
+def test_gemv_q8_vocab_multi_token(orc, m):
+    # k + 1 tokens through the vocabulary head (multi-token prediction
+    # verification with k = 1, 3)
+    check(orc, "gemv", "q8_0", m, 262144, 2048)
+
+
 def test_gemm_prefill(orc):
     check(orc, "gemm", "q4_0", 2048, 8192, 2048)
 
