@@ -352,6 +352,16 @@ def main():
                                          frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
                                          prefill_tokens_per_s=pre["M"] / (tp["mean_us"] * 1e-6))
         log(f"[bench] prefill GEMM: {tp['mean_us']:.2f} us, {tfl:.1f} TFLOP/s")
+        # the same prefill shape over Q8_0 weights
+        w8_h = synth.q8_0_weights(pre["N"], pre["K"])
+        w8 = pool(w8_h)
+        t8 = time_launches(lib.qmm_gemm_q8_0,
+                           gemv_args(xp, w8, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
+        tfl8 = fp / (t8["mean_us"] * 1e-6) / 1e12
+        rows["q8_0_gemm_prefill"] = dict(t8, flops=fp, tflops=tfl8,
+                                         frac_bf16_peak=tfl8 / BF16_PEAK_TFLOPS)
+        log(f"[bench] prefill GEMM Q8_0: {t8['mean_us']:.2f} us, {tfl8:.1f} TFLOP/s")
+        del w8
         # decode step model: 342 Q4_0 GEMVs (171 FFN pairs) + 1 Q8_0 GEMV
         t_step = 171 * (t_up["mean_us"] + t_dn["mean_us"]) + tv["mean_us"]
         rows["decode_tok_s_equiv"] = 1e6 / t_step

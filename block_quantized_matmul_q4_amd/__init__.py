@@ -5,10 +5,12 @@ Argument marshalling only: every step of the computation runs in the
 library's gfx950 kernels; PyTorch supplies device memory and the stream.
 
 Two layers:
-* ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0`` -- the C-ABI entry
-  points of ``include/qmm.h`` with the same names and arguments (device
-  addresses as integers, a HIP stream handle); they return the status code.
-* ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0`` -- tensor front ends that
+* ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0``, ``qmm_gemm_q8_0``
+  -- the C-ABI entry points of ``include/qmm.h`` with the same names and
+  arguments (device addresses as integers, a HIP stream handle); they return
+  the status code.
+* ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0``, ``gemm_q8_0`` -- tensor front
+  ends that
   check dtypes, shapes and devices, allocate ``y`` with torch, launch on the
   current stream and raise ``QmmError`` on a non-OK status.
 
@@ -30,8 +32,8 @@ MAX_K = 65536
 BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
 
 # Every symbol include/qmm.h declares.
-EXPORTS = ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_status_string",
-           "qmm_last_error", "qmm_version")
+EXPORTS = ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
+           "qmm_status_string", "qmm_last_error", "qmm_version")
 
 
 class QmmError(RuntimeError):
@@ -57,7 +59,7 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(str(LIBRARY))
         args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
-        for name in ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0"):
+        for name in ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0"):
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -85,6 +87,10 @@ def qmm_gemv_q8_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 
 
 def qmm_gemm_q4_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
     return library().qmm_gemm_q4_0(x, w, y, M, N, K, stream)
+
+
+def qmm_gemm_q8_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return library().qmm_gemm_q8_0(x, w, y, M, N, K, stream)
 
 
 def qmm_status_string(status: int) -> str:
@@ -157,3 +163,8 @@ def gemv_q8_0(x, w, n: int, k: int, out=None):
 def gemm_q4_0(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q4_0 W, any M."""
     return _call(qmm_gemm_q4_0, "q4_0", x, w, n, k, out)
+
+
+def gemm_q8_0(x, w, n: int, k: int, out=None):
+    """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q8_0 W, any M."""
+    return _call(qmm_gemm_q8_0, "q8_0", x, w, n, k, out)

@@ -1,5 +1,7 @@
-// Prefill GEMM over GGUF Q4_0 weights on the bf16 matrix cores:
-// y[m][n] = sum_k bf16(x[m][k]) * bf16(d * (q - 8)) with f32 accumulation.
+// Prefill GEMM over GGUF Q4_0 or Q8_0 weights on the bf16 matrix cores:
+// y[m][n] = sum_k bf16(x[m][k]) * bf16(w[n][k]) with f32 accumulation, where
+// w = d * (q - 8) (Q4_0) or d * q (Q8_0) is exact in f32 before its one
+// rounding to bf16.
 //
 // Workgroup tile BM x BN = 256 x 256, K step 64 (one pair of Q4_0 blocks per
 // weight row), 8 waves each owning a 128 x 64 sub-tile as 4 x 2 tiles of
@@ -8,8 +10,9 @@
 // Per K step every thread
 //  * converts 32 activations (8 float4, one row) from f32 to bf16 (round to
 //    nearest even, v_cvt_pk_bf16_f32) on their way into LDS, and
-//  * dequantizes one Q4_0 block of one weight row: d * (q - 8) is exact in
-//    f32 and is rounded once to bf16 (nearest even) into LDS.
+//  * dequantizes one block of one weight row: d * (q - 8) (Q4_0) or d * q
+//    (Q8_0) is exact in f32 and is rounded once to bf16 (nearest even) into
+//    LDS.
 // LDS is double buffered. During step s the registers hold step s+1, which
 // is converted into the other buffer a quarter per 16-wide substep,
 // interleaved with that substep's matrix-core instructions; as soon as a
@@ -47,7 +50,7 @@ constexpr int A_F4 = BM * BK / 4 / kThreads;           // 8 float4 per thread
 // word 3 of a raw (stride 0) buffer resource on gfx9: 32-bit data format
 constexpr int kBufferWord3 = 0x00020000;
 
-static_assert(BN * 2 == kThreads, "one Q4_0 block per thread per K step");
+static_assert(BN * 2 == kThreads, "one weight block per thread per K step");
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
@@ -58,7 +61,83 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
+// Weight staging per format. A thread owns block blk (0 or 1) of one pair
+// of a weight row per K step and loads the dword-aligned window of the pair
+// that holds it: the block's scale is the low (blk 0) or high (blk 1) half
+// of the window's first dword, and its codes start 2 bytes (blk 0) or 4
+// bytes (blk 1) into the window.
+template <int FMT> struct BFmt;
+
+template <> struct BFmt<FMT_Q4_0> {
+    static constexpr int kPairBytes = 36;
+    static constexpr int kWin = 5;          // window dwords at pair byte 16 blk
+    static constexpr int kWinStride = 16;
+
+    __device__ static void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                uint32_t (&b)[kWin])
+    {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+        b[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, 0);
+    }
+
+    // Half h of the block (qs dwords 2h, 2h+1: elements 8h..8h+7 from the
+    // low nibbles, 16+8h.. from the high ones) -> bf16(d * (q - 8)) at dst.
+    __device__ static void convert_half(const uint32_t (&b)[kWin], int blk, int h,
+                                        __bf16 *dst)
+    {
+        const float dq = half_lo(b[0] >> (16 * blk)) * (1.0f / 16.0f);
+#pragma unroll
+        for (int i = 2 * h; i < 2 * h + 2; ++i) {
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+            const uint32_t qs = blk ? b[i + 1] : realigned;
+            const uint32_t lo = lo16(qs), hi = hi16(qs);
+            uint2 l, u;
+            l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
+            l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
+            u.x = pack_bf16x2(sbyte(hi, 0) * dq, sbyte(hi, 1) * dq);
+            u.y = pack_bf16x2(sbyte(hi, 2) * dq, sbyte(hi, 3) * dq);
+            *reinterpret_cast<uint2 *>(dst + 4 * i) = l;        // elements 4i..4i+3
+            *reinterpret_cast<uint2 *>(dst + 16 + 4 * i) = u;   // elements 16+4i..
+        }
+    }
+};
+
+template <> struct BFmt<FMT_Q8_0> {
+    static constexpr int kPairBytes = 68;
+    static constexpr int kWin = 9;          // window dwords at pair byte 32 blk
+    static constexpr int kWinStride = 32;
+
+    __device__ static void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                uint32_t (&b)[kWin])
+    {
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0);
+        b[0] = v0.x; b[1] = v0.y; b[2] = v0.z; b[3] = v0.w;
+        b[4] = v1.x; b[5] = v1.y; b[6] = v1.z; b[7] = v1.w;
+        b[8] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 32, soff, 0);
+    }
+
+    // Half h of the block (q dwords 4h..4h+3: elements 16h..16h+15, element
+    // j is byte j) -> bf16(d * q) at dst.
+    __device__ static void convert_half(const uint32_t (&b)[kWin], int blk, int h,
+                                        __bf16 *dst)
+    {
+        const float d = half_lo(b[0] >> (16 * blk));
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i) {
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+            const uint32_t q = blk ? b[i + 1] : realigned;
+            uint2 v;
+            v.x = pack_bf16x2(sbyte(q, 0) * d, sbyte(q, 1) * d);
+            v.y = pack_bf16x2(sbyte(q, 2) * d, sbyte(q, 3) * d);
+            *reinterpret_cast<uint2 *>(dst + 4 * i) = v;        // elements 4i..4i+3
+        }
+    }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
     int per_xcd)
@@ -75,8 +154,9 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    using BF = BFmt<FMT>;
     const int P = K / 64;
-    const int row_bytes = P * 36;
+    const int row_bytes = P * BF::kPairBytes;
 
     // Resources over the tile's rows (all sizes fit 32 bits: K <= 65536).
     const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
@@ -95,13 +175,12 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
     int a_voff[A_F4];
 #pragma unroll
     for (int u = 0; u < A_F4; ++u) a_voff[u] = ((tid / 16 + 32 * u) * K + a_col) * 4;
-    // B staging: thread -> (row tid / 2, block tid % 2) of the tile; the
-    // block's 18 bytes lie in the 20 bytes at pair offset 16 * blk.
+    // B staging: thread -> (row tid / 2, block tid % 2) of the tile
     const int b_row = tid / 2, b_blk = tid % 2;
-    const int b_voff = b_row * row_bytes + 16 * b_blk;
+    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
 
     float4 a_reg[A_F4];
-    uint32_t b_reg[5];
+    uint32_t b_reg[BF::kWin];
 
     // global -> registers for K step p: activations, weights
     auto load_a = [&](int p) {
@@ -111,18 +190,14 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
     };
-    auto load_b = [&](int p) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_voff, p * 36, 0);
-        b_reg[0] = v.x; b_reg[1] = v.y; b_reg[2] = v.z; b_reg[3] = v.w;
-        b_reg[4] = __builtin_amdgcn_raw_buffer_load_b32(b_rsrc, b_voff + 16, p * 36, 0);
-    };
+    auto load_b = [&](int p) { BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg); };
 
     // Converts a quarter of the registers' step into LDS buffer buf, so the
     // conversion spreads over the four substeps' matrix-core work:
     // quarters 0, 1 are activation float4s 0-3 and 4-7 (f32 -> bf16, RNE),
-    // quarters 2, 3 are qs dwords 0-1 and 2-3 of block b_blk of the pair
-    // (-> bf16(d * (q - 8)), RNE). Selects, not branches: the loop body stays
-    // one basic block, so the waits for these registers' loads stay exact.
+    // quarters 2, 3 are halves 0 and 1 of block b_blk of the pair (-> bf16,
+    // RNE). Selects, not branches: the loop body stays one basic block, so
+    // the waits for these registers' loads stay exact.
     auto convert = [&](int buf, int quarter) {
         if (quarter < 2) {
 #pragma unroll
@@ -135,22 +210,7 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
             }
             return;
         }
-        const float d = half_lo(b_reg[0] >> (16 * b_blk));
-        const float dq = d * (1.0f / 16.0f);
-        __bf16 *dst = &Bs[buf][b_row * LDK + 32 * b_blk];
-#pragma unroll
-        for (int i = 2 * (quarter - 2); i < 2 * (quarter - 2) + 2; ++i) {
-            const uint32_t realigned = __builtin_amdgcn_alignbyte(b_reg[i + 1], b_reg[i], 2);
-            const uint32_t qs = b_blk ? b_reg[i + 1] : realigned;
-            const uint32_t lo = lo16(qs), hi = hi16(qs);
-            uint2 l, h;
-            l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
-            l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
-            h.x = pack_bf16x2(sbyte(hi, 0) * dq, sbyte(hi, 1) * dq);
-            h.y = pack_bf16x2(sbyte(hi, 2) * dq, sbyte(hi, 3) * dq);
-            *reinterpret_cast<uint2 *>(dst + 4 * i) = l;        // elements 4i..4i+3
-            *reinterpret_cast<uint2 *>(dst + 16 + 4 * i) = h;   // elements 16+4i..
-        }
+        BF::convert_half(b_reg, b_blk, quarter - 2, &Bs[buf][b_row * LDK + 32 * b_blk]);
     };
 
     f32x16 acc[TM][TN];
@@ -253,15 +313,19 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm_q4_0(const float *x, const uint8_t *w, float *y, int M,
-                            int N, int K, hipStream_t stream)
+hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
+                       int K, hipStream_t stream)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(gemm_q4_0_kernel, dim3(per_xcd * kXcds), dim3(kThreads), 0,
-                       stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
+    if (fmt == FMT_Q4_0)
+        hipLaunchKernelGGL(gemm_kernel<FMT_Q4_0>, dim3(per_xcd * kXcds), dim3(kThreads), 0,
+                           stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
+    else
+        hipLaunchKernelGGL(gemm_kernel<FMT_Q8_0>, dim3(per_xcd * kXcds), dim3(kThreads), 0,
+                           stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
     return hipGetLastError();
 }
 

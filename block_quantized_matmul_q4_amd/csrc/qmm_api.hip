@@ -72,6 +72,21 @@ int finish(const char *fn, hipError_t err)
     return QMM_OK;
 }
 
+int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const void *w,
+               float *y, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    int st = validate(fn, x, w, y, M, N, K, block_bytes, INT_MAX / 2);
+    if (st != QMM_OK) return st;
+    // the kernel addresses a 256-row band of y with 32-bit byte offsets
+    // (tiles rounded up to a multiple of 8 XCDs must still fit an int grid)
+    if (N > QMM_GEMM_MAX_N || ((M + 255) / 256) * ((N + 255) / 256) > INT_MAX - 8)
+        return fail(QMM_EUNSUPPORTED,
+                    "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
+                    (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX - 8);
+    return finish(fn, qmm::launch_gemm(fmt, x, (const uint8_t *)w, y, (int)M, (int)N, (int)K,
+                                       stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,16 +120,13 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
 QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream)
 {
-    const char *fn = "qmm_gemm_q4_0";
-    int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, INT_MAX / 2);
-    if (st != QMM_OK) return st;
-    // the kernel addresses a 256-row band of y with 32-bit byte offsets
-    if (N > QMM_GEMM_MAX_N || ((M + 255) / 256) * ((N + 255) / 256) > INT_MAX)
-        return fail(QMM_EUNSUPPORTED,
-                    "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
-                    (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX);
-    return finish(fn, qmm::launch_gemm_q4_0(x, (const uint8_t *)w, y, (int)M, (int)N,
-                                            (int)K, stream));
+    return gemm_entry("qmm_gemm_q4_0", qmm::FMT_Q4_0, qmm::kQ4Bytes, x, w, y, M, N, K, stream);
+}
+
+QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    return gemm_entry("qmm_gemm_q8_0", qmm::FMT_Q8_0, qmm::kQ8Bytes, x, w, y, M, N, K, stream);
 }
 
 QMM_API const char *qmm_status_string(int status)

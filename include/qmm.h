@@ -33,14 +33,14 @@
  *                    a byte size that overflows int64.
  *   QMM_EALIGN       x or w not 16-byte aligned, y not 4-byte aligned.
  *   QMM_EUNSUPPORTED K not a multiple of 256 (keeps every weight row
- *                    16-byte aligned), or K > QMM_MAX_K; for qmm_gemm_q4_0
- *                    also N > QMM_GEMM_MAX_N or more than INT32_MAX output
- *                    tiles of 256 x 256.
+ *                    16-byte aligned), or K > QMM_MAX_K; for the GEMM entry
+ *                    points also N > QMM_GEMM_MAX_N or more than
+ *                    INT32_MAX - 8 output tiles of 256 x 256.
  *   QMM_EHIP         the HIP runtime reported an error at launch.
  *
  * Accuracy contract, with s[m][n] = sum_k |x[m][k] * w[n][k]|:
  *   GEMV entry points (f32 arithmetic):  |y - y_exact| <= 1e-4 * s
- *   qmm_gemm_q4_0 (bf16 MFMA, f32 acc):   |y - y_exact| <= 8e-3 * s
+ *   qmm_gemm_q4_0, qmm_gemm_q8_0 (bf16 MFMA, f32 acc): |y - y_exact| <= 8e-3 * s
  * for finite inputs whose f32 products do not underflow. Results are
  * bitwise reproducible from call to call (no atomics, fixed reduction order).
  */
@@ -72,7 +72,7 @@ typedef enum qmm_status {
 #define QMM_MAX_K 65536
 /* Largest M accepted by the GEMV entry points. */
 #define QMM_GEMV_MAX_M 16
-/* Largest N accepted by qmm_gemm_q4_0 (a 256-row band of y stays below 2 GiB). */
+/* Largest N accepted by the GEMM entry points (a 256-row band of y stays below 2 GiB). */
 #define QMM_GEMM_MAX_N 2097151
 
 /*
@@ -98,6 +98,14 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
  * bf16 inside the kernel; products accumulate in f32 on the matrix cores.
  */
 QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Prefill GEMM over Q8_0 weights (a Q8_0 projection, e.g. the vocabulary
+ * head, over many tokens): same contract as qmm_gemm_q4_0, each weight
+ * d * q rounded once to bf16.
+ */
+QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
 
 /* Static English name of a status code ("QMM_OK", ...). */

@@ -53,6 +53,7 @@ ENTRY = {
     "qmm_gemv_q4_0": qmm.qmm_gemv_q4_0,
     "qmm_gemv_q8_0": qmm.qmm_gemv_q8_0,
     "qmm_gemm_q4_0": qmm.qmm_gemm_q4_0,
+    "qmm_gemm_q8_0": qmm.qmm_gemm_q8_0,
 }
 
 
@@ -93,15 +94,17 @@ def header_constant(name):
     return int(m.group(1))
 
 
-def test_gemm_rejects_n_past_its_bound():
+@pytest.mark.parametrize("name,block", [("qmm_gemm_q4_0", 18), ("qmm_gemm_q8_0", 34)])
+def test_gemm_rejects_n_past_its_bound(name, block):
     # a 256-row band of y must stay below 2 GiB for the kernel's offsets
     n_max = header_constant("QMM_GEMM_MAX_N")
     assert 256 * n_max * 4 < 2**31 <= 256 * (n_max + 1) * 4
-    w_len = (n_max + 1) * (256 // 32) * 18
-    assert B + w_len < C                    # no overlap with the fake y
-    got = qmm.qmm_gemm_q4_0(A, B, C, 1, n_max + 1, 256, 0)
+    w_len = (n_max + 1) * (256 // 32) * block
+    y = 0x80000000                          # fake y past the fake w
+    assert B + w_len < y
+    got = ENTRY[name](A, B, y, 1, n_max + 1, 256, 0)
     assert got == qmm.QMM_EUNSUPPORTED, qmm.qmm_last_error()
-    assert "unsupported" in qmm.qmm_last_error()
+    assert "unsupported" in qmm.qmm_last_error() and name in qmm.qmm_last_error()
 
 
 

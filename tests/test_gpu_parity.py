@@ -49,7 +49,7 @@ def run(entry, fmt, x, w, n, k):
     xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     wt = torch.from_numpy(np.ascontiguousarray(w).reshape(-1)).cuda()
     fn = {"gemv_q4_0": qmm.gemv_q4_0, "gemv_q8_0": qmm.gemv_q8_0,
-          "gemm_q4_0": qmm.gemm_q4_0}[f"{entry}_{fmt}"]
+          "gemm_q4_0": qmm.gemm_q4_0, "gemm_q8_0": qmm.gemm_q8_0}[f"{entry}_{fmt}"]
     y = fn(xt, wt, n, k)
     torch.cuda.synchronize()
     return y.cpu().numpy()
@@ -115,6 +115,11 @@ def test_gemm_prefill(orc):
     check(orc, "gemm", "q4_0", 2048, 8192, 2048)
 
 
+def test_gemm_prefill_q8_0(orc):
+    # the prefill shape over Q8_0 weights (a Q8_0 projection over many tokens)
+    check(orc, "gemm", "q8_0", 2048, 8192, 2048)
+
+
 # ---------------------------------------------------------------------------
 # Ragged and odd shapes (several tiles plus a tail)
 # ---------------------------------------------------------------------------
@@ -138,9 +143,10 @@ GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                (300, 17, 512), (256, 256, 4096), (1000, 520, 1280), (17, 2049, 256)]
 
 
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
-def test_gemm_shapes(orc, m, n, k):
-    check(orc, "gemm", "q4_0", m, n, k, seed=m + n)
+def test_gemm_shapes(orc, fmt, m, n, k):
+    check(orc, "gemm", fmt, m, n, k, seed=m + n)
 
 
 def test_q4_0_vs_q8_0_scale_distributions(orc):
@@ -173,8 +179,6 @@ def test_golden_on_gpu(orc, path, entry):
     exact values: within the contract bound, and bitwise where the exact value
     is an integer (every partial sum is then exact in f32)."""
     g = pins.load_golden(path)
-    if entry == "gemm" and g["fmt"] != "q4_0":
-        pytest.skip("the GEMM entry point is Q4_0 only")
     x, w = pad_golden(g)
     note(f"[golden] {path.name} {entry}")
     y = run(entry, g["fmt"], x, w, g["N"], 256)
@@ -187,7 +191,7 @@ def test_golden_on_gpu(orc, path, entry):
 
 @pytest.mark.parametrize("entry,fmt,m", [("gemv", "q4_0", 1), ("gemv", "q4_0", 4),
                                          ("gemv", "q8_0", 1), ("gemv", "q8_0", 16),
-                                         ("gemm", "q4_0", 64)])
+                                         ("gemm", "q4_0", 64), ("gemm", "q8_0", 70)])
 def test_one_hot_exact(orc, entry, fmt, m):
     n, k = 96, 512
     rng = np.random.default_rng(11)
@@ -204,14 +208,14 @@ def test_one_hot_exact(orc, entry, fmt, m):
     yref, _ = orc.matmul(fmt, x, w, n, k)
     if entry == "gemv":
         assert np.array_equal(y, yref.astype(np.float32).astype(np.float64))
-    else:  # bf16(d * (q - 8)) exactly
+    else:  # bf16(d * (q - 8)) or bf16(d * q) exactly
         want = torch.from_numpy(yref.astype(np.float32)).to(torch.bfloat16).float().numpy()
         assert np.array_equal(y, want.astype(np.float64))
 
 
 @pytest.mark.parametrize("entry,fmt,m", [("gemv", "q4_0", 1), ("gemv", "q4_0", 9),
                                          ("gemv", "q8_0", 1), ("gemv", "q8_0", 5),
-                                         ("gemm", "q4_0", 33)])
+                                         ("gemm", "q4_0", 33), ("gemm", "q8_0", 33)])
 def test_integer_exact(orc, entry, fmt, m):
     n, k = 200, 2048
     rng = np.random.default_rng(12)
@@ -274,7 +278,8 @@ def test_linear_in_d_bitwise():
 @pytest.mark.parametrize("entry,fmt,m,n,k", [("gemv", "q4_0", 1, 8192, 2048),
                                              ("gemv", "q4_0", 8, 8192, 2048),
                                              ("gemv", "q8_0", 1, 4096, 2048),
-                                             ("gemm", "q4_0", 512, 1024, 2048)])
+                                             ("gemm", "q4_0", 512, 1024, 2048),
+                                             ("gemm", "q8_0", 300, 700, 1024)])
 def test_bitwise_repeatable(entry, fmt, m, n, k):
     x = synth.activations(m, k, seed=21)
     w = weights(fmt, n, k, seed=21)
@@ -330,7 +335,7 @@ def test_randomized_small_shapes(orc):
     rng = np.random.default_rng(2024)
     for case in range(120):
         entry = ["gemv", "gemv", "gemm"][case % 3]
-        fmt = "q8_0" if (entry == "gemv" and case % 2) else "q4_0"
+        fmt = "q8_0" if case % 2 else "q4_0"
         m = int(rng.integers(1, 17)) if entry == "gemv" else int(rng.integers(1, 200))
         n = int(rng.integers(1, 600))
         k = 256 * int(rng.integers(1, 13))
