@@ -50,6 +50,11 @@ class Oracle:
             fn.restype = None
         lib.qmm_oracle_threads.argtypes = []
         lib.qmm_oracle_threads.restype = ctypes.c_int
+        lib.qmm_oracle_gelu_tanh.argtypes = [ctypes.c_double]
+        lib.qmm_oracle_gelu_tanh.restype = ctypes.c_double
+        lib.qmm_oracle_ffn_gate_up_q4_0.argtypes = [f32p, u8p, u8p, i64, i64, i64,
+                                                    f64p, f64p, f64p, f64p, f64p]
+        lib.qmm_oracle_ffn_gate_up_q4_0.restype = None
         self._lib = lib
 
     # -- helpers -------------------------------------------------------------
@@ -82,6 +87,23 @@ class Oracle:
             fn = self._lib.qmm_oracle_q4_0 if fmt == "q4_0" else self._lib.qmm_oracle_q8_0
             fn(x.ctypes.data, w.ctypes.data, m, n, k, y.ctypes.data, s.ctypes.data)
         return y, s
+
+    def gelu_tanh(self, g: float) -> float:
+        return self._lib.qmm_oracle_gelu_tanh(g)
+
+    def ffn_gate_up(self, x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, n: int,
+                    k: int):
+        """Gated FFN front half over Q4_0 weights: ``(h, g, u, s_g, s_u)``,
+        each ``float64[M, N]``, with h = gelu_tanh(g) * u."""
+        x, wg = self._operands("q4_0", x, w_gate, n, k)
+        _, wu = self._operands("q4_0", x, w_up, n, k)
+        m = x.shape[0]
+        out = [np.empty((m, n), dtype=np.float64) for _ in range(5)]
+        if m and n:
+            self._lib.qmm_oracle_ffn_gate_up_q4_0(
+                x.ctypes.data, wg.ctypes.data, wu.ctypes.data, m, n, k,
+                *(a.ctypes.data for a in out))
+        return tuple(out)
 
     def matmul_at(self, fmt: str, x: np.ndarray, w: np.ndarray, n: int, k: int,
                   ms, ns):

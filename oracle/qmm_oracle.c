@@ -10,6 +10,8 @@
  *   y[m][n] = sum_k x[m][k] * w[n][k],  w[n][k] = d * (q - 8)   (Q4_0)
  *                                        w[n][k] = d * q         (Q8_0)
  *   s[m][n] = sum_k |x[m][k] * w[n][k]|   (the scale of the error bound)
+ * and, for the gated FFN front half over two Q4_0 matrices,
+ *   h[m][n] = gelu_tanh(sum_k x w_gate[n][k]) * sum_k x w_up[n][k].
  * The pages ("Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3,
  * and GLiNER2", section Validation) name the two formats by their GGUF
  * names (Q4_0, Q8_0) and count their dispatches; the block layout is GGUF's:
@@ -26,6 +28,9 @@
  * summed serially in k order, so results do not depend on thread count.
  */
 #include <math.h>
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
 #include <stddef.h>
 #include <stdint.h>
 #ifdef _OPENMP
@@ -138,6 +143,35 @@ void qmm_oracle_q8_0_at(const float *x, const uint8_t *w, int64_t K,
                         double *y, double *s)
 {
     at(1, x, w, K, ms, ns, count, y, s);
+}
+
+/*
+ * Gated FFN front half (the step either side of the path: gate and up
+ * projections of one FFN read the same x, then the activation of the gate
+ * multiplies the up projection). The pages credit fused FFN paths ("Add
+ * generated quant-kernel JIT and accelerate Gemma4, BGE-M3, and GLiNER2",
+ * section Summary) without fixing an activation; the Gemma family's gated
+ * FFN uses the tanh form of GELU, taken here:
+ *   gelu(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))
+ */
+double qmm_oracle_gelu_tanh(double g)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g)));
+}
+
+/* For every (m, n): g = sum_k x[m][k] w_gate[n][k], u = the same over w_up,
+ * h = gelu(g) * u, and the two abs-sums s_g, s_u; all f64[M][N]. The sums
+ * are the plain matmul above. */
+void qmm_oracle_ffn_gate_up_q4_0(const float *x, const uint8_t *w_gate,
+                                 const uint8_t *w_up, int64_t M, int64_t N, int64_t K,
+                                 double *h, double *g, double *u, double *sg,
+                                 double *su)
+{
+    full(0, x, w_gate, M, N, K, g, sg);
+    full(0, x, w_up, M, N, K, u, su);
+    for (int64_t i = 0; i < M * N; ++i)
+        h[i] = qmm_oracle_gelu_tanh(g[i]) * u[i];
 }
 
 /* Threads an OpenMP region of this library uses (1 without OpenMP). */

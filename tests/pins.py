@@ -22,6 +22,13 @@ What each pin compares with:
 * ``permutations``     -- row permutation permutes y; a block permutation
                           along K of both W and x leaves y unchanged.
 * ``special_values``   -- Inf / NaN scales propagate as IEEE arithmetic does.
+* ``gelu_tanh_form``   -- the gate activation: gelu(0) = 0, the odd-part
+                          identity gelu(g) - gelu(-g) = g, saturation, and
+                          distance to the exact GELU g * Phi(g) (math.erf).
+* ``ffn_gate_up``      -- the gated FFN front half: its g and u equal the
+                          pinned matmul, h vanishes with g or u, and two
+                          rows with gates +g, -g over the same up row differ
+                          by exactly g * u (the odd-part identity again).
 
 The logical fields (fp16 scales and integer codes) are placed into bytes by
 ``synth.pack_q4_0`` / ``synth.pack_q8_0``; the golden fixtures spell their
@@ -280,9 +287,59 @@ def special_values(o):
     assert math.isnan(y[0, 0])
 
 
+def gelu_tanh_form(o):
+    assert o.gelu_tanh(0.0) == 0.0
+    for g in np.linspace(-7.0, 7.0, 141):
+        g = float(g)
+        a, b = o.gelu_tanh(g), o.gelu_tanh(-g)
+        # g/2 (1 + t) - (-g/2)(1 - t) = g for any odd argument of tanh
+        assert abs((a - b) - g) <= 4 * EPS64 * max(1.0, abs(g)), f"odd part at {g}"
+        exact = 0.5 * g * (1.0 + math.erf(g / math.sqrt(2.0)))
+        # the tanh form stays within a few 1e-4 of g * Phi(g)
+        assert abs(a - exact) < 1e-3, f"far from g * Phi(g) at {g}: {a} vs {exact}"
+    assert o.gelu_tanh(12.0) == 12.0 and abs(o.gelu_tanh(-12.0)) < 1e-30
+    assert 0.0 < o.gelu_tanh(0.5) < 0.5 and o.gelu_tanh(-0.5) < 0.0
+
+
+def ffn_gate_up(o, n=24, k=512, seed=10):
+    rng = np.random.default_rng(seed)
+    # rows 2i and 2i+1: gate codes mirrored around 8 (gates +g and -g under
+    # x = e_k0), up codes equal; d = 1, so g = q - 8 and u = q_up - 8 exactly
+    half = n // 2
+    qg = rng.integers(0, 16, (half, k), dtype=np.uint8)
+    qg = np.repeat(qg, 2, axis=0)
+    qg[1::2] = (16 - qg[1::2].astype(np.int64)).clip(0, 15).astype(np.uint8)
+    qu = np.repeat(rng.integers(0, 16, (half, k), dtype=np.uint8), 2, axis=0)
+    d = np.ones((n, k // 32), dtype=np.float16)
+    wg, wu = synth.pack_q4_0(d, qg), synth.pack_q4_0(d, qu)
+    k0 = int(rng.integers(0, k))
+    x = np.zeros((1, k), np.float32)
+    x[0, k0] = 1.0
+    h, g, u, sg, su = o.ffn_gate_up(x, wg, wu, n, k)
+    yg, syg = o.matmul("q4_0", x, wg, n, k)
+    yu, syu = o.matmul("q4_0", x, wu, n, k)
+    assert np.array_equal(g, yg) and np.array_equal(u, yu), "g, u are not the matmul"
+    assert np.array_equal(sg, syg) and np.array_equal(su, syu)
+    assert np.array_equal(g[0], qg[:, k0].astype(np.float64) - 8)
+    for i in range(half):
+        a, b = 2 * i, 2 * i + 1
+        if g[0, a] == -g[0, b]:               # mirrored (q = 0 has no mirror)
+            want = g[0, a] * u[0, a]
+            assert abs((h[0, a] - h[0, b]) - want) <= 8 * EPS64 * max(1.0, abs(want))
+        if g[0, a] == 0 or u[0, a] == 0:
+            assert h[0, a] == 0.0
+    # random operands: h is gelu(g) u with g, u the pinned sums
+    dg, qg2 = synth.q4_0_fields(n, k, seed=seed)
+    du, qu2 = synth.q4_0_fields(n, k, seed=seed + 1)
+    xr = synth.activations(3, k, seed=seed)
+    h2, g2, u2, _, _ = o.ffn_gate_up(xr, synth.pack_q4_0(dg, qg2), synth.pack_q4_0(du, qu2), n, k)
+    assert np.array_equal(g2, o.matmul("q4_0", xr, synth.pack_q4_0(dg, qg2), n, k)[0])
+    assert np.all(np.sign(h2[g2 > 0]) == np.sign(u2[g2 > 0]))   # gelu(g) > 0 for g > 0
+
+
 ALL = [half_decode, golden, exact_rational, library_matmul, one_hot, zero_point,
        extreme_nibbles, subnormal_scale, linear_in_d, integer_exact, q8_min,
-       permutations, special_values]
+       permutations, special_values, gelu_tanh_form, ffn_gate_up]
 
 
 def failures(o, quick=True):

@@ -38,6 +38,14 @@ MUTANTS = [
     ("x_row_ignored", "one_output(fmt, x + m * K,", "one_output(fmt, x,"),
     ("d_applied_twice", "return d * (double)(q - 8);", "return d * d * (double)(q - 8);"),
     ("f32_accumulation", "acc += t;", "acc = (float)(acc + t);"),
+    ("gelu_constant_swapped", "sqrt(2.0 / M_PI)", "sqrt(M_PI / 2.0)"),
+    ("gelu_cubic_term", "0.044715 * g * g * g", "0.44715 * g * g * g"),
+    ("gelu_half_dropped", "return 0.5 * g * (1.0 +", "return g * (1.0 +"),
+    ("gated_uses_up_twice", "full(0, x, w_gate, M, N, K, g, sg);", "full(0, x, w_up, M, N, K, g, sg);"),
+    ("gated_product_is_sum", "h[i] = qmm_oracle_gelu_tanh(g[i]) * u[i];",
+     "h[i] = qmm_oracle_gelu_tanh(g[i]) + u[i];"),
+    ("gated_activation_on_up", "h[i] = qmm_oracle_gelu_tanh(g[i]) * u[i];",
+     "h[i] = g[i] * qmm_oracle_gelu_tanh(u[i]);"),
 ]
 
 
