@@ -278,6 +278,18 @@ def main():
                 tflops=fl / (t["mean_us"] * 1e-6) / 1e12,
                 tokens_per_s=m / (t["mean_us"] * 1e-6))
             log(f"[bench] small M={m}: {t['mean_us']:.2f} us")
+        # gated FFN front half (gate + up in one launch), M = 1, the up shape;
+        # gate and up read two different cold pool copies per launch
+        hf = torch.empty((1, up["N"]), device=dev)
+        ffn_args = [(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
+                     w_up[(i + 1) % len(w_up)].data_ptr(), hf.data_ptr(), 1, up["N"], up["K"])
+                    for i in range(0, 2 * n, 2)]
+        tf = time_launches(lib.qmm_ffn_gate_up_q4_0, ffn_args)
+        bf = 2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4
+        rows["q4_0_ffn_gate_up"] = dict(tf, bytes=bf, gbs=bf / (tf["mean_us"] * 1e-6) / 1e9,
+                                        vs_two_gemv_us=2 * t_up["mean_us"])
+        log(f"[bench] ffn gate+up: {tf['mean_us']:.2f} us (two GEMVs: "
+            f"{2 * t_up['mean_us']:.2f} us)")
         # Q8_0 vocabulary GEMV
         voc = synth.WORKLOADS["q8_0_gemv_vocab"]
         xv_h, wv_h = synth.workload_inputs("q8_0_gemv_vocab")

@@ -5,14 +5,14 @@ Argument marshalling only: every step of the computation runs in the
 library's gfx950 kernels; PyTorch supplies device memory and the stream.
 
 Two layers:
-* ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0``, ``qmm_gemm_q8_0``
-  -- the C-ABI entry points of ``include/qmm.h`` with the same names and
-  arguments (device addresses as integers, a HIP stream handle); they return
-  the status code.
-* ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0``, ``gemm_q8_0`` -- tensor front
-  ends that
-  check dtypes, shapes and devices, allocate ``y`` with torch, launch on the
-  current stream and raise ``QmmError`` on a non-OK status.
+* ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0``, ``qmm_gemm_q8_0``,
+  ``qmm_ffn_gate_up_q4_0`` -- the C-ABI entry points of ``include/qmm.h``
+  with the same names and arguments (device addresses as integers, a HIP
+  stream handle); they return the status code.
+* ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0``, ``gemm_q8_0``,
+  ``ffn_gate_up_q4_0`` -- tensor front ends that check dtypes, shapes and
+  devices, allocate ``y`` with torch, launch on the current stream and raise
+  ``QmmError`` on a non-OK status.
 
 There is no fallback: if ``libqmm.so`` is missing, every call raises.
 Build it with ``python -m block_quantized_matmul_q4_amd._build``.
@@ -33,7 +33,7 @@ BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
 
 # Every symbol include/qmm.h declares.
 EXPORTS = ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
-           "qmm_status_string", "qmm_last_error", "qmm_version")
+           "qmm_ffn_gate_up_q4_0", "qmm_status_string", "qmm_last_error", "qmm_version")
 
 
 class QmmError(RuntimeError):
@@ -63,6 +63,9 @@ def library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        lib.qmm_ffn_gate_up_q4_0.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [
+            ctypes.c_void_p]
+        lib.qmm_ffn_gate_up_q4_0.restype = ctypes.c_int
         lib.qmm_status_string.argtypes = [ctypes.c_int]
         lib.qmm_status_string.restype = ctypes.c_char_p
         lib.qmm_last_error.argtypes = []
@@ -91,6 +94,11 @@ def qmm_gemm_q4_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 
 
 def qmm_gemm_q8_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
     return library().qmm_gemm_q8_0(x, w, y, M, N, K, stream)
+
+
+def qmm_ffn_gate_up_q4_0(x: int, w_gate: int, w_up: int, h: int, M: int, N: int, K: int,
+                         stream: int = 0) -> int:
+    return library().qmm_ffn_gate_up_q4_0(x, w_gate, w_up, h, M, N, K, stream)
 
 
 def qmm_status_string(status: int) -> str:
@@ -168,3 +176,20 @@ def gemm_q4_0(x, w, n: int, k: int, out=None):
 def gemm_q8_0(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q8_0 W, any M."""
     return _call(qmm_gemm_q8_0, "q8_0", x, w, n, k, out)
+
+
+def ffn_gate_up_q4_0(x, w_gate, w_up, n: int, k: int, out=None):
+    """h[1, N] = gelu_tanh(x @ W_gate^T) * (x @ W_up^T) for Q4_0 W_gate, W_up (M = 1)."""
+    import torch
+
+    if not isinstance(w_up, torch.Tensor):
+        raise TypeError("w_up must be a torch tensor")
+    if w_up.device != w_gate.device or w_up.dtype != torch.uint8 or not w_up.is_contiguous():
+        raise ValueError("w_up must be a contiguous uint8 tensor on w_gate's device")
+    if w_up.numel() != w_gate.numel():
+        raise ValueError("w_up and w_gate must have the same size")
+
+    def fn(xp, wp, yp, m, n_, k_, stream):
+        return qmm_ffn_gate_up_q4_0(xp, wp, w_up.data_ptr(), yp, m, n_, k_, stream)
+
+    return _call(fn, "q4_0", x, w_gate, n, k, out)

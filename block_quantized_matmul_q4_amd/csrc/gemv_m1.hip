@@ -121,6 +121,12 @@ template <> struct Pair<FMT_Q8_0> {
 // staged once per workgroup (else once per wave), NT non-temporal weight
 // loads. Grid: ceil(N / (WG / T * RPT)) workgroups.
 //
+// GATED (RPT = 2): the gated FFN front half. A thread's two rows are row n
+// of the gate matrix w and row n of the up matrix w2, and the output is
+// y[n] = gelu_tanh(gate) * up with gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi)
+// (g + 0.044715 g^3))), evaluated in f32 once the two sums are complete.
+// Grid: ceil(N / (WG / T)) workgroups.
+//
 // A wave owns TW = min(T, 64) consecutive pairs of each chunk for its rows
 // (a row wider than one wave is split over T / 64 waves). Per pass of CH
 // chunks along K:
@@ -136,12 +142,19 @@ template <> struct Pair<FMT_Q8_0> {
 //     FMAs for its RPT rows.
 // Every load is unconditional from a clamped in-bounds address: rows past N
 // are computed and dropped, pairs past P are masked by a select.
-template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT>
+__device__ __forceinline__ float gelu_tanh(float g)
+{
+    const float c = 0.7978845608028654f;        // sqrt(2 / pi)
+    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
+
+template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED>
 __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
-    float *__restrict__ y, int N, int P)
+    const uint8_t *__restrict__ w2, float *__restrict__ y, int N, int P)
 {
     using L = Pair<FMT>;
+    static_assert(!GATED || RPT == 2, "gated: one gate row and one up row per thread");
     constexpr int RPAR = WG / T;                // rows in flight per workgroup
     constexpr int TW = T < 64 ? T : 64;         // pairs per wave per chunk
     constexpr int WPR = T / TW;                 // waves per row
@@ -166,12 +179,16 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const int lp = SX ? t : lane % TW;          // this thread's pair in the unit
     float *xs = xs_all + (SX ? 0 : wave * REGION);
     const int64_t row_bytes = (int64_t)P * L::kBytes;
-    const int n_first = blockIdx.x * (RPAR * RPT) + r;
+    const int n_first = blockIdx.x * (RPAR * (GATED ? 1 : RPT)) + r;
 
     const uint8_t *wrow[RPT];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j)
-        wrow[j] = w + (int64_t)min(n_first + RPAR * j, N - 1) * row_bytes;
+    for (int j = 0; j < RPT; ++j) {
+        if constexpr (GATED)
+            wrow[j] = (j == 0 ? w : w2) + (int64_t)min(n_first, N - 1) * row_bytes;
+        else
+            wrow[j] = w + (int64_t)min(n_first + RPAR * j, N - 1) * row_bytes;
+    }
 
     float acc[RPT];
 #pragma unroll
@@ -232,7 +249,10 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
 #pragma unroll
     for (int j = 0; j < RPT; ++j) acc[j] = group_sum<TW>(acc[j]);
 
-    if constexpr (WPR == 1) {
+    if constexpr (WPR == 1 && GATED) {
+        if (t == T - 1 && n_first < N)
+            y[n_first] = gelu_tanh(acc[0] * L::kOutScale) * (acc[1] * L::kOutScale);
+    } else if constexpr (WPR == 1) {
         if (t == T - 1) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
@@ -248,7 +268,18 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
             for (int j = 0; j < RPT; ++j) red[wave * RPT + j] = acc[j];
         }
         __syncthreads();
-        if (tid < RPAR * RPT) {
+        if constexpr (GATED) {
+            if (tid < RPAR) {
+                float sg = 0.f, su = 0.f;
+#pragma unroll
+                for (int q = 0; q < WPR; ++q) {
+                    sg += red[(tid * WPR + q) * RPT + 0];
+                    su += red[(tid * WPR + q) * RPT + 1];
+                }
+                const int n = blockIdx.x * RPAR + tid;
+                if (n < N) y[n] = gelu_tanh(sg * L::kOutScale) * (su * L::kOutScale);
+            }
+        } else if (tid < RPAR * RPT) {
             const int rr = tid % RPAR, j = tid / RPAR;
             float s = 0.f;
 #pragma unroll
@@ -268,8 +299,19 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
 {
     constexpr int rows_per_wg = WG / T * RPT;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, SX, NT>), dim3(grid), dim3(WG), 0,
-                       stream, x, w, y, N, P);
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, SX, NT, false>), dim3(grid),
+                       dim3(WG), 0, stream, x, w, nullptr, y, N, P);
+    return hipGetLastError();
+}
+
+template <int T, int WG = kThreads, bool SX = false>
+hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, float *h, int N,
+                        int P, hipStream_t stream)
+{
+    constexpr int rows_per_wg = WG / T;
+    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT_Q4_0, T, 2, 1, WG, SX, false, true>), dim3(grid),
+                       dim3(WG), 0, stream, x, wg, wu, h, N, P);
     return hipGetLastError();
 }
 
@@ -304,6 +346,20 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
 }
 
 }  // namespace
+
+// Gated FFN front half: the M = 1 launch shapes with the thread's two rows
+// being one gate row and one up row.
+hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
+                              float *h, int N, int K, hipStream_t stream)
+{
+    const int P = K / 64;
+    if (P <= 4) return launch_gated<4>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 8) return launch_gated<8>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 16) return launch_gated<16>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 32) return launch_gated<32, 512, true>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 64) return launch_gated<64>(x, w_gate, w_up, h, N, P, stream);
+    return launch_gated<128>(x, w_gate, w_up, h, N, P, stream);
+}
 
 hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y,
                           int N, int K, hipStream_t stream)

@@ -129,6 +129,27 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
     return gemm_entry("qmm_gemm_q8_0", qmm::FMT_Q8_0, qmm::kQ8Bytes, x, w, y, M, N, K, stream);
 }
 
+QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void *w_up,
+                                 float *h, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t stream)
+{
+    const char *fn = "qmm_ffn_gate_up_q4_0";
+    int st = validate(fn, x, w_gate, h, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
+    if (st != QMM_OK) return st;
+    if (!w_up) return fail(QMM_EINVAL, "%s: null pointer (w_up)", fn);
+    if ((uintptr_t)w_up % 16)
+        return fail(QMM_EALIGN, "%s: misaligned pointer (w_up needs 16-byte alignment)", fn);
+    const uint64_t w_len = (uint64_t)N * (uint64_t)(K / 32) * (uint64_t)qmm::kQ4Bytes;
+    if (overlaps((uintptr_t)h, (uint64_t)M * (uint64_t)N * 4u, (uintptr_t)w_up, w_len))
+        return fail(QMM_EINVAL, "%s: h overlaps w_up", fn);
+    if (M != 1)
+        return fail(QMM_EUNSUPPORTED, "%s: M=%lld unsupported (one token: M must be 1)", fn,
+                    (long long)M);
+    return finish(fn, qmm::launch_ffn_gate_up(x, (const uint8_t *)w_gate,
+                                              (const uint8_t *)w_up, h, (int)N, (int)K,
+                                              stream));
+}
+
 QMM_API const char *qmm_status_string(int status)
 {
     switch (status) {

@@ -23,6 +23,8 @@ hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y,
                           int N, int K, hipStream_t stream);
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream);
+hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
+                              float *h, int N, int K, hipStream_t stream);
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream);
 

@@ -108,6 +108,25 @@ QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
 QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * Gated FFN front half over Q4_0 weights for one token (M = 1; the step
+ * either side of the path):
+ *   h[n] = gelu_tanh(g[n]) * u[n],  g = x * W_gate^T,  u = x * W_up^T,
+ *   gelu_tanh(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))).
+ * The pages ("Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3,
+ * and GLiNER2", section Summary) credit fused FFN paths without naming the
+ * activation; the tanh form of GELU is the Gemma family's. W_gate and W_up
+ * are both N rows of K/32 Q4_0 blocks (same layout as the GEMV's w); both
+ * stream in one launch that reads x once. h is f32[1][N], overwritten.
+ * Errors as above, plus QMM_EINVAL for a null or overlapping w_up,
+ * QMM_EALIGN for a w_up not 16-byte aligned, QMM_EUNSUPPORTED for M != 1.
+ * Accuracy: g and u within the GEMV bound (1e-4 of their abs-sums); the
+ * activation and product in f32.
+ */
+QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void *w_up,
+                                 float *h, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t stream);
+
 /* Static English name of a status code ("QMM_OK", ...). */
 QMM_API const char *qmm_status_string(int status);
 

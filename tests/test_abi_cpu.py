@@ -118,3 +118,20 @@ def test_tensor_front_end_checks_types():
         qmm.gemv_q4_0(x, w, 8, 256)          # CPU tensors are refused
     with pytest.raises(TypeError):
         qmm.gemv_q4_0(x.numpy(), w, 8, 256)
+
+
+@pytest.mark.parametrize("args,status,fragment", [
+    ((A, B, 0, C, 1, 8, 256), qmm.QMM_EINVAL, "null pointer (w_up)"),
+    ((A, B, B + 8 * 8 * 18 + 2, C, 1, 8, 256), qmm.QMM_EALIGN, "w_up"),
+    ((A, B, C, C + 16, 1, 8, 256), qmm.QMM_EINVAL, "overlaps w_up"),
+    ((A, B, B + 4096, C, 2, 8, 256), qmm.QMM_EUNSUPPORTED, "M must be 1"),
+    ((A, B, B + 4096, C, 17, 8, 256), qmm.QMM_EINVAL, "exceeds 16"),
+    ((0, B, B + 4096, C, 1, 8, 256), qmm.QMM_EINVAL, "null pointer"),
+    ((A, B, B + 4096, C, 1, 8, 96), qmm.QMM_EUNSUPPORTED, "unsupported"),
+    ((A, B + 2, B + 4096, C, 1, 8, 256), qmm.QMM_EALIGN, "misaligned"),
+])
+def test_ffn_gate_up_rejected_before_launch(args, status, fragment):
+    got = qmm.qmm_ffn_gate_up_q4_0(*args, 0)
+    assert got == status, (args, qmm.qmm_last_error())
+    assert fragment in qmm.qmm_last_error()
+    assert "qmm_ffn_gate_up_q4_0" in qmm.qmm_last_error()

@@ -272,6 +272,61 @@ def test_linear_in_d_bitwise():
 
 
 # ---------------------------------------------------------------------------
+# Gated FFN front half (M = 1)
+# ---------------------------------------------------------------------------
+
+GELU_SLOPE = 1.13    # max |d gelu_tanh / dg| over the reals (about 1.129)
+
+
+def ffn_bound(g, u, sg, su, h):
+    """|h - h_exact| bound: g and u within the GEMV contract (1e-4 of their
+    abs-sums), propagated through gelu(g) * u with gelu's slope <= 1.13, plus
+    f32 evaluation of the activation: 1 + tanh carries about one f32 ulp of
+    1 (times |g| / 2), and a few ulps relative to h."""
+    act = np.abs(0.5 * g * (1 + np.tanh(np.sqrt(2 / np.pi) * (g + 0.044715 * g ** 3))))
+    prop = TAU_GEMV * (GELU_SLOPE * np.abs(u) * sg + (act + TAU_GEMV * GELU_SLOPE * sg) * su)
+    return prop + 2.0 ** -20 * (np.abs(g) + 1) * np.abs(u) + 1e-5 * np.abs(h)
+
+
+def run_ffn(x, wg, wu, n, k):
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    gt = torch.from_numpy(np.ascontiguousarray(wg).reshape(-1)).cuda()
+    ut = torch.from_numpy(np.ascontiguousarray(wu).reshape(-1)).cuda()
+    h = qmm.ffn_gate_up_q4_0(xt, gt, ut, n, k)
+    torch.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k", [(8192, 2048), (1, 256), (1000, 256), (333, 512), (257, 1024),
+                                 (4097, 1280), (100, 4096), (2048, 8192), (65, 16384)])
+def test_ffn_gate_up(orc, n, k):
+    note(f"[parity] ffn_gate_up_q4_0 N={n} K={k}")
+    x = synth.activations(1, k, seed=n)
+    wg, wu = synth.q4_0_weights(n, k, seed=n), synth.q4_0_weights(n, k, seed=n + 1)
+    h = run_ffn(x, wg, wu, n, k)
+    href, g, u, sg, su = orc.ffn_gate_up(x, wg, wu, n, k)
+    err = np.abs(h.astype(np.float64) - href)
+    bound = ffn_bound(g, u, sg, su, href)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{int(bad.sum())} outputs out of bound; worst err/bound "
+                           f"{float(np.max(err / bound)):.3g}")
+
+
+def test_ffn_gate_up_exact_cases(orc):
+    n, k = 300, 1024
+    rng = np.random.default_rng(17)
+    x = synth.activations(1, k, seed=17)
+    d = pins.random_fp16(rng, (n, k // 32))
+    wu = synth.pack_q4_0(d, rng.integers(0, 16, (n, k), dtype=np.uint8))
+    note("[exact] ffn gate all-8 nibbles")
+    zero_gate = synth.pack_q4_0(d, np.full((n, k), 8, np.uint8))
+    assert np.all(run_ffn(x, zero_gate, wu, n, k) == 0.0)      # gelu(0) * u
+    note("[exact] ffn up all-8 nibbles")
+    wg = synth.pack_q4_0(d, rng.integers(0, 16, (n, k), dtype=np.uint8))
+    assert np.all(run_ffn(x, wg, zero_gate, n, k) == 0.0)      # gelu(g) * 0
+
+
+# ---------------------------------------------------------------------------
 # Determinism, streams, errors
 # ---------------------------------------------------------------------------
 
