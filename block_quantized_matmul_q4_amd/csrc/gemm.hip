@@ -39,18 +39,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WAVES_M = 2, WAVES_N = 4;
-constexpr int kThreads = 64 * WAVES_M * WAVES_N;       // 512
-constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // 128 x 64 per wave
-constexpr int TM = WTM / 32, TN = WTN / 32;            // 4 x 2 MFMA tiles
+constexpr int BK = 64;
 constexpr int LDK = BK + 8;                            // padded LDS row (bf16)
 constexpr int kXcds = 8;
-constexpr int A_F4 = BM * BK / 4 / kThreads;           // 8 float4 per thread
 // word 3 of a raw (stride 0) buffer resource on gfx9: 32-bit data format
 constexpr int kBufferWord3 = 0x00020000;
 
-static_assert(BN * 2 == kThreads, "one weight block per thread per K step");
+// Workgroup shapes: the 256 x 256 tile with 8 waves of 128 x 64, and a
+// 128 x 128 tile with 4 waves of 64 x 64 for problems with fewer 256 x 256
+// tiles than compute units (then the smaller tiles fill more of the chip).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_> struct Tile {
+    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // per wave
+    static constexpr int TM = WTM / 32, TN = WTN / 32;            // MFMA tiles per wave
+    static constexpr int A_F4 = BM * BK / 4 / kThreads;           // float4 per thread
+    static constexpr int A_ROW_STRIDE = kThreads / 16;            // rows between them
+    static_assert(BN * 2 == kThreads, "one weight block per thread per K step");
+    static_assert(A_F4 == 8, "activation float4s split into two quarters of four");
+};
+using TileLarge = Tile<256, 256, 2, 4>;
+using TileSmall = Tile<128, 128, 2, 2>;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
@@ -136,12 +145,15 @@ template <> struct BFmt<FMT_Q8_0> {
     }
 };
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+template <int FMT, class TL>
+__global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
     int per_xcd)
 {
+    constexpr int BM = TL::BM, BN = TL::BN, WAVES_N = TL::WAVES_N;
+    constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
+    constexpr int A_F4 = TL::A_F4, A_ROW_STRIDE = TL::A_ROW_STRIDE;
     __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN * LDK];
 
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, b_rows * row_bytes,
         kBufferWord3);
 
-    // A staging: 16 threads per row (one float4 each), rows tid/16 + 32u.
+    // A staging: 16 threads per row (one float4 each), rows tid/16 + A_ROW_STRIDE u.
     // The row lives in the lane offset (the part of the address the
     // hardware range-checks, whether or not it includes the uniform
     // offset); the step's column offset goes into the uniform offset and
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int a_col = (tid % 16) * 4;
     int a_voff[A_F4];
 #pragma unroll
-    for (int u = 0; u < A_F4; ++u) a_voff[u] = ((tid / 16 + 32 * u) * K + a_col) * 4;
+    for (int u = 0; u < A_F4; ++u) a_voff[u] = ((tid / 16 + A_ROW_STRIDE * u) * K + a_col) * 4;
     // B staging: thread -> (row tid / 2, block tid % 2) of the tile
     const int b_row = tid / 2, b_blk = tid % 2;
     const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
@@ -206,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                 uint2 pk;
                 pk.x = pack_bf16x2(v.x, v.y);
                 pk.y = pack_bf16x2(v.z, v.w);
-                *reinterpret_cast<uint2 *>(&As[buf][(tid / 16 + 32 * u) * LDK + a_col]) = pk;
+                *reinterpret_cast<uint2 *>(
+                    &As[buf][(tid / 16 + A_ROW_STRIDE * u) * LDK + a_col]) = pk;
             }
             return;
         }
@@ -311,22 +324,40 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
+template <int FMT, class TL>
+hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                        hipStream_t stream)
+{
+    const int tiles_m = (M + TL::BM - 1) / TL::BM;
+    const int tiles_n = (N + TL::BN - 1) / TL::BN;
+    const int tiles = tiles_m * tiles_n;
+    const int per_xcd = (tiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((gemm_kernel<FMT, TL>), dim3(per_xcd * kXcds), dim3(TL::kThreads), 0,
+                       stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
+    return hipGetLastError();
+}
+
+// MI355X has 256 compute units: with fewer 256 x 256 tiles than that, the
+// 128 x 128 tile (4 x as many workgroups) keeps more of the chip busy.
+constexpr int64_t kComputeUnits = 256;
+
+template <int FMT>
+hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                      hipStream_t stream)
+{
+    const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (large_tiles < kComputeUnits)
+        return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);
+    return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream)
 {
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int tiles = tiles_m * tiles_n;
-    const int per_xcd = (tiles + kXcds - 1) / kXcds;
-    if (fmt == FMT_Q4_0)
-        hipLaunchKernelGGL(gemm_kernel<FMT_Q4_0>, dim3(per_xcd * kXcds), dim3(kThreads), 0,
-                           stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
-    else
-        hipLaunchKernelGGL(gemm_kernel<FMT_Q8_0>, dim3(per_xcd * kXcds), dim3(kThreads), 0,
-                           stream, x, w, y, M, N, K, tiles_m, tiles_n, per_xcd);
-    return hipGetLastError();
+    return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
+                           : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }
 
 }  // namespace qmm

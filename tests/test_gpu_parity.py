@@ -149,6 +149,20 @@ def test_gemm_shapes(orc, fmt, m, n, k):
     check(orc, "gemm", fmt, m, n, k, seed=m + n)
 
 
+# Shapes with at least 256 tiles of 256 x 256 (the large-tile kernel; the
+# shapes above use the 128 x 128 one), with ragged M and N edges.
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512)])
+def test_gemm_large_tile_shapes(orc, fmt, m, n, k):
+    check(orc, "gemm", fmt, m, n, k, seed=m + n)
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 2048, 8192), (255, 8191, 1024)])
+def test_gemm_small_tile_full_k(orc, m, n, k):
+    # fewer than 256 large tiles: 128 x 128 tiles, long K and a ragged edge
+    check(orc, "gemm", "q4_0", m, n, k, seed=m + n)
+
+
 def test_q4_0_vs_q8_0_scale_distributions(orc):
     # the Q4_0 scale recipe on Q8_0 bytes and vice versa (wider/narrower d)
     w = synth.q8_0_weights(512, 2048, seed=5, sigma=0.02)
