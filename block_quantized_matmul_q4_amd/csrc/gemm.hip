@@ -8,16 +8,18 @@
 // v_mfma_f32_32x32x16_bf16 (f32 accumulators, 128 per lane).
 //
 // Per K step every thread
-//  * converts 32 activations (8 float4, one row) from f32 to bf16 (round to
-//    nearest even, v_cvt_pk_bf16_f32) on their way into LDS, and
+//  * converts 32 activations (a float4 in each of 8 rows) from f32 to bf16
+//    (round to nearest even, v_cvt_pk_bf16_f32) on their way into LDS, and
 //  * dequantizes one block of one weight row: d * (q - 8) (Q4_0) or d * q
 //    (Q8_0) is exact in f32 and is rounded once to bf16 (nearest even) into
 //    LDS.
 // LDS is double buffered. During step s the registers hold step s+1, which
-// is converted into the other buffer a quarter per 16-wide substep,
-// interleaved with that substep's matrix-core instructions; as soon as a
-// half (activations, weights) is written, its registers are reloaded with
-// step s+2, so each global load has most of a K step to land. LDS fragments
+// is converted into the other buffer a quarter per 16-wide substep (a
+// quarter of the activations and a quarter of the weight block each),
+// interleaved with that substep's matrix-core instructions. Each activation
+// quarter is reloaded with step s+2 as soon as it is written; the weight
+// window is double buffered in registers and loads step s+2 at the top of
+// step s. So every global load has most of a K step to land. LDS fragments
 // are prefetched one substep ahead. One barrier per step.
 //
 // Global traffic goes through buffer resources based at the tile's first
@@ -31,6 +33,8 @@
 // of x with all its column tiles) are given to the same XCD, so each XCD's
 // L2 holds the activation band its compute units share.
 #include "qmm_internal.h"
+
+#include <type_traits>
 
 namespace qmm {
 namespace {
@@ -56,7 +60,7 @@ template <int BM_, int BN_, int WAVES_M_, int WAVES_N_> struct Tile {
     static constexpr int A_F4 = BM * BK / 4 / kThreads;           // float4 per thread
     static constexpr int A_ROW_STRIDE = kThreads / 16;            // rows between them
     static_assert(BN * 2 == kThreads, "one weight block per thread per K step");
-    static_assert(A_F4 == 8, "activation float4s split into two quarters of four");
+    static_assert(A_F4 == 8, "activation float4s split into four quarters of two");
 };
 using TileLarge = Tile<256, 256, 2, 4>;
 using TileSmall = Tile<128, 128, 2, 2>;
@@ -90,25 +94,22 @@ template <> struct BFmt<FMT_Q4_0> {
         b[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, 0);
     }
 
-    // Half h of the block (qs dwords 2h, 2h+1: elements 8h..8h+7 from the
-    // low nibbles, 16+8h.. from the high ones) -> bf16(d * (q - 8)) at dst.
-    __device__ static void convert_half(const uint32_t (&b)[kWin], int blk, int h,
-                                        __bf16 *dst)
+    // Quarter i of the block (qs dword i: elements 4i..4i+3 from the low
+    // nibbles, 16+4i..16+4i+3 from the high ones) -> bf16(d * (q - 8)) at dst.
+    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int i,
+                                           __bf16 *dst)
     {
         const float dq = half_lo(b[0] >> (16 * blk)) * (1.0f / 16.0f);
-#pragma unroll
-        for (int i = 2 * h; i < 2 * h + 2; ++i) {
-            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
-            const uint32_t qs = blk ? b[i + 1] : realigned;
-            const uint32_t lo = lo16(qs), hi = hi16(qs);
-            uint2 l, u;
-            l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
-            l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
-            u.x = pack_bf16x2(sbyte(hi, 0) * dq, sbyte(hi, 1) * dq);
-            u.y = pack_bf16x2(sbyte(hi, 2) * dq, sbyte(hi, 3) * dq);
-            *reinterpret_cast<uint2 *>(dst + 4 * i) = l;        // elements 4i..4i+3
-            *reinterpret_cast<uint2 *>(dst + 16 + 4 * i) = u;   // elements 16+4i..
-        }
+        const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+        const uint32_t qs = blk ? b[i + 1] : realigned;
+        const uint32_t lo = lo16(qs), hi = hi16(qs);
+        uint2 l, u;
+        l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
+        l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
+        u.x = pack_bf16x2(sbyte(hi, 0) * dq, sbyte(hi, 1) * dq);
+        u.y = pack_bf16x2(sbyte(hi, 2) * dq, sbyte(hi, 3) * dq);
+        *reinterpret_cast<uint2 *>(dst + 4 * i) = l;        // elements 4i..4i+3
+        *reinterpret_cast<uint2 *>(dst + 16 + 4 * i) = u;   // elements 16+4i..
     }
 };
 
@@ -127,14 +128,14 @@ template <> struct BFmt<FMT_Q8_0> {
         b[8] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 32, soff, 0);
     }
 
-    // Half h of the block (q dwords 4h..4h+3: elements 16h..16h+15, element
+    // Quarter h of the block (q dwords 2h, 2h+1: elements 8h..8h+7, element
     // j is byte j) -> bf16(d * q) at dst.
-    __device__ static void convert_half(const uint32_t (&b)[kWin], int blk, int h,
-                                        __bf16 *dst)
+    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int h,
+                                           __bf16 *dst)
     {
         const float d = half_lo(b[0] >> (16 * blk));
 #pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i) {
+        for (int i = 2 * h; i < 2 * h + 2; ++i) {
             const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
             const uint32_t q = blk ? b[i + 1] : realigned;
             uint2 v;
@@ -192,38 +193,35 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
 
     float4 a_reg[A_F4];
-    uint32_t b_reg[BF::kWin];
+    uint32_t b_reg[2][BF::kWin];    // weight windows of two consecutive steps
 
-    // global -> registers for K step p: activations, weights
-    auto load_a = [&](int p) {
+    // global -> registers for K step p: activation quarter q (float4s 2q,
+    // 2q+1), weight window
+    auto load_a = [&](int p, int q) {
 #pragma unroll
-        for (int u = 0; u < A_F4; ++u) {
+        for (int u = 2 * q; u < 2 * q + 2; ++u) {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[u], p * 256, 0);
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
     };
-    auto load_b = [&](int p) { BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg); };
+    auto load_b = [&](uint32_t (&b)[BF::kWin], int p) {
+        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b);
+    };
 
-    // Converts a quarter of the registers' step into LDS buffer buf, so the
-    // conversion spreads over the four substeps' matrix-core work:
-    // quarters 0, 1 are activation float4s 0-3 and 4-7 (f32 -> bf16, RNE),
-    // quarters 2, 3 are halves 0 and 1 of block b_blk of the pair (-> bf16,
-    // RNE). Selects, not branches: the loop body stays one basic block, so
-    // the waits for these registers' loads stay exact.
-    auto convert = [&](int buf, int quarter) {
-        if (quarter < 2) {
+    // Converts quarter q of a step into LDS buffer buf: activation float4s
+    // 2q, 2q+1 (f32 -> bf16, RNE) and quarter q of weight block b_blk (->
+    // bf16, RNE), so each of the four substeps' matrix-core work hides the
+    // same share of the conversion.
+    auto convert = [&](int buf, int q, const uint32_t (&b)[BF::kWin]) {
 #pragma unroll
-            for (int u = 4 * quarter; u < 4 * quarter + 4; ++u) {
-                const float4 v = a_reg[u];
-                uint2 pk;
-                pk.x = pack_bf16x2(v.x, v.y);
-                pk.y = pack_bf16x2(v.z, v.w);
-                *reinterpret_cast<uint2 *>(
-                    &As[buf][(tid / 16 + A_ROW_STRIDE * u) * LDK + a_col]) = pk;
-            }
-            return;
+        for (int u = 2 * q; u < 2 * q + 2; ++u) {
+            const float4 v = a_reg[u];
+            uint2 pk;
+            pk.x = pack_bf16x2(v.x, v.y);
+            pk.y = pack_bf16x2(v.z, v.w);
+            *reinterpret_cast<uint2 *>(&As[buf][(tid / 16 + A_ROW_STRIDE * u) * LDK + a_col]) = pk;
         }
-        BF::convert_half(b_reg, b_blk, quarter - 2, &Bs[buf][b_row * LDK + 32 * b_blk]);
+        BF::convert_quarter(b, b_blk, q, &Bs[buf][b_row * LDK + 32 * b_blk]);
     };
 
     f32x16 acc[TM][TN];
@@ -237,19 +235,28 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     const int frow = lane % 32, fk = 8 * (lane / 32);
 
     // Steps past the last one reload (and convert) the last step, into the
-    // buffer nobody reads any more: the loop body has no branches.
-    load_a(0);
-    load_b(0);
+    // buffer nobody reads any more: the loop body has no branches, so the
+    // waits for the registers' loads stay exact.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) convert(0, q);
-    load_a(min(1, P - 1));
-    load_b(min(1, P - 1));
+    for (int q = 0; q < 4; ++q) load_a(0, q);
+    load_b(b_reg[0], 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) convert(0, q, b_reg[0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_a(min(1, P - 1), q);
+    load_b(b_reg[1], min(1, P - 1));
     __syncthreads();
 
-    for (int p = 0; p < P; ++p) {
-        const int buf = p & 1;
-        const __bf16 *as = &As[buf][(wm * WTM + frow) * LDK + fk];
-        const __bf16 *bs = &Bs[buf][(wn * WTN + frow) * LDK + fk];
+    // K step p out of LDS buffer PAR = p % 2. On entry the registers hold
+    // step p+1 (weights in b_reg[PAR ^ 1]); b_reg[PAR] is free and takes
+    // step p+2 at once, and each activation quarter is refilled with step
+    // p+2 right after it is converted.
+    auto step = [&](int p, auto par) {
+        constexpr int PAR = decltype(par)::value;
+        const int p2 = min(p + 2, P - 1);
+        load_b(b_reg[PAR], p2);
+        const __bf16 *as = &As[PAR][(wm * WTM + frow) * LDK + fk];
+        const __bf16 *bs = &Bs[PAR][(wn * WTN + frow) * LDK + fk];
         // fragments double-buffered across the four 16-wide substeps
         bf16x8 a[2][TM], b[2][TN];
 #pragma unroll
@@ -278,12 +285,8 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j],
                                                                        acc[i][j], 0, 0, 0);
-            // a quarter of step p+1 (in registers since most of a step ago)
-            // goes into the other buffer; once a half is written, its
-            // registers are refilled with step p+2
-            convert(buf ^ 1, s);
-            if (s == 1) load_a(min(p + 2, P - 1));
-            if (s == 3) load_b(min(p + 2, P - 1));
+            convert(PAR ^ 1, s, b_reg[PAR ^ 1]);
+            load_a(p2, s);
             // interleave: each matrix-core instruction is followed by a few
             // VALU instructions of the conversion and one LDS access
 #pragma unroll
@@ -296,6 +299,12 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
+    };
+    // two steps per iteration (the weight registers and the LDS buffers
+    // alternate with the step's parity); P is even, K being a multiple of 256
+    for (int p = 0; p < P; p += 2) {
+        step(p, std::integral_constant<int, 0>());
+        step(p + 1, std::integral_constant<int, 1>());
     }
 
     // ---- epilogue: acc[i][j][e] = C[32i + 8(e/4) + 4(lane/32) + e%4][32j + lane%32]
@@ -328,6 +337,8 @@ template <int FMT, class TL>
 hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                         hipStream_t stream)
 {
+    // the kernel runs K steps of 64 in pairs
+    if (K % (2 * BK) != 0) return hipErrorInvalidValue;
     const int tiles_m = (M + TL::BM - 1) / TL::BM;
     const int tiles_n = (N + TL::BN - 1) / TL::BN;
     const int tiles = tiles_m * tiles_n;
