@@ -94,22 +94,26 @@ template <> struct BFmt<FMT_Q4_0> {
         b[4] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 16, soff, 0);
     }
 
-    // Quarter i of the block (qs dword i: elements 4i..4i+3 from the low
-    // nibbles, 16+4i..16+4i+3 from the high ones) -> bf16(d * (q - 8)) at dst.
-    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int i,
+    // Quarter q of the block: the low (q = 0, 1) or high (q = 2, 3) nibbles
+    // of qs dwords 2h, 2h+1 with h = q % 2, i.e. elements 16 (q / 2) + 8h ..
+    // +7 -> bf16(d * (q - 8)), one 16-byte LDS store at dst.
+    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int q,
                                            __bf16 *dst)
     {
         const float dq = half_lo(b[0] >> (16 * blk)) * (1.0f / 16.0f);
-        const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
-        const uint32_t qs = blk ? b[i + 1] : realigned;
-        const uint32_t lo = lo16(qs), hi = hi16(qs);
-        uint2 l, u;
-        l.x = pack_bf16x2(sbyte(lo, 0) * dq, sbyte(lo, 1) * dq);
-        l.y = pack_bf16x2(sbyte(lo, 2) * dq, sbyte(lo, 3) * dq);
-        u.x = pack_bf16x2(sbyte(hi, 0) * dq, sbyte(hi, 1) * dq);
-        u.y = pack_bf16x2(sbyte(hi, 2) * dq, sbyte(hi, 3) * dq);
-        *reinterpret_cast<uint2 *>(dst + 4 * i) = l;        // elements 4i..4i+3
-        *reinterpret_cast<uint2 *>(dst + 16 + 4 * i) = u;   // elements 16+4i..
+        const int h = q % 2, nib = q / 2;
+        uint4 v;
+        uint32_t *o = &v.x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i = 2 * h + t;
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+            const uint32_t qs = blk ? b[i + 1] : realigned;
+            const uint32_t s = nib ? hi16(qs) : lo16(qs);
+            o[2 * t] = pack_bf16x2(sbyte(s, 0) * dq, sbyte(s, 1) * dq);
+            o[2 * t + 1] = pack_bf16x2(sbyte(s, 2) * dq, sbyte(s, 3) * dq);
+        }
+        *reinterpret_cast<uint4 *>(dst + 16 * nib + 8 * h) = v;
     }
 };
 
@@ -129,20 +133,22 @@ template <> struct BFmt<FMT_Q8_0> {
     }
 
     // Quarter h of the block (q dwords 2h, 2h+1: elements 8h..8h+7, element
-    // j is byte j) -> bf16(d * q) at dst.
+    // j is byte j) -> bf16(d * q), one 16-byte LDS store at dst.
     __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int h,
                                            __bf16 *dst)
     {
         const float d = half_lo(b[0] >> (16 * blk));
+        uint4 v;
+        uint32_t *o = &v.x;
 #pragma unroll
-        for (int i = 2 * h; i < 2 * h + 2; ++i) {
+        for (int t = 0; t < 2; ++t) {
+            const int i = 2 * h + t;
             const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
             const uint32_t q = blk ? b[i + 1] : realigned;
-            uint2 v;
-            v.x = pack_bf16x2(sbyte(q, 0) * d, sbyte(q, 1) * d);
-            v.y = pack_bf16x2(sbyte(q, 2) * d, sbyte(q, 3) * d);
-            *reinterpret_cast<uint2 *>(dst + 4 * i) = v;        // elements 4i..4i+3
+            o[2 * t] = pack_bf16x2(sbyte(q, 0) * d, sbyte(q, 1) * d);
+            o[2 * t + 1] = pack_bf16x2(sbyte(q, 2) * d, sbyte(q, 3) * d);
         }
+        *reinterpret_cast<uint4 *>(dst + 8 * h) = v;
     }
 };
 

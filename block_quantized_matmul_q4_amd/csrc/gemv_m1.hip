@@ -197,13 +197,16 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     for (int c0 = 0; c0 < P; c0 += CH * T) {
         // 1. activations: float4 i of the unit's pass belongs to chunk
         //    i / (16 SP), pair (i / 16) % SP of that chunk (clamped to P-1)
-        float4 xst[XF4];
+        // (four scalar arrays, not one of float4: the float4 array ends up in
+        // scratch memory once XF4 >= 4 with workgroup-wide staging)
+        float xsx[XF4], xsy[XF4], xsz[XF4], xsw[XF4];
 #pragma unroll
         for (int u = 0; u < XF4; ++u) {
             const int i = sid + ST * u;
             const int h = i / (16 * SP), q = (i / 16) % SP;
             const int pp = min(c0 + h * T + sp0 + q, P - 1);
-            xst[u] = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
+            const float4 v = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
+            xsx[u] = v.x; xsy[u] = v.y; xsz[u] = v.z; xsw[u] = v.w;
         }
         __builtin_amdgcn_sched_barrier(0);
         // 2. weight pairs
@@ -222,7 +225,8 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
 #pragma unroll
         for (int u = 0; u < XF4; ++u) {
             const int i = sid + ST * u;
-            *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) = xst[u];
+            *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) =
+                make_float4(xsx[u], xsy[u], xsz[u], xsw[u]);
         }
         if constexpr (SX) __syncthreads();
         else __builtin_amdgcn_wave_barrier();
@@ -319,11 +323,14 @@ hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, fl
 // 9 MB to 570 MB per call; uniform bytes draw more power than constant
 // ones and change the ranking). P = pairs per row = K / 64.
 //   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
-//   P <= 32 : T = 32, one row per thread, 512-thread workgroups sharing
-//             one activation copy (Q4_0 with N >= 65536: T = 16 x 2 chunks)
-//   P <= 64 : T = 64 (Q4_0), T = 32 x 2 chunks (Q8_0)
-//   P > 64  : T = 128 (a row spans two waves), looping over K in chunks of
-//             128 pairs; 4 rows per thread from N = 4096, else 2
+//   P <= 32 : T = 32, one row per thread, workgroups sharing one
+//             activation copy: 512 threads from N = 65536, else 256
+//   P <= 64 : T = 64, one row per thread, 512-thread workgroups sharing one
+//             activation copy
+//   P > 64  : T = 128 (a row spans two waves), one row per thread, looping
+//             over K in chunks of 128 pairs, workgroups sharing one
+//             activation copy: 1024 threads (8 rows) from N = 4096 (Q4_0)
+//             or N = 2048 (Q8_0), else 512 (4 rows)
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
                       hipStream_t stream)
@@ -333,22 +340,20 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
     if (P <= 8) return launch<FMT, 8, 2, 256, 1>(x, w, y, N, P, stream);
     if (P <= 16) return launch<FMT, 16, 2, 256, 1>(x, w, y, N, P, stream);
     if (P <= 32) {
-        if (FMT == FMT_Q4_0 && N >= 65536)
-            return launch<FMT, 16, 1, 512, 2, true>(x, w, y, N, P, stream);
-        return launch<FMT, 32, 1, 512, 1, true>(x, w, y, N, P, stream);
+        if (N >= 65536) return launch<FMT, 32, 1, 512, 1, true>(x, w, y, N, P, stream);
+        return launch<FMT, 32, 1, 256, 1, true>(x, w, y, N, P, stream);
     }
-    if (P <= 64) {
-        if constexpr (FMT == FMT_Q4_0) return launch<FMT, 64, 2, 256, 1>(x, w, y, N, P, stream);
-        else return launch<FMT, 32, 2, 256, 2>(x, w, y, N, P, stream);
-    }
-    if (N >= 4096) return launch<FMT, 128, 4, 256, 1>(x, w, y, N, P, stream);
-    return launch<FMT, 128, 2, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 64) return launch<FMT, 64, 1, 512, 1, true>(x, w, y, N, P, stream);
+    if (N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
+        return launch<FMT, 128, 1, 1024, 1, true>(x, w, y, N, P, stream);
+    return launch<FMT, 128, 1, 512, 1, true>(x, w, y, N, P, stream);
 }
 
 }  // namespace
 
-// Gated FFN front half: the M = 1 launch shapes with the thread's two rows
-// being one gate row and one up row.
+// Gated FFN front half: a thread's two rows are one gate row and one up
+// row; from P = 32 on, workgroups share one activation copy (timing sweeps
+// as above).
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                               float *h, int N, int K, hipStream_t stream)
 {
@@ -356,9 +361,9 @@ hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8
     if (P <= 4) return launch_gated<4>(x, w_gate, w_up, h, N, P, stream);
     if (P <= 8) return launch_gated<8>(x, w_gate, w_up, h, N, P, stream);
     if (P <= 16) return launch_gated<16>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 32) return launch_gated<32, 512, true>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 64) return launch_gated<64>(x, w_gate, w_up, h, N, P, stream);
-    return launch_gated<128>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 32) return launch_gated<32, 256, true>(x, w_gate, w_up, h, N, P, stream);
+    if (P <= 64 || N >= 8192) return launch_gated<64, 512, true>(x, w_gate, w_up, h, N, P, stream);
+    return launch_gated<128, 512, true>(x, w_gate, w_up, h, N, P, stream);
 }
 
 hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y,

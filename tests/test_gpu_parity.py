@@ -129,7 +129,7 @@ GEMV_SHAPES = [
     (1, 333, 4096), (1, 65, 16384), (1, 50, 65536), (1, 4097, 1280),
     (2, 1, 256), (3, 257, 768), (5, 1000, 2048), (7, 17, 2304), (11, 130, 512),
     (16, 33, 8192), (16, 1, 256), (13, 4100, 1024),
-    (1, 65539, 1280), (1, 4100, 8192),
+    (1, 65539, 1280), (1, 4100, 8192), (1, 4099, 8448), (1, 2049, 4352),
 ]
 
 
@@ -312,7 +312,8 @@ def run_ffn(x, wg, wu, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(8192, 2048), (1, 256), (1000, 256), (333, 512), (257, 1024),
-                                 (4097, 1280), (100, 4096), (2048, 8192), (65, 16384)])
+                                 (4097, 1280), (100, 4096), (2048, 8192), (65, 16384),
+                                 (8200, 4352)])
 def test_ffn_gate_up(orc, n, k):
     note(f"[parity] ffn_gate_up_q4_0 N={n} K={k}")
     x = synth.activations(1, k, seed=n)
