@@ -79,6 +79,47 @@ template <> struct Pair<FMT_Q4_0> {
         acc = fmaf(half_hi(D[4]), s1, acc);
         return acc;
     }
+
+    // The codes of a pair as floats, 16(q-8) in element order, for reuse
+    // over several activation rows.
+    __device__ static void decode(const uint32_t (&D)[kDwords], float (&wv)[64])
+    {
+#pragma unroll
+        for (int pb = 2; pb < 18; ++pb) {
+            const uint32_t v = D[pb >> 2];
+            wv[pb - 2] = sbyte(lo16(v), pb & 3);
+            wv[pb - 2 + 16] = sbyte(hi16(v), pb & 3);
+        }
+#pragma unroll
+        for (int pb = 20; pb < 36; ++pb) {
+            const uint32_t v = D[pb >> 2];
+            wv[32 + pb - 20] = sbyte(lo16(v), pb & 3);
+            wv[48 + pb - 20] = sbyte(hi16(v), pb & 3);
+        }
+    }
+
+    // dot() over decoded codes and activations in LDS (64 floats at xp),
+    // with the same operations in the same order, so it rounds identically.
+    __device__ static float dot_decoded(const uint32_t (&D)[kDwords], const float (&wv)[64],
+                                        const float *xp)
+    {
+        float s[2] = {0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 lo = *reinterpret_cast<const float4 *>(xp + 32 * b + 4 * i);
+                const float4 hi = *reinterpret_cast<const float4 *>(xp + 32 * b + 16 + 4 * i);
+                const float *w0 = &wv[32 * b + 4 * i];
+                s[b] = fmaf(w0[0], lo.x, s[b]); s[b] = fmaf(w0[16], hi.x, s[b]);
+                s[b] = fmaf(w0[1], lo.y, s[b]); s[b] = fmaf(w0[17], hi.y, s[b]);
+                s[b] = fmaf(w0[2], lo.z, s[b]); s[b] = fmaf(w0[18], hi.z, s[b]);
+                s[b] = fmaf(w0[3], lo.w, s[b]); s[b] = fmaf(w0[19], hi.w, s[b]);
+            }
+        }
+        float acc = fmaf(half_lo(D[0]), s[0], 0.f);
+        return fmaf(half_hi(D[4]), s[1], acc);
+    }
 };
 
 template <> struct Pair<FMT_Q8_0> {
@@ -114,32 +155,64 @@ template <> struct Pair<FMT_Q8_0> {
         acc = fmaf(half_hi(D[8]), s1, acc);
         return acc;
     }
+
+    __device__ static void decode(const uint32_t (&D)[kDwords], float (&wv)[64])
+    {
+#pragma unroll
+        for (int pb = 2; pb < 34; ++pb) wv[pb - 2] = sbyte(D[pb >> 2], pb & 3);
+#pragma unroll
+        for (int pb = 36; pb < 68; ++pb) wv[32 + pb - 36] = sbyte(D[pb >> 2], pb & 3);
+    }
+
+    __device__ static float dot_decoded(const uint32_t (&D)[kDwords], const float (&wv)[64],
+                                        const float *xp)
+    {
+        float s[2] = {0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = *reinterpret_cast<const float4 *>(xp + 32 * b + 4 * i);
+                const float *w0 = &wv[32 * b + 4 * i];
+                s[b] = fmaf(w0[0], v.x, s[b]); s[b] = fmaf(w0[1], v.y, s[b]);
+                s[b] = fmaf(w0[2], v.z, s[b]); s[b] = fmaf(w0[3], v.w, s[b]);
+            }
+        }
+        float acc = fmaf(half_lo(D[0]), s[0], 0.f);
+        return fmaf(half_hi(D[8]), s[1], acc);
+    }
 };
 
 // T threads per row (power of two, 4..WG), RPT rows per thread, CH chunks
 // of T pairs per pass along K, WG threads per workgroup, SX activations
 // staged once per workgroup (else once per wave), NT non-temporal weight
-// loads. Grid: ceil(N / (WG / T * RPT)) workgroups.
+// loads, MR activation rows (M <= MR; rows past M repeat row M-1 and are not
+// stored). Grid: ceil(N / (WG / T * RPT)) workgroups.
 //
-// GATED (RPT = 2): the gated FFN front half. A thread's two rows are row n
-// of the gate matrix w and row n of the up matrix w2, and the output is
-// y[n] = gelu_tanh(gate) * up with gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi)
+// GATED (RPT = 2, MR = 1): the gated FFN front half. A thread's two rows are
+// row n of the gate matrix w and row n of the up matrix w2, and the output
+// is y[n] = gelu_tanh(gate) * up with gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi)
 // (g + 0.044715 g^3))), evaluated in f32 once the two sums are complete.
 // Grid: ceil(N / (WG / T)) workgroups.
 //
 // A wave owns TW = min(T, 64) consecutive pairs of each chunk for its rows
 // (a row wider than one wave is split over T / 64 waves). Per pass of CH
 // chunks along K:
-//  1. the activations of the pass's pairs (64 floats each) are loaded with
-//     coalesced 16-byte loads (L2-resident after the first workgroup): by
-//     the whole workgroup (SX) or by each wave for its own pairs;
+//  1. the activations of the pass's pairs (64 floats each, MR rows) are
+//     loaded with coalesced 16-byte loads (L2-resident after the first
+//     workgroup): by the whole workgroup (SX) or by each wave for its own
+//     pairs;
 //  2. each thread issues the loads of all its CH * RPT weight pairs (HBM);
 //  3. the activations go to LDS, in rows of 64 floats padded by 4 so that
 //     consecutive lanes' 16-byte reads fall in distinct banks; SX needs one
 //     workgroup barrier here (the weights are already in flight), per-wave
 //     staging none;
-//  4. per chunk, each thread reads its 64 activations back and runs the
-//     FMAs for its RPT rows.
+//  4. per chunk, each thread runs the FMAs for its RPT weight rows against
+//     its 64 activations of each of the MR rows. With one activation row the
+//     codes are converted as they are used; with several, a pair is decoded
+//     once into 64 floats and reused for every activation row, in the same
+//     order of operations, so each output row rounds exactly as in a
+//     one-row call.
 // Every load is unconditional from a clamped in-bounds address: rows past N
 // are computed and dropped, pairs past P are masked by a select.
 __device__ __forceinline__ float gelu_tanh(float g)
@@ -148,13 +221,14 @@ __device__ __forceinline__ float gelu_tanh(float g)
     return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
 }
 
-template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED>
+template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED, int MR>
 __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
-    const uint8_t *__restrict__ w2, float *__restrict__ y, int N, int P)
+    const uint8_t *__restrict__ w2, float *__restrict__ y, int M, int N, int P)
 {
     using L = Pair<FMT>;
-    static_assert(!GATED || RPT == 2, "gated: one gate row and one up row per thread");
+    static_assert(!GATED || (RPT == 2 && MR == 1),
+                  "gated: one gate row and one up row per thread, one activation row");
     constexpr int RPAR = WG / T;                // rows in flight per workgroup
     constexpr int TW = T < 64 ? T : 64;         // pairs per wave per chunk
     constexpr int WPR = T / TW;                 // waves per row
@@ -163,11 +237,12 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     // one wave for its TW pairs
     constexpr int SP = SX ? T : TW;             // pairs staged per unit and chunk
     constexpr int ST = SX ? WG : 64;            // threads per staging unit
-    constexpr int XF4 = 16 * SP * CH / ST;      // float4s per thread per pass
+    constexpr int XF4 = 16 * SP * CH / ST;      // float4s per thread, row and pass
     static_assert(16 * SP * CH % ST == 0, "staging must tile the pass exactly");
-    constexpr int REGION = CH * SP * XS;        // floats per staging unit
+    constexpr int REGION = CH * SP * XS;        // floats per staging unit and row
     constexpr int UNITS = SX ? 1 : WG / 64;
-    __shared__ __attribute__((aligned(16))) float xs_all[UNITS * REGION];
+    static_assert(WG / 64 * RPT * MR <= UNITS * MR * REGION, "reduction fits in LDS");
+    __shared__ __attribute__((aligned(16))) float xs_all[UNITS * MR * REGION];
 
     const int tid = threadIdx.x;
     const int lane = tid % 64, wave = tid / 64;
@@ -177,7 +252,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const int sid = SX ? tid : lane;            // thread index in its unit
     const int sp0 = SX ? 0 : tw0;               // first pair staged by the unit
     const int lp = SX ? t : lane % TW;          // this thread's pair in the unit
-    float *xs = xs_all + (SX ? 0 : wave * REGION);
+    float *xs = xs_all + (SX ? 0 : wave * MR * REGION);   // [MR][CH * SP][XS]
     const int64_t row_bytes = (int64_t)P * L::kBytes;
     const int n_first = blockIdx.x * (RPAR * (GATED ? 1 : RPT)) + r;
 
@@ -189,24 +264,33 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         else
             wrow[j] = w + (int64_t)min(n_first + RPAR * j, N - 1) * row_bytes;
     }
-
-    float acc[RPT];
+    const float *xrow[MR];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) acc[j] = 0.f;
+    for (int m = 0; m < MR; ++m) xrow[m] = x + (int64_t)min(m, M - 1) * (64 * P);
+
+    float acc[RPT][MR];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[j][m] = 0.f;
 
     for (int c0 = 0; c0 < P; c0 += CH * T) {
         // 1. activations: float4 i of the unit's pass belongs to chunk
-        //    i / (16 SP), pair (i / 16) % SP of that chunk (clamped to P-1)
-        // (four scalar arrays, not one of float4: the float4 array ends up in
-        // scratch memory once XF4 >= 4 with workgroup-wide staging)
-        float xsx[XF4], xsy[XF4], xsz[XF4], xsw[XF4];
+        //    i / (16 SP), pair (i / 16) % SP of that chunk (clamped to P-1).
+        //    Four scalar arrays, not one of float4: the float4 array ends up
+        //    in scratch memory once XF4 >= 4 with workgroup-wide staging.
+        float xsx[MR][XF4], xsy[MR][XF4], xsz[MR][XF4], xsw[MR][XF4];
 #pragma unroll
         for (int u = 0; u < XF4; ++u) {
             const int i = sid + ST * u;
             const int h = i / (16 * SP), q = (i / 16) % SP;
             const int pp = min(c0 + h * T + sp0 + q, P - 1);
-            const float4 v = *reinterpret_cast<const float4 *>(x + 64 * pp + 4 * (i % 16));
-            xsx[u] = v.x; xsy[u] = v.y; xsz[u] = v.z; xsw[u] = v.w;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float4 v =
+                    *reinterpret_cast<const float4 *>(xrow[m] + 64 * pp + 4 * (i % 16));
+                xsx[m][u] = v.x; xsy[m][u] = v.y; xsz[m][u] = v.z; xsw[m][u] = v.w;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // 2. weight pairs
@@ -223,53 +307,76 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         if constexpr (SX) __syncthreads();      // previous pass's readers done
         else __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int u = 0; u < XF4; ++u) {
-            const int i = sid + ST * u;
-            *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) =
-                make_float4(xsx[u], xsy[u], xsz[u], xsw[u]);
+        for (int m = 0; m < MR; ++m) {
+#pragma unroll
+            for (int u = 0; u < XF4; ++u) {
+                const int i = sid + ST * u;
+                *reinterpret_cast<float4 *>(&xs[m * REGION + (i / 16) * XS + 4 * (i % 16)]) =
+                    make_float4(xsx[m][u], xsy[m][u], xsz[m][u], xsw[m][u]);
+            }
         }
         if constexpr (SX) __syncthreads();
         else __builtin_amdgcn_wave_barrier();
-        // 4. per chunk: activations back to VGPRs, FMAs
+        // 4. per chunk: FMAs
 #pragma unroll
         for (int h = 0; h < CH; ++h) {
-            float xv[64];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 v = *reinterpret_cast<const float4 *>(
-                    &xs[(h * SP + lp) * XS + 4 * i]);
-                xv[4 * i + 0] = v.x; xv[4 * i + 1] = v.y;
-                xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
-            }
             const bool pv = c0 + h * T + t < P;
+            if constexpr (MR == 1) {
+                float xv[64];
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) {
-                const float part = L::dot(D[h][j], xv, 0.f);
-                acc[j] += pv ? part : 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    const float4 v = *reinterpret_cast<const float4 *>(
+                        &xs[(h * SP + lp) * XS + 4 * i]);
+                    xv[4 * i + 0] = v.x; xv[4 * i + 1] = v.y;
+                    xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) {
+                    const float part = L::dot(D[h][j], xv, 0.f);
+                    acc[j][0] += pv ? part : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) {
+                    float wv[64];
+                    L::decode(D[h][j], wv);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const float part =
+                            L::dot_decoded(D[h][j], wv, &xs[m * REGION + (h * SP + lp) * XS]);
+                        acc[j][m] += pv ? part : 0.f;
+                    }
+                }
             }
         }
     }
 
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) acc[j] = group_sum<TW>(acc[j]);
+    for (int j = 0; j < RPT; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[j][m] = group_sum<TW>(acc[j][m]);
 
     if constexpr (WPR == 1 && GATED) {
         if (t == T - 1 && n_first < N)
-            y[n_first] = gelu_tanh(acc[0] * L::kOutScale) * (acc[1] * L::kOutScale);
+            y[n_first] = gelu_tanh(acc[0][0] * L::kOutScale) * (acc[1][0] * L::kOutScale);
     } else if constexpr (WPR == 1) {
         if (t == T - 1) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int n = n_first + RPAR * j;
-                if (n < N) y[n] = acc[j] * L::kOutScale;
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    if (n < N && m < M) y[(int64_t)m * N + n] = acc[j][m] * L::kOutScale;
             }
         }
     } else {
         __syncthreads();                        // every wave is done with xs
-        float *red = xs_all;                    // [WG / 64][RPT]
+        float *red = xs_all;                    // [WG / 64][RPT][MR]
         if (lane == 63) {
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) red[wave * RPT + j] = acc[j];
+            for (int j = 0; j < RPT; ++j)
+#pragma unroll
+                for (int m = 0; m < MR; ++m) red[(wave * RPT + j) * MR + m] = acc[j][m];
         }
         __syncthreads();
         if constexpr (GATED) {
@@ -283,13 +390,13 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
                 const int n = blockIdx.x * RPAR + tid;
                 if (n < N) y[n] = gelu_tanh(sg * L::kOutScale) * (su * L::kOutScale);
             }
-        } else if (tid < RPAR * RPT) {
-            const int rr = tid % RPAR, j = tid / RPAR;
+        } else if (tid < RPAR * RPT * MR) {
+            const int m = tid % MR, rr = (tid / MR) % RPAR, j = tid / (MR * RPAR);
             float s = 0.f;
 #pragma unroll
-            for (int q = 0; q < WPR; ++q) s += red[(rr * WPR + q) * RPT + j];
+            for (int q = 0; q < WPR; ++q) s += red[((rr * WPR + q) * RPT + j) * MR + m];
             const int n = blockIdx.x * (RPAR * RPT) + rr + RPAR * j;
-            if (n < N) y[n] = s * L::kOutScale;
+            if (n < N && m < M) y[(int64_t)m * N + n] = s * L::kOutScale;
         }
     }
 }
@@ -297,14 +404,14 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
 constexpr int kThreads = 256;
 
 template <int FMT, int T, int RPT, int WG = kThreads, int CH = 1, bool SX = false,
-          bool NT = false>
-hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int P,
+          bool NT = false, int MR = 1>
+hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int P,
                   hipStream_t stream)
 {
     constexpr int rows_per_wg = WG / T * RPT;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, SX, NT, false>), dim3(grid),
-                       dim3(WG), 0, stream, x, w, nullptr, y, N, P);
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT, T, RPT, CH, WG, SX, NT, false, MR>), dim3(grid),
+                       dim3(WG), 0, stream, x, w, nullptr, y, M, N, P);
     return hipGetLastError();
 }
 
@@ -314,39 +421,59 @@ hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, fl
 {
     constexpr int rows_per_wg = WG / T;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT_Q4_0, T, 2, 1, WG, SX, false, true>), dim3(grid),
-                       dim3(WG), 0, stream, x, wg, wu, h, N, P);
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT_Q4_0, T, 2, 1, WG, SX, false, true, 1>), dim3(grid),
+                       dim3(WG), 0, stream, x, wg, wu, h, 1, N, P);
     return hipGetLastError();
 }
 
 // Launch shapes, from timing sweeps on MI355X over random weights (cold,
 // 9 MB to 570 MB per call; uniform bytes draw more power than constant
-// ones and change the ranking). P = pairs per row = K / 64.
+// ones and change the ranking). P = pairs per row = K / 64; MR activation
+// rows per launch (1, 2, or 4 for M = 3, 4).
 //   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
 //   P <= 32 : T = 32, one row per thread, workgroups sharing one
-//             activation copy: 512 threads from N = 65536, else 256
+//             activation copy: 512 threads from N = 65536 (with MR > 1:
+//             T = 16 x 2 chunks), else 256 (MR = 4: 512)
 //   P <= 64 : T = 64, one row per thread, 512-thread workgroups sharing one
 //             activation copy
 //   P > 64  : T = 128 (a row spans two waves), one row per thread, looping
 //             over K in chunks of 128 pairs, workgroups sharing one
-//             activation copy: 1024 threads (8 rows) from N = 4096 (Q4_0)
-//             or N = 2048 (Q8_0), else 512 (4 rows)
-template <int FMT>
-hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int N, int K,
+//             activation copy: 512 threads (4 rows); with MR = 1, 1024
+//             threads (8 rows) from N = 4096 (Q4_0) or N = 2048 (Q8_0)
+template <int FMT, int MR>
+hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
     const int P = K / 64;  // K % 256 == 0, so P % 4 == 0
-    if (P <= 4) return launch<FMT, 4, 2, 256, 1>(x, w, y, N, P, stream);
-    if (P <= 8) return launch<FMT, 8, 2, 256, 1>(x, w, y, N, P, stream);
-    if (P <= 16) return launch<FMT, 16, 2, 256, 1>(x, w, y, N, P, stream);
+    if (P <= 4) return launch<FMT, 4, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);
+    if (P <= 8) return launch<FMT, 8, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);
+    if (P <= 16) return launch<FMT, 16, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);
     if (P <= 32) {
-        if (N >= 65536) return launch<FMT, 32, 1, 512, 1, true>(x, w, y, N, P, stream);
-        return launch<FMT, 32, 1, 256, 1, true>(x, w, y, N, P, stream);
+        if constexpr (MR == 1) {
+            if (N >= 65536)
+                return launch<FMT, 32, 1, 512, 1, true, false, 1>(x, w, y, M, N, P, stream);
+            return launch<FMT, 32, 1, 256, 1, true, false, 1>(x, w, y, M, N, P, stream);
+        } else {
+            if (N >= 65536)
+                return launch<FMT, 16, 1, 512, 2, true, false, MR>(x, w, y, M, N, P, stream);
+            return launch<FMT, 32, 1, MR == 2 ? 256 : 512, 1, true, false, MR>(x, w, y, M, N,
+                                                                               P, stream);
+        }
     }
-    if (P <= 64) return launch<FMT, 64, 1, 512, 1, true>(x, w, y, N, P, stream);
-    if (N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
-        return launch<FMT, 128, 1, 1024, 1, true>(x, w, y, N, P, stream);
-    return launch<FMT, 128, 1, 512, 1, true>(x, w, y, N, P, stream);
+    if (P <= 64) return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+    if (MR == 1 && N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
+        return launch<FMT, 128, 1, 1024, 1, true, false, 1>(x, w, y, M, N, P, stream);
+    return launch<FMT, 128, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+}
+
+template <int FMT>
+hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                       hipStream_t stream)
+{
+    if (M == 1) return launch_fmt<FMT, 1>(x, w, y, M, N, K, stream);
+    if (M == 2) return launch_fmt<FMT, 2>(x, w, y, M, N, K, stream);
+    if (M <= kGemvRowsMax) return launch_fmt<FMT, 4>(x, w, y, M, N, K, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -366,11 +493,11 @@ hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8
     return launch_gated<128, 512, true>(x, w_gate, w_up, h, N, P, stream);
 }
 
-hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y,
+hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, int M,
                           int N, int K, hipStream_t stream)
 {
-    return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, N, K, stream)
-                           : launch_fmt<FMT_Q8_0>(x, w, y, N, K, stream);
+    return fmt == FMT_Q4_0 ? launch_rows<FMT_Q4_0>(x, w, y, M, N, K, stream)
+                           : launch_rows<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }
 
 }  // namespace qmm

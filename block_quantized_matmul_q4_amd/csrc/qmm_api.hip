@@ -98,8 +98,9 @@ QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
     const uint8_t *wb = (const uint8_t *)w;
-    if (M == 1)
-        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)N, (int)K, stream));
+    if (M <= qmm::kGemvRowsMax)
+        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N, (int)K,
+                                              stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
                                                (int)K, stream));
 }
@@ -111,8 +112,9 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ8Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
     const uint8_t *wb = (const uint8_t *)w;
-    if (M == 1)
-        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)N, (int)K, stream));
+    if (M <= qmm::kGemvRowsMax)
+        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N, (int)K,
+                                              stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
                                                (int)K, stream));
 }

@@ -19,7 +19,10 @@ inline constexpr int block_bytes(int fmt) { return fmt == FMT_Q4_0 ? kQ4Bytes : 
 // pointers non-null and aligned, 1 <= M, 1 <= N, 256 <= K <= 65536,
 // K % 256 == 0, N and M * N within int32 range. Each returns the
 // hipGetLastError() of its launch.
-hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y,
+// GEMV with f32 FMAs for M <= kGemvRowsMax activation rows (the weights
+// streamed once per launch); more rows take the matrix-core small-M kernel.
+constexpr int kGemvRowsMax = 4;
+hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, int M,
                           int N, int K, hipStream_t stream);
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream);

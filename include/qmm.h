@@ -79,7 +79,10 @@ typedef enum qmm_status {
  * Decode GEMV over Q4_0 weights, 1 <= M <= 16 activation rows (M = 1 for
  * one decoded token, M = 2..16 for batched or speculative decode, where
  * several tokens share one pass over the weights). f32 accumulation; the
- * weights stream from HBM once per call.
+ * weights stream from HBM once per call. Up to 4 rows take f32 FMAs on
+ * codes converted exactly to f32, and each row rounds as in a one-row call
+ * of the same launch shape; 5 to 16 rows take the bf16 matrix cores with
+ * exact products (codes exact in bf16, x split into two bf16 terms).
  */
 QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

@@ -130,6 +130,10 @@ GEMV_SHAPES = [
     (2, 1, 256), (3, 257, 768), (5, 1000, 2048), (7, 17, 2304), (11, 130, 512),
     (16, 33, 8192), (16, 1, 256), (13, 4100, 1024),
     (1, 65539, 1280), (1, 4100, 8192), (1, 4099, 8448), (1, 2049, 4352),
+    # 2-4 rows on the f32 FMA kernel: every K branch, ragged N and K, a
+    # clamped third row (M = 3 runs four), N >= 65536
+    (2, 100, 1024), (4, 17, 512), (2, 1000, 2048), (4, 1000, 2048), (3, 333, 4096),
+    (2, 2049, 8192), (4, 65, 16384), (3, 4099, 8448), (2, 65539, 1280), (3, 65537, 2048),
 ]
 
 
@@ -137,6 +141,23 @@ GEMV_SHAPES = [
 @pytest.mark.parametrize("m,n,k", GEMV_SHAPES)
 def test_gemv_shapes(orc, fmt, m, n, k):
     check(orc, "gemv", fmt, m, n, k, seed=m * 7 + n)
+
+
+# Up to 4 rows run the f32 FMA kernel with each pair decoded once for all
+# rows, in the same order of operations as a one-row call: where both use
+# the same threads per row (every K branch, N < 65536), each row of a
+# multi-row result equals the one-row result bit for bit.
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("n,k", [(1000, 1024), (8192, 2048), (333, 4096), (4099, 8448)])
+def test_gemv_rows_match_single_row_bitwise(fmt, n, k):
+    note(f"[bitwise] gemv_{fmt} rows vs single-row calls N={n} K={k}")
+    x = synth.activations(4, k, seed=n)
+    w = weights(fmt, n, k, seed=n + 1)
+    single = np.stack([run("gemv", fmt, x[m:m + 1], w, n, k)[0] for m in range(4)])
+    for m in (2, 3, 4):
+        y = run("gemv", fmt, x[:m], w, n, k)
+        assert np.array_equal(y.view(np.uint32), single[:m].view(np.uint32)), \
+            f"M={m}: {int((y != single[:m]).sum())} outputs differ from one-row calls"
 
 
 GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
