@@ -269,6 +269,19 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
         const int grid = (N + 16 * NT - 1) / (16 * NT);
         hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, WAVES>), dim3(grid),
                            dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
+    } else if (N < 8192) {
+        // fewer than 256 workgroups of 32 rows: 16 rows per workgroup, eight
+        // waves over K (six for M > 8, whose A fragments take twice the LDS)
+        // (FFN down shape N = 2048, K = 8192: M = 5 14.9 -> 11.6 us, M = 16
+        // 26.4 -> 23.1 us)
+        constexpr int NT = 1;
+        const int grid = (N + 16 * NT - 1) / (16 * NT);
+        if (M <= 8)
+            hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, 8>), dim3(grid),
+                               dim3(64 * 8), 0, stream, x, w, y, M, N, K);
+        else
+            hipLaunchKernelGGL((gemv_small_m_kernel<FMT, false, NT, 6>), dim3(grid),
+                               dim3(64 * 6), 0, stream, x, w, y, M, N, K);
     } else if (M <= 8) {
         constexpr int NT = 2, WAVES = 8;
         const int grid = (N + 16 * NT - 1) / (16 * NT);

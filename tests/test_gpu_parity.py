@@ -134,6 +134,8 @@ GEMV_SHAPES = [
     # clamped third row (M = 3 runs four), N >= 65536
     (2, 100, 1024), (4, 17, 512), (2, 1000, 2048), (4, 1000, 2048), (3, 333, 4096),
     (2, 2049, 8192), (4, 65, 16384), (3, 4099, 8448), (2, 65539, 1280), (3, 65537, 2048),
+    # 5-16 rows with N < 8192 (16-row matrix-core workgroups)
+    (5, 2048, 8192), (12, 2049, 8448),
 ]
 
 
