@@ -162,6 +162,20 @@ def test_gemv_rows_match_single_row_bitwise(fmt, n, k):
             f"M={m}: {int((y != single[:m]).sum())} outputs differ from one-row calls"
 
 
+# The GEMM entry points hand M <= 16 to the decode GEMV kernels: the same
+# launches, so the same bits.
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 2048), (3, 333, 4096), (4, 2049, 8192),
+                                   (5, 1000, 2048), (16, 257, 1024)])
+def test_gemm_small_m_is_gemv(fmt, m, n, k):
+    note(f"[bitwise] gemm_{fmt} vs gemv_{fmt} M={m} N={n} K={k}")
+    x = synth.activations(m, k, seed=n)
+    w = weights(fmt, n, k, seed=n + 2)
+    yg = run("gemm", fmt, x, w, n, k)
+    yv = run("gemv", fmt, x, w, n, k)
+    assert np.array_equal(yg.view(np.uint32), yv.view(np.uint32))
+
+
 GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                (300, 17, 512), (256, 256, 4096), (1000, 520, 1280), (17, 2049, 256)]
 
@@ -279,7 +293,7 @@ def test_zero_point_exact(entry, m):
     assert np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("entry,m", [("gemv", 1), ("gemv", 2), ("gemm", 3)])
+@pytest.mark.parametrize("entry,m", [("gemv", 1), ("gemv", 2), ("gemm", 17)])
 def test_subnormal_scale_exact(entry, m):
     n, k = 4, 256
     bits = np.array([0x0001, 0x03FF, 0x8001, 0x0200], np.uint16)
