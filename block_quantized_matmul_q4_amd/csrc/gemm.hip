@@ -339,6 +339,136 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     }
 }
 
+// Medium M: few output tiles, so instead of one tile's K loop per compute
+// unit, a workgroup owns a 32-column slice of y for a band of 32 MT rows
+// (grid: column slices x row bands) and its WAVES waves take interleaved K
+// steps of 64 in parallel
+// (wave w: steps w, w + WAVES, ...), each with its own accumulators, meeting
+// in LDS at the end (summed in wave order). Same arithmetic as the tile
+// kernel: x and w rounded once to bf16 (RNE), f32 accumulation.
+//
+// Per step a wave loads its activation rows (16 lanes per row, a float4
+// each) and one weight block per lane (row lane / 2 of the slice, block
+// lane % 2 of the pair), converts both into its own LDS region, then runs
+// MT 32x32x16 MFMAs per 16-wide substep; the next step's loads are issued
+// before this step's matrix-core work. Rows past M and columns past N load
+// zeros through the buffer resources' range checks and are not stored.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int FMT, int MT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
+    const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
+    int M, int N, int K)
+{
+    constexpr int BM = 32 * MT, BN = 32;
+    constexpr int AF4 = BM / 4;                         // activation float4 per lane
+    constexpr int REGION = (BM + BN) * LDK;             // bf16 per wave
+    static_assert(MT * 1024 * 4 <= REGION * 2, "wave partials fit the wave's region");
+    __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
+
+    using BF = BFmt<FMT>;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int rows = min(BM, M - m0);
+    const int P = K / 64;
+    const int row_bytes = P * BF::kPairBytes;
+    __bf16 *As = lds + wave * REGION;
+    __bf16 *Bs = As + BM * LDK;
+
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + (int64_t)m0 * K), 0, rows * K * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, min(BN, N - n0) * row_bytes,
+        kBufferWord3);
+    // activation row lane / 16 + 4 u, columns 4 (lane % 16) .. +3 of the step
+    const int a_col = 4 * (lane % 16);
+    const int a_voff0 = ((lane / 16) * K + a_col) * 4;
+    // weight row lane / 2 of the slice, block lane % 2 of the step's pair
+    const int b_row = lane / 2, b_blk = lane % 2;
+    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
+
+    float4 a_reg[AF4];
+    uint32_t b_reg[BF::kWin];
+    auto load = [&](int p) {
+#pragma unroll
+        for (int u = 0; u < AF4; ++u) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
+            a_reg[u] = __builtin_bit_cast(float4, v);
+        }
+        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg);
+    };
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+    const int frow = lane % 32, fk = 8 * (lane / 32);
+    // a wave without steps (P < WAVES) loads the last step and never uses it
+    load(min(wave, P - 1));
+    for (int p = wave; p < P; p += WAVES) {
+#pragma unroll
+        for (int u = 0; u < AF4; ++u) {
+            const float4 v = a_reg[u];
+            uint2 pk;
+            pk.x = pack_bf16x2(v.x, v.y);
+            pk.y = pack_bf16x2(v.z, v.w);
+            *reinterpret_cast<uint2 *>(&As[(lane / 16 + 4 * u) * LDK + a_col]) = pk;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            BF::convert_quarter(b_reg, b_blk, q, &Bs[b_row * LDK + 32 * b_blk]);
+        load(min(p + WAVES, P - 1));            // registers are free again
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[frow * LDK + fk + 16 * s]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                    &As[(32 * i + frow) * LDK + fk + 16 * s]);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+            }
+        }
+        wave_lds_sync();                        // fragments read before the next writes
+    }
+
+    // partials: red[wave][i][e][lane] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][lane % 32]
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[((wave * MT + i) * 16 + e) * 64 + lane] = acc[i][e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < MT * 16 * 64; o += 64 * WAVES) {
+        const int l = o % 64, e = (o / 64) % 16, i = o / 1024;
+        const int r = 32 * i + 8 * (e / 4) + 4 * (l / 32) + e % 4;
+        const int n = n0 + l % 32;
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < WAVES; ++q) s += red[((q * MT + i) * 16 + e) * 64 + l];
+        if (r < rows && n < N) y[(int64_t)(m0 + r) * N + n] = s;
+    }
+}
+
+template <int FMT, int MT, int WAVES>
+hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                      hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_mid_kernel<FMT, MT, WAVES>),
+                       dim3((N + 31) / 32, (M + 32 * MT - 1) / (32 * MT)), dim3(64 * WAVES), 0,
+                       stream, x, w, y, M, N, K);
+    return hipGetLastError();
+}
+
 template <int FMT, class TL>
 hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                         hipStream_t stream)
@@ -358,10 +488,20 @@ hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N
 // 128 x 128 tile (4 x as many workgroups) keeps more of the chip busy.
 constexpr int64_t kComputeUnits = 256;
 
+// Up to kMidRowsMax rows the medium-M kernel: 64-row bands when there are
+// at least 128 column slices (N >= 4096), else 32-row bands for more
+// workgroups (timing sweeps at K = 2048 .. 8192: M = 16, N = 8192 7.3 us and
+// M = 128, N = 2048, K = 8192 22.5 us, against 23 and 88 us on tiles).
+constexpr int kMidRowsMax = 128;
+
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
+    if (M <= kMidRowsMax) {
+        if (M > 32 && N >= 4096) return launch_mid<FMT, 2, 8>(x, w, y, M, N, K, stream);
+        return launch_mid<FMT, 1, 8>(x, w, y, M, N, K, stream);
+    }
     const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (large_tiles < kComputeUnits)
         return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);

@@ -84,14 +84,11 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
                     "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
                     (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX - 8);
     const uint8_t *wb = (const uint8_t *)w;
-    // Up to 16 rows the decode GEMV kernels stream the weights once with
-    // f32-exact products: faster than tiles that are mostly padding, and
-    // well inside this entry point's bound.
+    // Up to 4 rows the decode GEMV kernel streams the weights once with
+    // f32-exact products: faster than any matrix-core tiling there, and well
+    // inside this entry point's bound.
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
-    if (M <= QMM_GEMV_MAX_M)
-        return finish(fn, qmm::launch_gemv_small_m(fmt, x, wb, y, (int)M, (int)N, (int)K,
-                                                   stream));
     return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
 }
 
