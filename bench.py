@@ -18,7 +18,8 @@ Timing:
   bracketed by HIP events on the launch stream; the per-launch mean
   includes the dispatch gap between consecutive kernels.
 * the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
-  vocabulary GEMV and the Q4_0 prefill GEMM, reported under "rows".
+  vocabulary GEMV and the Q4_0 prefill GEMM (M = 2048, and short prompts
+  M = 16, 64, 128), reported under "rows".
 * decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
   at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
   weight copy, captured in one HIP graph; 5 replays bracketed by HIP events
@@ -364,6 +365,18 @@ def main():
                                          frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
                                          prefill_tokens_per_s=pre["M"] / (tp["mean_us"] * 1e-6))
         log(f"[bench] prefill GEMM: {tp['mean_us']:.2f} us, {tfl:.1f} TFLOP/s")
+        # short prompts over the same weights (the medium-M kernel), cold pool
+        for ms in (16, 64, 128):
+            xs = torch.from_numpy(synth.activations(ms, pre["K"])).to(dev)
+            ys = torch.empty((ms, pre["N"]), device=dev)
+            ts = time_launches(lib.qmm_gemm_q4_0,
+                               gemv_args(xs, w_up, ys, ms, pre["N"], pre["K"], max(20, n // 2)))
+            fs = 2 * ms * pre["N"] * pre["K"]
+            rows[f"q4_0_gemm_m{ms}"] = dict(ts, flops=fs,
+                                            tflops=fs / (ts["mean_us"] * 1e-6) / 1e12,
+                                            prefill_tokens_per_s=ms / (ts["mean_us"] * 1e-6))
+            log(f"[bench] prefill GEMM M={ms}: {ts['mean_us']:.2f} us")
+        del xs, ys
         # the same prefill shape over Q8_0 weights
         w8_h = synth.q8_0_weights(pre["N"], pre["K"])
         w8 = pool(w8_h)
