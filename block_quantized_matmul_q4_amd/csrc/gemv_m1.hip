@@ -80,45 +80,37 @@ template <> struct Pair<FMT_Q4_0> {
         return acc;
     }
 
-    // The codes of a pair as floats, 16(q-8) in element order, for reuse
-    // over several activation rows.
-    __device__ static void decode(const uint32_t (&D)[kDwords], float (&wv)[64])
+    // dot() in chunks, for reuse of each activation chunk over several
+    // weight rows: chunk i of block b covers elements 4i..4i+3 (low
+    // nibbles) and 16+4i..16+4i+3 (high nibbles); chunk_fma runs exactly
+    // dot()'s operations for them, in dot()'s order, so the chunks of a block
+    // in turn round identically to dot().
+    static constexpr int kChunks = 4;           // per block
+    static constexpr int kChunkCodes = 8;
+    static constexpr bool kHiHalf = true;       // chunks also read x[16 + ..]
+    __device__ static void chunk_codes(const uint32_t (&D)[kDwords], int b, int i,
+                                       float (&wc)[kChunkCodes])
     {
 #pragma unroll
-        for (int pb = 2; pb < 18; ++pb) {
+        for (int e = 0; e < 4; ++e) {
+            const int pb = 2 + 18 * b + 4 * i + e;
             const uint32_t v = D[pb >> 2];
-            wv[pb - 2] = sbyte(lo16(v), pb & 3);
-            wv[pb - 2 + 16] = sbyte(hi16(v), pb & 3);
-        }
-#pragma unroll
-        for (int pb = 20; pb < 36; ++pb) {
-            const uint32_t v = D[pb >> 2];
-            wv[32 + pb - 20] = sbyte(lo16(v), pb & 3);
-            wv[48 + pb - 20] = sbyte(hi16(v), pb & 3);
+            wc[e] = sbyte(lo16(v), pb & 3);
+            wc[4 + e] = sbyte(hi16(v), pb & 3);
         }
     }
-
-    // dot() over decoded codes and activations in LDS (64 floats at xp),
-    // with the same operations in the same order, so it rounds identically.
-    __device__ static float dot_decoded(const uint32_t (&D)[kDwords], const float (&wv)[64],
-                                        const float *xp)
+    __device__ static float chunk_fma(float s, const float (&wc)[kChunkCodes], float4 lo,
+                                      float4 hi)
     {
-        float s[2] = {0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 lo = *reinterpret_cast<const float4 *>(xp + 32 * b + 4 * i);
-                const float4 hi = *reinterpret_cast<const float4 *>(xp + 32 * b + 16 + 4 * i);
-                const float *w0 = &wv[32 * b + 4 * i];
-                s[b] = fmaf(w0[0], lo.x, s[b]); s[b] = fmaf(w0[16], hi.x, s[b]);
-                s[b] = fmaf(w0[1], lo.y, s[b]); s[b] = fmaf(w0[17], hi.y, s[b]);
-                s[b] = fmaf(w0[2], lo.z, s[b]); s[b] = fmaf(w0[18], hi.z, s[b]);
-                s[b] = fmaf(w0[3], lo.w, s[b]); s[b] = fmaf(w0[19], hi.w, s[b]);
-            }
-        }
-        float acc = fmaf(half_lo(D[0]), s[0], 0.f);
-        return fmaf(half_hi(D[4]), s[1], acc);
+        s = fmaf(wc[0], lo.x, s); s = fmaf(wc[4], hi.x, s);
+        s = fmaf(wc[1], lo.y, s); s = fmaf(wc[5], hi.y, s);
+        s = fmaf(wc[2], lo.z, s); s = fmaf(wc[6], hi.z, s);
+        s = fmaf(wc[3], lo.w, s); s = fmaf(wc[7], hi.w, s);
+        return s;
+    }
+    __device__ static float scale(const uint32_t (&D)[kDwords], int b)
+    {
+        return b ? half_hi(D[4]) : half_lo(D[0]);
     }
 };
 
@@ -156,30 +148,28 @@ template <> struct Pair<FMT_Q8_0> {
         return acc;
     }
 
-    __device__ static void decode(const uint32_t (&D)[kDwords], float (&wv)[64])
+    // chunk i of block b: elements 4i..4i+3 (see Pair<FMT_Q4_0>)
+    static constexpr int kChunks = 8;
+    static constexpr int kChunkCodes = 4;
+    static constexpr bool kHiHalf = false;
+    __device__ static void chunk_codes(const uint32_t (&D)[kDwords], int b, int i,
+                                       float (&wc)[kChunkCodes])
     {
 #pragma unroll
-        for (int pb = 2; pb < 34; ++pb) wv[pb - 2] = sbyte(D[pb >> 2], pb & 3);
-#pragma unroll
-        for (int pb = 36; pb < 68; ++pb) wv[32 + pb - 36] = sbyte(D[pb >> 2], pb & 3);
-    }
-
-    __device__ static float dot_decoded(const uint32_t (&D)[kDwords], const float (&wv)[64],
-                                        const float *xp)
-    {
-        float s[2] = {0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 v = *reinterpret_cast<const float4 *>(xp + 32 * b + 4 * i);
-                const float *w0 = &wv[32 * b + 4 * i];
-                s[b] = fmaf(w0[0], v.x, s[b]); s[b] = fmaf(w0[1], v.y, s[b]);
-                s[b] = fmaf(w0[2], v.z, s[b]); s[b] = fmaf(w0[3], v.w, s[b]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int pb = 2 + 34 * b + 4 * i + e;
+            wc[e] = sbyte(D[pb >> 2], pb & 3);
         }
-        float acc = fmaf(half_lo(D[0]), s[0], 0.f);
-        return fmaf(half_hi(D[8]), s[1], acc);
+    }
+    __device__ static float chunk_fma(float s, const float (&wc)[kChunkCodes], float4 v, float4)
+    {
+        s = fmaf(wc[0], v.x, s); s = fmaf(wc[1], v.y, s);
+        s = fmaf(wc[2], v.z, s); s = fmaf(wc[3], v.w, s);
+        return s;
+    }
+    __device__ static float scale(const uint32_t (&D)[kDwords], int b)
+    {
+        return b ? half_hi(D[8]) : half_lo(D[0]);
     }
 };
 
@@ -336,14 +326,44 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
                     acc[j][0] += pv ? part : 0.f;
                 }
             } else {
+                // chunk by chunk: each activation chunk is read from LDS once
+                // for all RPT weight rows, each chunk of codes decoded once
+                // for all MR activation rows
+                float s[RPT][MR][2];
+#pragma unroll
+                for (int j = 0; j < RPT; ++j)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) s[j][m][0] = s[j][m][1] = 0.f;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                    for (int i = 0; i < L::kChunks; ++i) {
+                        float4 xl[MR], xh[MR];
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            const float *xp = &xs[m * REGION + (h * SP + lp) * XS + 32 * b + 4 * i];
+                            xl[m] = *reinterpret_cast<const float4 *>(xp);
+                            if constexpr (L::kHiHalf)
+                                xh[m] = *reinterpret_cast<const float4 *>(xp + 16);
+                            else
+                                xh[m] = xl[m];
+                        }
+#pragma unroll
+                        for (int j = 0; j < RPT; ++j) {
+                            float wc[L::kChunkCodes];
+                            L::chunk_codes(D[h][j], b, i, wc);
+#pragma unroll
+                            for (int m = 0; m < MR; ++m)
+                                s[j][m][b] = L::chunk_fma(s[j][m][b], wc, xl[m], xh[m]);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < RPT; ++j) {
-                    float wv[64];
-                    L::decode(D[h][j], wv);
+                    const float d0 = L::scale(D[h][j], 0), d1 = L::scale(D[h][j], 1);
 #pragma unroll
                     for (int m = 0; m < MR; ++m) {
-                        const float part =
-                            L::dot_decoded(D[h][j], wv, &xs[m * REGION + (h * SP + lp) * XS]);
+                        const float part = fmaf(d1, s[j][m][1], fmaf(d0, s[j][m][0], 0.f));
                         acc[j][m] += pv ? part : 0.f;
                     }
                 }
@@ -432,14 +452,15 @@ hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, fl
 // rows per launch (1, 2, or 4 for M = 3, 4).
 //   P <= 16 : one wave-local chunk of T = P pairs, 2 rows per thread
 //   P <= 32 : T = 32, one row per thread, workgroups sharing one
-//             activation copy: 512 threads from N = 65536 (with MR > 1:
-//             T = 16 x 2 chunks), else 256 (MR = 4: 512)
+//             activation copy: 512 threads from N = 65536 (MR = 2: T = 16 x
+//             2 chunks; MR = 4: 2 rows per thread), else 256
 //   P <= 64 : T = 64, one row per thread, 512-thread workgroups sharing one
 //             activation copy
 //   P > 64  : T = 128 (a row spans two waves), one row per thread, looping
 //             over K in chunks of 128 pairs, workgroups sharing one
-//             activation copy: 512 threads (4 rows); with MR = 1, 1024
-//             threads (8 rows) from N = 4096 (Q4_0) or N = 2048 (Q8_0)
+//             activation copy: 512 threads (4 rows; MR = 4: 2 rows per
+//             thread); with MR = 1, 1024 threads (8 rows) from N = 4096
+//             (Q4_0) or N = 2048 (Q8_0)
 template <int FMT, int MR>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
@@ -453,16 +474,20 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
             if (N >= 65536)
                 return launch<FMT, 32, 1, 512, 1, true, false, 1>(x, w, y, M, N, P, stream);
             return launch<FMT, 32, 1, 256, 1, true, false, 1>(x, w, y, M, N, P, stream);
+        } else if constexpr (MR == 2) {
+            if (N >= 65536)
+                return launch<FMT, 16, 1, 512, 2, true, false, 2>(x, w, y, M, N, P, stream);
+            return launch<FMT, 32, 1, 256, 1, true, false, 2>(x, w, y, M, N, P, stream);
         } else {
             if (N >= 65536)
-                return launch<FMT, 16, 1, 512, 2, true, false, MR>(x, w, y, M, N, P, stream);
-            return launch<FMT, 32, 1, MR == 2 ? 256 : 512, 1, true, false, MR>(x, w, y, M, N,
-                                                                               P, stream);
+                return launch<FMT, 32, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+            return launch<FMT, 32, 1, 256, 1, true, false, MR>(x, w, y, M, N, P, stream);
         }
     }
     if (P <= 64) return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
     if (MR == 1 && N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
         return launch<FMT, 128, 1, 1024, 1, true, false, 1>(x, w, y, M, N, P, stream);
+    if (MR == 4) return launch<FMT, 128, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
     return launch<FMT, 128, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
 }
 
