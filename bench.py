@@ -12,13 +12,17 @@ previous layer produced them.
 Timing:
 * ms_per_step / value: K steps captured in one HIP graph and replayed
   between two device synchronizations (wall clock); the GPU runs the steps
-  back to back.
+  back to back. Before it, the W warmup steps (their own graph) run, then
+  are replayed untimed for --settle-ms (default 50 ms): the shader clock
+  rises over the first 20-30 ms of sustained load, and a timing taken right
+  after an idle spell or a fresh allocation reads up to 25 % slow.
 * per-kernel durations: --samples launches of one kernel (cycling through
   the cold pool) captured back to back in a HIP graph; each of 5 replays is
   bracketed by HIP events on the launch stream; the per-launch mean
   includes the dispatch gap between consecutive kernels.
 * the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
-  vocabulary GEMV and the Q4_0 prefill GEMM (M = 2048, and short prompts
+  vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
+  GEMM (M = 2048, and short prompts
   M = 16, 64, 128), reported under "rows".
 * decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
   at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
@@ -65,6 +69,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="replay the warmup work for at least this long before each "
+                         "timing (clocks rise over the first ~20-30 ms of sustained load)")
     ap.add_argument("--samples", type=int, default=100,
                     help="back-to-back launches per timed graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -180,17 +187,26 @@ def main():
         ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[i % len(w_dn)].data_ptr(),
                              y_dn.data_ptr(), 1, down["N"], down["K"], s))
 
+    def settle(g, min_ms):
+        """Replays graph g (untimed) until min_ms of wall time have passed."""
+        t_end = time.perf_counter() + min_ms * 1e-3
+        g.replay()
+        torch.cuda.synchronize()
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
+
     def time_launches(fn, arglists, replays=5):
         """Mean duration per launch of fn(*arglists[i], stream): the launches
-        are captured back to back in one HIP graph, and each replay is
-        bracketed by HIP events on the stream it runs on."""
+        are captured back to back in one HIP graph, replayed untimed for
+        --settle-ms (code objects, TLB, clocks), then each of `replays`
+        replays is bracketed by HIP events on the stream it runs on."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
             for a in arglists:
                 ok(fn(*a, cs))
-        g.replay()                       # warm: code objects, TLB, clocks
-        torch.cuda.synchronize()
+        settle(g, args.settle_ms)
         ev = hip.events(2 * replays)
         rec = hip.lib.hipEventRecord
         for r in range(replays):
@@ -231,7 +247,8 @@ def main():
     g_warm = capture(args.warmup, len(w_up) // 2) if args.warmup > 0 else None
     g_timed = capture(args.steps, 0)
     if g_warm is not None:
-        g_warm.replay()
+        g_warm.replay()                  # the W warmup steps
+        settle(g_warm, args.settle_ms)   # and more of them until clocks settle
     torch.cuda.synchronize()
     ev0, ev1 = hip.events(2)
     t0 = time.perf_counter()
@@ -331,8 +348,7 @@ def main():
         g_dec = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_dec):
             decode_step(torch.cuda.current_stream().cuda_stream)
-        g_dec.replay()
-        torch.cuda.synchronize()
+        settle(g_dec, args.settle_ms)
         reps = 5
         ev = hip.events(2 * reps)
         for r in range(reps):
@@ -352,6 +368,17 @@ def main():
         log(f"[bench] decode step replay (343 GEMVs): {td['mean_us']:.1f} us, "
             f"{1e6 / td['mean_us']:.0f} tok/s")
         del wv
+        # the same vocabulary head over Q4_0 weights (302 MB): the Q4_0 GEMV at
+        # a size that amortizes launch costs
+        w4v_h = synth.q4_0_weights(voc["N"], voc["K"])
+        w4v = pool(w4v_h)
+        t4 = time_launches(lib.qmm_gemv_q4_0,
+                           gemv_args(xv, w4v, yv, 1, voc["N"], voc["K"], max(20, n // 4)))
+        b4 = w4v_h.nbytes + xv_h.nbytes + yv.numel() * 4
+        g4 = b4 / (t4["mean_us"] * 1e-6) / 1e9
+        rows["q4_0_gemv_vocab"] = dict(t4, bytes=b4, gbs=g4, frac_hbm_peak=g4 / HBM_PEAK_GBS)
+        log(f"[bench] q4 vocab: {t4['mean_us']:.2f} us, {b4 / t4['mean_us'] / 1e3:.0f} GB/s")
+        del w4v, w4v_h
         # Q4_0 prefill GEMM
         pre = synth.WORKLOADS["q4_0_gemm_prefill"]
         xp = torch.from_numpy(synth.activations(pre["M"], pre["K"])).to(dev)
@@ -423,6 +450,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

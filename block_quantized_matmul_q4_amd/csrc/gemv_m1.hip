@@ -455,7 +455,8 @@ hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, fl
 //             activation copy: 512 threads from N = 65536 (MR = 2: T = 16 x
 //             2 chunks; MR = 4: 2 rows per thread), else 256
 //   P <= 64 : T = 64, one row per thread, 512-thread workgroups sharing one
-//             activation copy
+//             activation copy (MR = 1 with N >= 32768: T = 32 x 2 chunks;
+//             Q4_0, N = 128256, K = 4096: 68-75 -> 57 us)
 //   P > 64  : T = 128 (a row spans two waves), one row per thread, looping
 //             over K in chunks of 128 pairs, workgroups sharing one
 //             activation copy: 512 threads (4 rows; MR = 4: 2 rows per
@@ -484,7 +485,11 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
             return launch<FMT, 32, 1, 256, 1, true, false, MR>(x, w, y, M, N, P, stream);
         }
     }
-    if (P <= 64) return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+    if (P <= 64) {
+        if (MR == 1 && N >= 32768)
+            return launch<FMT, 32, 1, 512, 2, true, false, 1>(x, w, y, M, N, P, stream);
+        return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+    }
     if (MR == 1 && N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
         return launch<FMT, 128, 1, 1024, 1, true, false, 1>(x, w, y, M, N, P, stream);
     if (MR == 4) return launch<FMT, 128, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);

@@ -136,6 +136,8 @@ GEMV_SHAPES = [
     (2, 2049, 8192), (4, 65, 16384), (3, 4099, 8448), (2, 65539, 1280), (3, 65537, 2048),
     # 5-16 rows with N < 8192 (16-row matrix-core workgroups)
     (5, 2048, 8192), (12, 2049, 8448),
+    # one row, wide N, K <= 4096 (32 lanes x 2 chunks per row, ragged K)
+    (1, 32769, 3328),
 ]
 
 
