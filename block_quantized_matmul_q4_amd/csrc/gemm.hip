@@ -65,6 +65,12 @@ template <int BM_, int BN_, int WAVES_M_, int WAVES_N_> struct Tile {
 using TileLarge = Tile<256, 256, 2, 4>;
 using TileSmall = Tile<128, 128, 2, 2>;
 
+// f rounded to bf16 (nearest even), back in f32
+__device__ __forceinline__ float bf16_round(float f)
+{
+    return (float)(__bf16)f;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -115,6 +121,30 @@ template <> struct BFmt<FMT_Q4_0> {
         }
         *reinterpret_cast<uint4 *>(dst + 16 * nib + 8 * h) = v;
     }
+
+    // The same quarter as integer codes 16 (q - 8), exact in bf16, for
+    // products kept exact; the block's scale is applied afterwards.
+    static constexpr float kCodeScale = 1.0f / 16.0f;
+    __device__ static void codes_quarter(const uint32_t (&b)[kWin], int blk, int q, __bf16 *dst)
+    {
+        const int h = q % 2, nib = q / 2;
+        uint4 v;
+        uint32_t *o = &v.x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i = 2 * h + t;
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+            const uint32_t qs = blk ? b[i + 1] : realigned;
+            const uint32_t s = nib ? hi16(qs) : lo16(qs);
+            o[2 * t] = pack_bf16x2(sbyte(s, 0), sbyte(s, 1));
+            o[2 * t + 1] = pack_bf16x2(sbyte(s, 2), sbyte(s, 3));
+        }
+        *reinterpret_cast<uint4 *>(dst + 16 * nib + 8 * h) = v;
+    }
+    __device__ static float scale(const uint32_t (&b)[kWin], int blk)
+    {
+        return half_lo(b[0] >> (16 * blk));
+    }
 };
 
 template <> struct BFmt<FMT_Q8_0> {
@@ -149,6 +179,27 @@ template <> struct BFmt<FMT_Q8_0> {
             o[2 * t + 1] = pack_bf16x2(sbyte(q, 2) * d, sbyte(q, 3) * d);
         }
         *reinterpret_cast<uint4 *>(dst + 8 * h) = v;
+    }
+
+    // the quarter as integer codes q, exact in bf16
+    static constexpr float kCodeScale = 1.0f;
+    __device__ static void codes_quarter(const uint32_t (&b)[kWin], int blk, int h, __bf16 *dst)
+    {
+        uint4 v;
+        uint32_t *o = &v.x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i = 2 * h + t;
+            const uint32_t realigned = __builtin_amdgcn_alignbyte(b[i + 1], b[i], 2);
+            const uint32_t q = blk ? b[i + 1] : realigned;
+            o[2 * t] = pack_bf16x2(sbyte(q, 0), sbyte(q, 1));
+            o[2 * t + 1] = pack_bf16x2(sbyte(q, 2), sbyte(q, 3));
+        }
+        *reinterpret_cast<uint4 *>(dst + 8 * h) = v;
+    }
+    __device__ static float scale(const uint32_t (&b)[kWin], int blk)
+    {
+        return half_lo(b[0] >> (16 * blk));
     }
 };
 
@@ -469,6 +520,121 @@ hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, 
     return hipGetLastError();
 }
 
+// f32-exact variant for 5 .. 16 activation rows (the GEMV entry points'
+// accuracy): the same slices and interleaved K steps, but the 32 A rows
+// hold hi = bf16(x) of the (up to 16) activation rows in rows 0-15 and
+// lo = bf16(x - hi) in rows 16-31, the weight operand holds the integer
+// codes (exact in bf16), and each block's two MFMAs run into a fresh f32
+// tile that is scaled by the block's fp16 d in f32 before it is added to
+// the accumulators. Products are exact; y[m] = (C[m] + C[m + 16]) x the
+// codes' scale.
+template <int FMT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
+    const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
+    int M, int N, int K)
+{
+    constexpr int BM = 32, BN = 32;
+    constexpr int REGION = (BM + BN) * LDK + 2 * BN * 2;   // bf16: A, B, then 64 f32 scales
+    static_assert(1024 * 4 <= REGION * 2, "wave partials fit the wave's region");
+    __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
+
+    using BF = BFmt<FMT>;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int n0 = blockIdx.x * BN;
+    const int P = K / 64;
+    const int row_bytes = P * BF::kPairBytes;
+    __bf16 *As = lds + wave * REGION;
+    __bf16 *Bs = As + BM * LDK;
+    float *ds = reinterpret_cast<float *>(Bs + BN * LDK);  // [BN][2]
+
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x), 0, M * K * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, min(BN, N - n0) * row_bytes,
+        kBufferWord3);
+    // activation row lane / 16 + 4 u (u < 4), columns 4 (lane % 16) .. +3
+    const int a_col = 4 * (lane % 16);
+    const int a_voff0 = ((lane / 16) * K + a_col) * 4;
+    const int b_row = lane / 2, b_blk = lane % 2;
+    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
+
+    float4 a_reg[4];
+    uint32_t b_reg[BF::kWin];
+    auto load = [&](int p) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
+            a_reg[u] = __builtin_bit_cast(float4, v);
+        }
+        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg);
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const f32x16 zero = acc;
+
+    const int frow = lane % 32, fk = 8 * (lane / 32);
+    load(min(wave, P - 1));
+    for (int p = wave; p < P; p += WAVES) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 v = a_reg[u];
+            uint2 hi, lo;
+            hi.x = pack_bf16x2(v.x, v.y);
+            hi.y = pack_bf16x2(v.z, v.w);
+            lo.x = pack_bf16x2(v.x - bf16_round(v.x), v.y - bf16_round(v.y));
+            lo.y = pack_bf16x2(v.z - bf16_round(v.z), v.w - bf16_round(v.w));
+            const int r = lane / 16 + 4 * u;
+            *reinterpret_cast<uint2 *>(&As[r * LDK + a_col]) = hi;
+            *reinterpret_cast<uint2 *>(&As[(r + 16) * LDK + a_col]) = lo;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            BF::codes_quarter(b_reg, b_blk, q, &Bs[b_row * LDK + 32 * b_blk]);
+        ds[2 * b_row + b_blk] = BF::scale(b_reg, b_blk);
+        load(min(p + WAVES, P - 1));            // registers are free again
+        wave_lds_sync();
+        const float d0 = ds[2 * frow], d1 = ds[2 * frow + 1];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16 c = zero;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int s = 2 * blk + s2;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[frow * LDK + fk + 16 * s]);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[frow * LDK + fk + 16 * s]);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+            }
+            const float d = blk ? d1 : d0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = fmaf(d, c[e], acc[e]);
+        }
+        wave_lds_sync();                        // operands read before the next writes
+    }
+
+    // partials red[wave][e][lane] = C[8 (e / 4) + 4 (lane / 32) + e % 4][lane % 32];
+    // activation row m = that row for e < 8, its lo part at e + 8
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 8 * 64; o += 64 * WAVES) {
+        const int l = o % 64, e = o / 64;
+        const int m = 8 * (e / 4) + 4 * (l / 32) + e % 4;
+        const int n = n0 + l % 32;
+        float hi = 0.f, lo = 0.f;
+#pragma unroll
+        for (int q = 0; q < WAVES; ++q) {
+            hi += red[(q * 16 + e) * 64 + l];
+            lo += red[(q * 16 + e + 8) * 64 + l];
+        }
+        if (m < M && n < N) y[(int64_t)m * N + n] = (hi + lo) * BF::kCodeScale;
+    }
+}
+
 template <int FMT, class TL>
 hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                         hipStream_t stream)
@@ -509,6 +675,20 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 }
 
 }  // namespace
+
+hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
+                              int N, int K, hipStream_t stream)
+{
+    if (M > 16) return hipErrorInvalidValue;
+    const dim3 grid((N + 31) / 32);
+    if (fmt == FMT_Q4_0)
+        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 8>), grid, dim3(512), 0, stream, x, w, y,
+                           M, N, K);
+    else
+        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q8_0, 8>), grid, dim3(512), 0, stream, x, w, y,
+                           M, N, K);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream)

@@ -106,6 +106,9 @@ QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N, (int)K,
                                               stream));
+    if (M > 8 && N >= 8192)
+        return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
+                                                  (int)K, stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
                                                (int)K, stream));
 }
@@ -120,6 +123,9 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N, (int)K,
                                               stream));
+    if (M > 8 && N >= 8192)
+        return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
+                                                  (int)K, stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
                                                (int)K, stream));
 }

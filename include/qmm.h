@@ -82,7 +82,8 @@ typedef enum qmm_status {
  * weights stream from HBM once per call. Up to 4 rows take f32 FMAs on
  * codes converted exactly to f32, and each row rounds as in a one-row call
  * of the same launch shape; 5 to 16 rows take the bf16 matrix cores with
- * exact products (codes exact in bf16, x split into two bf16 terms).
+ * exact products (codes exact in bf16, x split into two bf16 terms, the
+ * fp16 scale applied per block in f32).
  */
 QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

@@ -138,6 +138,9 @@ GEMV_SHAPES = [
     (5, 2048, 8192), (12, 2049, 8448),
     # one row, wide N, K <= 4096 (32 lanes x 2 chunks per row, ragged K)
     (1, 32769, 3328),
+    # 9-16 rows with N >= 8192 (f32-exact 32-row weight slices): ragged M and
+    # N, K steps not a multiple of the waves, wide N
+    (9, 8193, 1024), (12, 8192, 8448), (16, 65537, 512), (13, 9000, 256),
 ]
 
 
