@@ -681,9 +681,11 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
 {
     if (M > 16) return hipErrorInvalidValue;
     const dim3 grid((N + 31) / 32);
+    // Q4_0: 16 waves (more K steps in flight per slice: M = 16, N = 2048,
+    // K = 8192 20.3 us against 22.0 with 8); Q8_0: 8 (its wider windows)
     if (fmt == FMT_Q4_0)
-        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 8>), grid, dim3(512), 0, stream, x, w, y,
-                           M, N, K);
+        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 16>), grid, dim3(1024), 0, stream, x, w,
+                           y, M, N, K);
     else
         hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q8_0, 8>), grid, dim3(512), 0, stream, x, w, y,
                            M, N, K);

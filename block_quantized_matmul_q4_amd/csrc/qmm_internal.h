@@ -27,8 +27,9 @@ hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, i
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream);
 // f32-exact GEMV on the matrix cores over 32-row weight slices, M <= 16
-// (taken for 9 <= M <= 16 with N >= 8192: at M = 16, N = 8192, K = 2048
-// 8.5 us against 10.6 us; Q8_0, N = 65536: 54 against 79 us)
+// (taken for 9 <= M <= 16, Q8_0 only from N = 8192: Q4_0 at M = 16,
+// N = 8192, K = 2048 7.9 us against 10.6 us on the small-M kernel; Q8_0 at
+// N = 65536 54 against 79 us)
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream);
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
