@@ -231,8 +231,10 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     static_assert(16 * SP * CH % ST == 0, "staging must tile the pass exactly");
     constexpr int REGION = CH * SP * XS;        // floats per staging unit and row
     constexpr int UNITS = SX ? 1 : WG / 64;
-    static_assert(WG / 64 * RPT * MR <= UNITS * MR * REGION, "reduction fits in LDS");
     __shared__ __attribute__((aligned(16))) float xs_all[UNITS * MR * REGION];
+    // per-wave partials of rows split over several waves, apart from the
+    // activations so that no barrier has to wait for their last readers
+    __shared__ float red[WPR > 1 ? WG / 64 * RPT * MR : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid % 64, wave = tid / 64;
@@ -390,8 +392,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
             }
         }
     } else {
-        __syncthreads();                        // every wave is done with xs
-        float *red = xs_all;                    // [WG / 64][RPT][MR]
+        // red[wave][RPT][MR]
         if (lane == 63) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j)
