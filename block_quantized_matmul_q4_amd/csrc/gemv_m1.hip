@@ -195,7 +195,8 @@ template <> struct Pair<FMT_Q8_0> {
 //  2. each thread issues the loads of all its CH * RPT weight pairs (HBM);
 //  3. the activations go to LDS, in rows of 64 floats padded by 4 so that
 //     consecutive lanes' 16-byte reads fall in distinct banks; SX needs one
-//     workgroup barrier here (the weights are already in flight), per-wave
+//     workgroup barrier after the writes (the weights are already in
+//     flight) and, from the second pass on, one before them; per-wave
 //     staging none;
 //  4. per chunk, each thread runs the FMAs for its RPT weight rows against
 //     its 64 activations of each of the MR rows. With one activation row the
@@ -296,8 +297,11 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
         // 3. activations to LDS
-        if constexpr (SX) __syncthreads();      // previous pass's readers done
-        else __builtin_amdgcn_wave_barrier();
+        if constexpr (SX) {
+            if (c0 != 0) __syncthreads();       // previous pass's readers done
+        } else {
+            __builtin_amdgcn_wave_barrier();
+        }
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
 #pragma unroll
