@@ -1,3 +1,7 @@
+// Matrix-core kernels over GGUF Q4_0 / Q8_0 weights: the prefill GEMM's
+// tile kernel (described here), the medium-M GEMM (5-128 rows) and the
+// f32-exact weight-slice GEMV (9-16 rows), each introduced where it starts.
+//
 // Prefill GEMM over GGUF Q4_0 or Q8_0 weights on the bf16 matrix cores:
 // y[m][n] = sum_k bf16(x[m][k]) * bf16(w[n][k]) with f32 accumulation, where
 // w = d * (q - 8) (Q4_0) or d * q (Q8_0) is exact in f32 before its one
