@@ -446,6 +446,20 @@ def test_errors_raise_on_gpu():
     assert e.value.status == qmm.QMM_EINVAL
 
 
+def test_randomized_wide_shapes(orc):
+    """Seeded randomized differential test with wide N (4000-9000): the launch
+    shapes that only wide matrices select (64-row medium-M bands, Q8_0 weight
+    slices, ...), at ragged sizes."""
+    rng = np.random.default_rng(77)
+    for case in range(24):
+        entry = "gemv" if case % 3 else "gemm"
+        fmt = "q8_0" if case % 2 else "q4_0"
+        m = int(rng.integers(1, 17)) if entry == "gemv" else int(rng.integers(5, 129))
+        n = int(rng.integers(4000, 9001))
+        k = 256 * int(rng.integers(1, 9 if entry == "gemv" else 5))
+        check(orc, entry, fmt, m, n, k, seed=5000 + case)
+
+
 def test_randomized_small_shapes(orc):
     """Seeded randomized differential test over many small shapes."""
     rng = np.random.default_rng(2024)
