@@ -362,11 +362,15 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
         __syncthreads();
     };
     // two steps per iteration (the weight registers and the LDS buffers
-    // alternate with the step's parity); P is even, K being a multiple of 256
-    for (int p = 0; p < P; p += 2) {
+    // alternate with the step's parity), then an odd last step: it reads
+    // buffer 0, written during the step before, and its own conversion goes
+    // to buffer 1, which nobody reads any more
+    int p = 0;
+    for (; p + 1 < P; p += 2) {
         step(p, std::integral_constant<int, 0>());
         step(p + 1, std::integral_constant<int, 1>());
     }
+    if (p < P) step(p, std::integral_constant<int, 0>());
 
     // ---- epilogue: acc[i][j][e] = C[32i + 8(e/4) + 4(lane/32) + e%4][32j + lane%32]
     // Columns past N get bit 31 set in their offset, which puts them outside
@@ -643,8 +647,8 @@ template <int FMT, class TL>
 hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                         hipStream_t stream)
 {
-    // the kernel runs K steps of 64 in pairs
-    if (K % (2 * BK) != 0) return hipErrorInvalidValue;
+    // the kernel runs whole K steps of 64
+    if (K % BK != 0) return hipErrorInvalidValue;
     const int tiles_m = (M + TL::BM - 1) / TL::BM;
     const int tiles_n = (N + TL::BN - 1) / TL::BN;
     const int tiles = tiles_m * tiles_n;

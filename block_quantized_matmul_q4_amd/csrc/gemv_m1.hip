@@ -471,7 +471,7 @@ template <int FMT, int MR>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
-    const int P = K / 64;  // K % 256 == 0, so P % 4 == 0
+    const int P = K / 64;  // K % 64 == 0
     if (P <= 4) return launch<FMT, 4, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);
     if (P <= 8) return launch<FMT, 8, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);
     if (P <= 16) return launch<FMT, 16, 2, 256, 1, false, false, MR>(x, w, y, M, N, P, stream);

@@ -43,9 +43,9 @@ int validate(const char *fn, const float *x, const void *w, const float *y,
     if (K % 32)
         return fail(QMM_EINVAL, "%s: K=%lld is not a multiple of 32 (the block size)", fn,
                     (long long)K);
-    if (K % 256 || K > QMM_MAX_K)
+    if (K % 64 || K > QMM_MAX_K)
         return fail(QMM_EUNSUPPORTED,
-                    "%s: K=%lld unsupported (need K %% 256 == 0 and K <= %d)", fn,
+                    "%s: K=%lld unsupported (need K %% 64 == 0 and K <= %d)", fn,
                     (long long)K, QMM_MAX_K);
     // Sizes: every index the kernels form fits in int32 element counts for
     // x and y rows, and byte offsets are 64-bit.
@@ -106,7 +106,8 @@ QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N, (int)K,
                                               stream));
-    if (M > 8)
+    // the 16x16 small-M kernel takes K in slices of 256
+    if (M > 8 || K % 256)
         return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
                                                   (int)K, stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
@@ -123,7 +124,7 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N, (int)K,
                                               stream));
-    if (M > 8 && N >= 8192)
+    if ((M > 8 && N >= 8192) || K % 256)
         return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
                                                   (int)K, stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,

@@ -16,8 +16,9 @@ constexpr int kQ8Bytes = 34;         // fp16 d + 32 int8
 inline constexpr int block_bytes(int fmt) { return fmt == FMT_Q4_0 ? kQ4Bytes : kQ8Bytes; }
 
 // Launchers. Arguments are already validated by the C-ABI layer:
-// pointers non-null and aligned, 1 <= M, 1 <= N, 256 <= K <= 65536,
-// K % 256 == 0, N and M * N within int32 range. Each returns the
+// pointers non-null and aligned, 1 <= M, 1 <= N, 64 <= K <= 65536,
+// K % 64 == 0 (whole pairs of blocks per row), N and M * N within int32
+// range; launch_gemv_small_m also needs K % 256 == 0. Each returns the
 // hipGetLastError() of its launch.
 // GEMV with f32 FMAs for M <= kGemvRowsMax activation rows (the weights
 // streamed once per launch); more rows take the matrix-core small-M kernel.

@@ -32,8 +32,9 @@
  *                    M > 16 for a GEMV entry point; y overlapping x or w;
  *                    a byte size that overflows int64.
  *   QMM_EALIGN       x or w not 16-byte aligned, y not 4-byte aligned.
- *   QMM_EUNSUPPORTED K not a multiple of 256 (keeps every weight row
- *                    16-byte aligned), or K > QMM_MAX_K; for the GEMM entry
+ *   QMM_EUNSUPPORTED K not a multiple of 64 (every weight row then holds
+ *                    whole, dword-aligned pairs of blocks), or K > QMM_MAX_K;
+ *                    for the GEMM entry
  *                    points also N > QMM_GEMM_MAX_N or more than
  *                    INT32_MAX - 8 output tiles of 256 x 256.
  *   QMM_EHIP         the HIP runtime reported an error at launch.

@@ -141,6 +141,9 @@ GEMV_SHAPES = [
     # 9-16 rows with N >= 8192 (f32-exact 32-row weight slices): ragged M and
     # N, K steps not a multiple of the waves, wide N
     (9, 8193, 1024), (12, 8192, 8448), (16, 65537, 512), (13, 9000, 256),
+    # K a multiple of 64 but not of 256 (pair counts 1, 5, 14, 17, 47)
+    (1, 300, 64), (1, 4097, 896), (2, 1000, 320), (3, 2049, 1088), (4, 65537, 896),
+    (6, 500, 896), (8, 8192, 3008), (12, 700, 320), (16, 9000, 1088),
 ]
 
 
@@ -186,7 +189,11 @@ GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                # medium M: 64-row bands (N >= 4096), 32-row bands, more waves
                # than K steps (K = 256), K steps not a multiple of the waves
                (64, 4100, 1024), (100, 8193, 2048), (33, 2048, 8448), (128, 300, 256),
-               (6, 64, 256), (128, 4096, 512)]
+               (6, 64, 256), (128, 4096, 512),
+               # K a multiple of 64 but not of 256: odd step counts on the
+               # tile kernels (15, 17, 1), medium M, GEMV routing
+               (300, 300, 960), (1000, 520, 1088), (2100, 4100, 1088), (129, 257, 64),
+               (40, 8192, 896), (3, 100, 320)]
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
@@ -198,7 +205,7 @@ def test_gemm_shapes(orc, fmt, m, n, k):
 # Shapes with at least 256 tiles of 256 x 256 (the large-tile kernel; the
 # shapes above use the 128 x 128 one), with ragged M and N edges.
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
-@pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512)])
+@pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512), (4097, 4100, 320)])
 def test_gemm_large_tile_shapes(orc, fmt, m, n, k):
     check(orc, "gemm", fmt, m, n, k, seed=m + n)
 
@@ -359,7 +366,7 @@ def run_ffn(x, wg, wu, n, k):
 
 @pytest.mark.parametrize("n,k", [(8192, 2048), (1, 256), (1000, 256), (333, 512), (257, 1024),
                                  (4097, 1280), (100, 4096), (2048, 8192), (65, 16384),
-                                 (8200, 4352)])
+                                 (8200, 4352), (1000, 896), (300, 64)])
 def test_ffn_gate_up(orc, n, k):
     note(f"[parity] ffn_gate_up_q4_0 N={n} K={k}")
     x = synth.activations(1, k, seed=n)
@@ -456,7 +463,7 @@ def test_randomized_wide_shapes(orc):
         fmt = "q8_0" if case % 2 else "q4_0"
         m = int(rng.integers(1, 17)) if entry == "gemv" else int(rng.integers(5, 129))
         n = int(rng.integers(4000, 9001))
-        k = 256 * int(rng.integers(1, 9 if entry == "gemv" else 5))
+        k = 64 * int(rng.integers(1, 33 if entry == "gemv" else 17))
         check(orc, entry, fmt, m, n, k, seed=5000 + case)
 
 
