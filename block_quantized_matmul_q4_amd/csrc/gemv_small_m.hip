@@ -1,6 +1,7 @@
 // Small-M GEMV (2 <= M <= 16 activation rows: batched or speculative
 // decode) over GGUF Q4_0 / Q8_0 weights, on the bf16 matrix cores. The
-// C-ABI sends 5 <= M <= 8, and Q8_0 with 9 <= M <= 16 and N < 8192, here: up to 4
+// C-ABI sends 5 <= M <= 8, and Q8_0 with 9 <= M <= 16 and N < 8192, here when
+// K % 256 == 0 (each wave takes K in slices of 256): up to 4
 // rows the f32 FMA kernel that streams the weights for one row is faster
 // (it decodes each pair once for all rows), and from 9 rows over wide
 // matrices the 32-row weight-slice kernel is.
