@@ -401,10 +401,14 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
 // Medium M: few output tiles, so instead of one tile's K loop per compute
 // unit, a workgroup owns a 32-column slice of y for a band of 32 MT rows
 // (grid: column slices x row bands) and its WAVES waves take interleaved K
-// steps of 64 in parallel
-// (wave w: steps w, w + WAVES, ...), each with its own accumulators, meeting
-// in LDS at the end (summed in wave order). Same arithmetic as the tile
-// kernel: x and w rounded once to bf16 (RNE), f32 accumulation.
+// steps of 64 in parallel (wave w: steps w, w + WAVES, ...), each with its
+// own accumulators, meeting in LDS at the end (summed in wave order). Same
+// arithmetic as the tile kernel: x and w rounded once to bf16 (RNE), f32
+// accumulation.
+//
+// The waves never share LDS during the K loop: each wave's region holds its
+// own step, so the only synchronization inside the loop is the wave's own
+// ordering of its LDS writes before its reads (wave_lds_sync).
 //
 // Per step a wave loads its activation rows (16 lanes per row, a float4
 // each) and one weight block per lane (row lane / 2 of the slice, block
