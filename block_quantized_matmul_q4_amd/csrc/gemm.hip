@@ -298,14 +298,19 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     // Steps past the last one reload (and convert) the last step, into the
     // buffer nobody reads any more: the loop body has no branches, so the
     // waits for the registers' loads stay exact.
+    // Step 1's weight window is requested together with step 0, and each of
+    // its activation quarters as soon as step 0's quarter has been written,
+    // so that step 1 lands while step 0 is converted rather than one memory
+    // latency later.
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_a(0, q);
     load_b(b_reg[0], 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) convert(0, q, b_reg[0]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load_a(min(1, P - 1), q);
     load_b(b_reg[1], min(1, P - 1));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        convert(0, q, b_reg[0]);
+        load_a(min(1, P - 1), q);
+    }
     __syncthreads();
 
     // K step p out of LDS buffer PAR = p % 2. On entry the registers hold
