@@ -24,6 +24,10 @@ Timing:
   vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
   GEMM (M = 2048, and short prompts
   M = 16, 64, 128), reported under "rows".
+* HBM read references (bench_read.hip): the same timing over kernels that
+  only read, on the same 9.4 MB weight copies (a plain coalesced read and
+  the GEMV's 36-byte-pair pattern) and on 512 MiB buffers (the achievable
+  streaming rate), reported under "hbm_reference" and "rows".
 * decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
   at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
   weight copy, captured in one HIP graph; 5 replays bracketed by HIP events
@@ -117,6 +121,22 @@ class Hip:
         ms = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return ms.value
+
+
+def bench_read_library():
+    """bench_read.so (reference read kernels), built by __graft_entry__.build()
+    and compiled here only if it is missing."""
+    import __graft_entry__ as entry
+
+    path = entry.BENCH_READ_LIB
+    if not path.exists():
+        entry.build_bench_read()
+    lib = ctypes.CDLL(str(path))
+    for f in ("bench_read_plain", "bench_read_pairs"):
+        fn = getattr(lib, f)
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    return lib
 
 
 def summarize(us):
@@ -281,6 +301,29 @@ def main():
         "q4_0_gemv_ffn_down": dict(t_dn, bytes=bytes_dn,
                                    gbs=bytes_dn / (t_dn["mean_us"] * 1e-6) / 1e9),
     }
+
+    # ------------------------------------------------ HBM read references
+    # The same timing method over kernels that only read: one FFN weight
+    # copy (9.4 MB) per launch as a plain coalesced read and in the GEMV's
+    # own 36-byte-pair pattern, and 512 MiB per launch for the achievable
+    # streaming rate.
+    rd = bench_read_library()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    nb = w_up_h.nbytes
+    t_rp = time_launches(rd.bench_read_plain,
+                         [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)])
+    t_rq = time_launches(rd.bench_read_pairs,
+                         [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)])
+    big = [torch.randint(0, 256, (1 << 29,), dtype=torch.uint8, device=dev) for _ in range(2)]
+    t_rb = time_launches(rd.bench_read_plain,
+                         [(big[i % 2].data_ptr(), 1 << 29, sink.data_ptr()) for i in range(20)])
+    del big
+    achievable = (1 << 29) / (t_rb["mean_us"] * 1e-6) / 1e9
+    for key, t, b in (("hbm_read_plain_9mb", t_rp, nb), ("hbm_read_pairs_9mb", t_rq, nb),
+                      ("hbm_read_plain_512mib", t_rb, 1 << 29)):
+        rows[key] = dict(t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9)
+    log(f"[bench] plain read 9.4 MB {t_rp['mean_us']:.2f} us, pair-pattern read "
+        f"{t_rq['mean_us']:.2f} us, 512 MiB {achievable:.0f} GB/s")
 
     if not args.decode_only:
         # small-M GEMV on the up shape (same weight pool)
@@ -471,6 +514,14 @@ def main():
         "graph_step_bitwise_vs_eager": graph_ok,
         "gpu_event_us_per_step": gpu_ms * 1e3 / args.steps,
         "pct_hbm_peak": 100 * value / HBM_PEAK_GBS,
+        "hbm_reference": {
+            "achievable_read_gbs": achievable,
+            "roofline_achieved_frac_of_achievable": achieved / achievable,
+            "plain_read_us_per_ffn_weight_copy": t_rp["mean_us"],
+            "gemv_pattern_read_us_per_ffn_weight_copy": t_rq["mean_us"],
+            "note": "read-only kernels timed like the GEMVs: a 9.4 MB read per launch "
+                    "costs this much before any arithmetic",
+        },
         "rows": rows,
         "device": props.name,
     }

@@ -135,3 +135,19 @@ def test_ffn_gate_up_rejected_before_launch(args, status, fragment):
     assert got == status, (args, qmm.qmm_last_error())
     assert fragment in qmm.qmm_last_error()
     assert "qmm_ffn_gate_up_q4_0" in qmm.qmm_last_error()
+
+
+def test_bench_read_kernels_load_and_reject_bad_arguments():
+    """bench.py's reference read kernels: built by build(), loadable on the
+    host, and their argument checks fail before any launch."""
+    import sys
+
+    sys.path.insert(0, str(ROOT))
+    import bench
+
+    lib = bench.bench_read_library()
+    assert lib.bench_read_plain(None, 16, A, None) == 1
+    assert lib.bench_read_plain(A, 24, A, None) == 1          # not a multiple of 16
+    assert lib.bench_read_plain(A + 4, 16, A, None) == 1      # not 16-byte aligned
+    assert lib.bench_read_pairs(A, 40, A, None) == 1          # not a multiple of 36
+    assert lib.bench_read_pairs(A, 36, None, None) == 1
