@@ -196,8 +196,9 @@ template <> struct Pair<FMT_Q8_0> {
 //  3. the activations go to LDS, in rows of 64 floats padded by 4 so that
 //     consecutive lanes' 16-byte reads fall in distinct banks; SX needs one
 //     workgroup barrier after the writes (the weights are already in
-//     flight) and, from the second pass on, one before them; per-wave
-//     staging none;
+//     flight; where measured faster it waits for LDS only, so each wave
+//     reads its activations while its weights arrive) and, from the second
+//     pass on, one before them; per-wave staging none;
 //  4. per chunk, each thread runs the FMAs for its RPT weight rows against
 //     its 64 activations of each of the MR rows. With one activation row the
 //     codes are converted as they are used; with several, a pair is decoded
@@ -210,6 +211,17 @@ __device__ __forceinline__ float gelu_tanh(float g)
 {
     const float c = 0.7978845608028654f;        // sqrt(2 / pi)
     return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its weight loads still in flight (__syncthreads() waits for every
+// outstanding memory access first). The scheduling barriers keep the
+// compiler from moving work across it.
+__device__ __forceinline__ void lds_only_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED, int MR>
@@ -232,6 +244,12 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     static_assert(16 * SP * CH % ST == 0, "staging must tile the pass exactly");
     constexpr int REGION = CH * SP * XS;        // floats per staging unit and row
     constexpr int UNITS = SX ? 1 : WG / 64;
+    // After the shared staging, let each wave go on to its LDS reads while
+    // its weights are still arriving. Measured faster for one activation
+    // row with T = 128 (FFN down, K = 8192, N = 2048: 4.87 -> 4.67 us) and
+    // with T = 32 in 256-thread workgroups; slower with 512-thread
+    // workgroups of T = 32 or T = 64 (Q4_0, N = 262144, K = 2048: 58 -> 62 us).
+    constexpr bool LB = SX && !GATED && MR == 1 && (T == 128 || (T == 32 && WG == 256));
     __shared__ __attribute__((aligned(16))) float xs_all[UNITS * MR * REGION];
     // per-wave partials of rows split over several waves, apart from the
     // activations so that no barrier has to wait for their last readers
@@ -311,7 +329,8 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
                     make_float4(xsx[m][u], xsy[m][u], xsz[m][u], xsw[m][u]);
             }
         }
-        if constexpr (SX) __syncthreads();
+        if constexpr (LB) lds_only_barrier();
+        else if constexpr (SX) __syncthreads();
         else __builtin_amdgcn_wave_barrier();
         // 4. per chunk: FMAs
 #pragma unroll
