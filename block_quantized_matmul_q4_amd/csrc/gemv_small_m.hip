@@ -137,6 +137,18 @@ __device__ __forceinline__ void split4(const float4 v, bf16x4 &hi, bf16x4 &lo)
     }
 }
 
+// LDS dword address of A-fragment slot s (one lane's 16 bytes of one block's
+// operand). Slot group G = s / 16 starts 4 (G + G / 8) dwords further on, so
+// the staging writes, in which the lanes of one instruction hold the same
+// activation row in slots 16 apart (different blocks and lane groups), fall
+// in different banks, while each group's 16 slots (read by 16 lanes) stay
+// contiguous.
+__device__ __forceinline__ int afrag(int s)
+{
+    const int g = s >> 4;
+    return 4 * s + 4 * (g + (g >> 3));
+}
+
 template <int FMT, bool PACK, int NT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
@@ -145,7 +157,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     using L = Fmt<FMT>;
     constexpr int TERMS = PACK ? 1 : 2;             // A operands per block
     constexpr int MMAX = PACK ? 8 : 16;
-    constexpr int AF = BPW * TERMS * 64 * 4;        // A-fragment dwords per wave
+    constexpr int NG = BPW * TERMS * 4;             // A-fragment slot groups per wave
+    constexpr int AF = NG * 64 + 4 * (NG + NG / 8); // A-fragment dwords per wave, with shifts
     constexpr int WROWS = 16 * NT;                  // weight rows per workgroup
     constexpr int PPL = WROWS * PPW / 64;           // pairs loaded per lane
     constexpr int WD = WROWS * PPW * L::kPairDwords;  // weight dwords per wave
@@ -207,9 +220,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
                     const int rl = PACK ? M + m : m;  // A row of the lo part
                     const int tl = PACK ? 0 : 1;      // A operand of the lo part
                     *reinterpret_cast<bf16x4 *>(
-                        &af[((b * TERMS + 0) * 64 + 16 * g + m) * 4 + e0 / 2]) = hi;
+                        &af[afrag((b * TERMS + 0) * 64 + 16 * g + m) + e0 / 2]) = hi;
                     *reinterpret_cast<bf16x4 *>(
-                        &af[((b * TERMS + tl) * 64 + 16 * g + rl) * 4 + e0 / 2]) = lo;
+                        &af[afrag((b * TERMS + tl) * 64 + 16 * g + rl) + e0 / 2]) = lo;
                 }
             }
         }
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
             bf16x8 a[TERMS];
 #pragma unroll
             for (int tt = 0; tt < TERMS; ++tt)
-                a[tt] = *reinterpret_cast<const bf16x8 *>(&af[((b * TERMS + tt) * 64 + lane) * 4]);
+                a[tt] = *reinterpret_cast<const bf16x8 *>(&af[afrag((b * TERMS + tt) * 64 + lane)]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint32_t *pair = wl + ((16 * t + col) * PPW + b / 2) * L::kPairDwords;
