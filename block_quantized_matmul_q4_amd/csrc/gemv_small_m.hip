@@ -161,7 +161,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     constexpr int AF = NG * 64 + 4 * (NG + NG / 8); // A-fragment dwords per wave, with shifts
     constexpr int WROWS = 16 * NT;                  // weight rows per workgroup
     constexpr int PPL = WROWS * PPW / 64;           // pairs loaded per lane
-    constexpr int WD = WROWS * PPW * L::kPairDwords;  // weight dwords per wave
+    // a weight row's PPW pairs plus one dword, so that the rows (and the
+    // lanes staging them) start in different banks
+    constexpr int WROW = PPW * L::kPairDwords + 1;
+    constexpr int WD = WROWS * WROW;                // weight dwords per wave
     constexpr int REGION = AF + WD;
     static_assert(PPL * 64 == WROWS * PPW, "pairs must tile the wave");
     static_assert(PPW % PPL == 0, "a lane's pairs lie in one weight row");
@@ -212,23 +215,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
             const int b = lane / 8, kk = 4 * (lane % 8);
             int g, e0;
             L::slot(kk, g, e0);
+            // slots of A row 0 for the hi and lo parts; row r (< 16) of the
+            // same fragment is 4 r dwords further on (same slot group)
+            const int tl = PACK ? 0 : 1;              // A operand of the lo part
+            uint32_t *ahi = &af[afrag((b * TERMS + 0) * 64 + 16 * g) + e0 / 2];
+            uint32_t *alo = &af[afrag((b * TERMS + tl) * 64 + 16 * g) + e0 / 2];
 #pragma unroll
             for (int m = 0; m < MMAX; ++m) {
                 if (m < M) {
                     bf16x4 hi, lo;
                     split4(xv[m], hi, lo);
                     const int rl = PACK ? M + m : m;  // A row of the lo part
-                    const int tl = PACK ? 0 : 1;      // A operand of the lo part
-                    *reinterpret_cast<bf16x4 *>(
-                        &af[afrag((b * TERMS + 0) * 64 + 16 * g + m) + e0 / 2]) = hi;
-                    *reinterpret_cast<bf16x4 *>(
-                        &af[afrag((b * TERMS + tl) * 64 + 16 * g + rl) + e0 / 2]) = lo;
+                    *reinterpret_cast<bf16x4 *>(ahi + 4 * m) = hi;
+                    *reinterpret_cast<bf16x4 *>(alo + 4 * rl) = lo;
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < PPL; ++u)
-            L::relayout(D[u], wl + (lrow * PPW + lp0 + u) * L::kPairDwords);
+            L::relayout(D[u], wl + lrow * WROW + (lp0 + u) * L::kPairDwords);
         __builtin_amdgcn_wave_barrier();
         // ---- 3. matrix cores
         const int col = lane % 16, g = lane / 16;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
                 a[tt] = *reinterpret_cast<const bf16x8 *>(&af[afrag((b * TERMS + tt) * 64 + lane)]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint32_t *pair = wl + ((16 * t + col) * PPW + b / 2) * L::kPairDwords;
+                const uint32_t *pair = wl + (16 * t + col) * WROW + (b / 2) * L::kPairDwords;
                 bf16x8 bq;
                 float d;
                 L::b_operand(pair, b & 1, g, bq, d);
