@@ -245,11 +245,12 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     constexpr int REGION = CH * SP * XS;        // floats per staging unit and row
     constexpr int UNITS = SX ? 1 : WG / 64;
     // After the shared staging, let each wave go on to its LDS reads while
-    // its weights are still arriving. Measured faster for one activation
-    // row with T = 128 (FFN down, K = 8192, N = 2048: 4.87 -> 4.67 us) and
-    // with T = 32 in 256-thread workgroups; slower with 512-thread
-    // workgroups of T = 32 or T = 64 (Q4_0, N = 262144, K = 2048: 58 -> 62 us).
-    constexpr bool LB = SX && !GATED && MR == 1 && (T == 128 || (T == 32 && WG == 256));
+    // its weights are still arriving. Measured faster with T = 128 (FFN
+    // down, K = 8192, N = 2048: 4.87 -> 4.67 us; gated, 6.93 -> 6.47 us)
+    // and with T = 32 in 256-thread workgroups (FFN up shape, 4 activation
+    // rows: 6.62 -> 6.30 us); slower with 512-thread workgroups of T = 32 or
+    // T = 64 (Q4_0, N = 262144, K = 2048: 58 -> 62 us).
+    constexpr bool LB = SX && (T == 128 || (T == 32 && WG == 256));
     __shared__ __attribute__((aligned(16))) float xs_all[UNITS * MR * REGION];
     // per-wave partials of rows split over several waves, apart from the
     // activations so that no barrier has to wait for their last readers
