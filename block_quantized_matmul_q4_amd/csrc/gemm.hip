@@ -295,13 +295,13 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
 
     const int frow = lane % 32, fk = 8 * (lane / 32);
 
+    // Prologue: step 0 is converted into buffer 0. Step 1's weight window is
+    // requested together with step 0, and each of its activation quarters
+    // as soon as step 0's quarter has been written, so that step 1 lands
+    // while step 0 is converted rather than one memory latency later.
     // Steps past the last one reload (and convert) the last step, into the
     // buffer nobody reads any more: the loop body has no branches, so the
     // waits for the registers' loads stay exact.
-    // Step 1's weight window is requested together with step 0, and each of
-    // its activation quarters as soon as step 0's quarter has been written,
-    // so that step 1 lands while step 0 is converted rather than one memory
-    // latency later.
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_a(0, q);
     load_b(b_reg[0], 0);
