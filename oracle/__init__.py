@@ -1,7 +1,8 @@
 """CPU oracle for the block-quantized matmul -- TEST INFRASTRUCTURE ONLY.
 
 Plain f64 reference (``qmm_oracle.c``) for y = x * W^T over GGUF Q4_0 / Q8_0
-weight blocks, plus the error-bound scale s = sum_k |x_k * w_k|. Only the
+weight blocks and Q4_K super-blocks, plus the error-bound scale
+s = sum_k |x_k * w_k|. Only the
 tests, the smoke check and the benchmark's CPU-baseline leg may import this
 package; the product path (the HIP library and its binding) never does, and
 the two share no code.
@@ -22,7 +23,8 @@ HERE = pathlib.Path(__file__).resolve().parent
 SOURCE = HERE / "qmm_oracle.c"
 LIBRARY = HERE / "libqmm_oracle.so"
 
-_FMT_BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+# format -> (weights per block, bytes per block)
+_FMT_BLOCK = {"q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144)}
 
 
 class Oracle:
@@ -40,11 +42,11 @@ class Oracle:
                                       ctypes.c_void_p)
         lib.qmm_oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.qmm_oracle_half_to_double.restype = ctypes.c_double
-        for name in ("qmm_oracle_q4_0", "qmm_oracle_q8_0"):
+        for name in ("qmm_oracle_q4_0", "qmm_oracle_q8_0", "qmm_oracle_q4_k"):
             fn = getattr(lib, name)
             fn.argtypes = [f32p, u8p, i64, i64, i64, f64p, f64p]
             fn.restype = None
-        for name in ("qmm_oracle_q4_0_at", "qmm_oracle_q8_0_at"):
+        for name in ("qmm_oracle_q4_0_at", "qmm_oracle_q8_0_at", "qmm_oracle_q4_k_at"):
             fn = getattr(lib, name)
             fn.argtypes = [f32p, u8p, i64, i64p, i64p, i64, f64p, f64p]
             fn.restype = None
@@ -64,9 +66,10 @@ class Oracle:
         w = np.ascontiguousarray(w, dtype=np.uint8)
         if x.ndim != 2 or x.shape[1] != k:
             raise ValueError(f"x shape {x.shape} does not match K={k}")
-        if k % 32:
-            raise ValueError("K must be a multiple of 32")
-        row = k // 32 * _FMT_BLOCK_BYTES[fmt]
+        per, nbytes = _FMT_BLOCK[fmt]
+        if k % per:
+            raise ValueError(f"K must be a multiple of {per} for {fmt}")
+        row = k // per * nbytes
         if w.size != n * row:
             raise ValueError(f"w has {w.size} bytes, expected {n * row}")
         return x, w
@@ -84,7 +87,7 @@ class Oracle:
         y = np.empty((m, n), dtype=np.float64)
         s = np.empty((m, n), dtype=np.float64)
         if m and n:
-            fn = self._lib.qmm_oracle_q4_0 if fmt == "q4_0" else self._lib.qmm_oracle_q8_0
+            fn = getattr(self._lib, f"qmm_oracle_{fmt}")
             fn(x.ctypes.data, w.ctypes.data, m, n, k, y.ctypes.data, s.ctypes.data)
         return y, s
 
@@ -119,8 +122,7 @@ class Oracle:
         y = np.empty(ms.size, dtype=np.float64)
         s = np.empty(ms.size, dtype=np.float64)
         if ms.size:
-            fn = (self._lib.qmm_oracle_q4_0_at if fmt == "q4_0"
-                  else self._lib.qmm_oracle_q8_0_at)
+            fn = getattr(self._lib, f"qmm_oracle_{fmt}_at")
             fn(x.ctypes.data, w.ctypes.data, k, ms.ctypes.data, ns.ctypes.data,
                ms.size, y.ctypes.data, s.ctypes.data)
         return y, s
@@ -143,3 +145,7 @@ def q4_0(x, w, n, k):
 
 def q8_0(x, w, n, k):
     return load().matmul("q8_0", x, w, n, k)
+
+
+def q4_k(x, w, n, k):
+    return load().matmul("q4_k", x, w, n, k)

@@ -2,7 +2,8 @@
  * qmm_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, obviously correct CPU reference for the block-quantized
- * weight matmul y = x * W^T over GGUF Q4_0 / Q8_0 weight blocks. Only the
+ * weight matmul y = x * W^T over GGUF Q4_0 / Q8_0 weight blocks (and Q4_K
+ * super-blocks, further down). Only the
  * test suite, the smoke check and the benchmark's CPU-baseline leg may load
  * this library; the product path never calls it and shares no code with it.
  *
@@ -143,6 +144,89 @@ void qmm_oracle_q8_0_at(const float *x, const uint8_t *w, int64_t K,
                         double *y, double *s)
 {
     at(1, x, w, K, ms, ns, count, y, s);
+}
+
+/*
+ * Q4_K, the k-quant 4-bit format the pages keep for their CLIP/CLAP path
+ * ("Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3, and
+ * GLiNER2", section Summary). The pages name it without a layout; GGUF's
+ * is taken. A super-block of 256 weights takes 144 bytes:
+ *   bytes 0-1   fp16 d      (scale of the sub-block scales)
+ *   bytes 2-3   fp16 dmin   (scale of the sub-block minimums)
+ *   bytes 4-15  eight 6-bit sub-block scales sc[j] and eight 6-bit
+ *               minimums mn[j], j = 0..7 (bit placement below)
+ *   bytes 16-143 nibbles: weight 64c + i (c = 0..3, i < 32) is the low
+ *               nibble of byte 16 + 32c + i and belongs to sub-block 2c;
+ *               weight 64c + 32 + i is the high nibble of the same byte
+ *               and belongs to sub-block 2c + 1.
+ *   w = d * sc[j] * q - dmin * mn[j] for a weight of sub-block j.
+ * The twelve scale bytes b[0..11]: for j < 4, sc[j] is the low 6 bits of
+ * b[j] and mn[j] the low 6 bits of b[4 + j]; for j >= 4, the low 4 bits of
+ * sc[j] are the low nibble of b[4 + j] and of mn[j] its high nibble, and
+ * their top 2 bits are the top 2 bits of b[j - 4] (sc) and b[j] (mn).
+ *
+ * Exactness: d * sc * q has at most 11 + 6 + 4 bits and dmin * mn 17; their
+ * difference is exact in f64 unless d and dmin lie more than 2^32 apart,
+ * and so is its product with an f32 activation unless that difference needs
+ * more than 29 bits: outside those cases each term is exact, inside them it
+ * carries one f64 rounding (2^-53 relative).
+ */
+static void q4_k_scales(const uint8_t *b, int sc[8], int mn[8])
+{
+    for (int j = 0; j < 4; ++j) {
+        sc[j] = b[j] & 63;
+        mn[j] = b[4 + j] & 63;
+    }
+    for (int j = 4; j < 8; ++j) {
+        sc[j] = (b[4 + j] & 15) | ((b[j - 4] >> 6) << 4);
+        mn[j] = (b[4 + j] >> 4) | ((b[j] >> 6) << 4);
+    }
+}
+
+static void one_output_q4_k(const float *xrow, const uint8_t *wrow, int64_t nsuper,
+                            double *y, double *s)
+{
+    double acc = 0.0, abs_acc = 0.0;
+    for (int64_t b = 0; b < nsuper; ++b) {
+        const uint8_t *blk = wrow + b * 144;
+        const double d = qmm_oracle_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+        const double dmin = qmm_oracle_half_to_double((uint16_t)(blk[2] | (blk[3] << 8)));
+        int sc[8], mn[8];
+        q4_k_scales(blk + 4, sc, mn);
+        for (int e = 0; e < 256; ++e) {
+            const int c = e / 64, i = e % 64;
+            const int j = 2 * c + (i >= 32);
+            const uint8_t byte = blk[16 + 32 * c + (i % 32)];
+            const int q = i < 32 ? (byte & 15) : (byte >> 4);
+            const double w = d * (double)sc[j] * (double)q - dmin * (double)mn[j];
+            const double t = w * (double)xrow[b * 256 + e];
+            acc += t;
+            abs_acc += fabs(t);
+        }
+    }
+    *y = acc;
+    *s = abs_acc;
+}
+
+/* Full Q4_K outputs: w is N x (K/256) super-blocks; K a multiple of 256. */
+void qmm_oracle_q4_k(const float *x, const uint8_t *w, int64_t M, int64_t N,
+                     int64_t K, double *y, double *s)
+{
+    const int64_t nsuper = K / 256, row_bytes = nsuper * 144, total = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        one_output_q4_k(x + m * K, w + n * row_bytes, nsuper, y + i, s + i);
+    }
+}
+
+void qmm_oracle_q4_k_at(const float *x, const uint8_t *w, int64_t K, const int64_t *ms,
+                        const int64_t *ns, int64_t count, double *y, double *s)
+{
+    const int64_t nsuper = K / 256, row_bytes = nsuper * 144;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        one_output_q4_k(x + ms[i] * K, w + ns[i] * row_bytes, nsuper, y + i, s + i);
 }
 
 /*

@@ -29,6 +29,13 @@ What each pin compares with:
                           pinned matmul, h vanishes with g or u, and two
                           rows with gates +g, -g over the same up row differ
                           by exactly g * u (the odd-part identity again).
+* ``q4k_*``            -- Q4_K super-blocks: torch float64 matmul of a dense
+                          dequantization of the logical fields, one-hot x,
+                          zero nibbles and minimums give 0, scales 0 leave
+                          -dmin * mn (closed form), d = dmin = 1 with integer
+                          x is an exact integer, y(2d, 2dmin) = 2 y, row
+                          permutations; the hand-worked golden super-block
+                          (``golden``) pins the byte placement.
 
 The logical fields (fp16 scales and integer codes) are placed into bytes by
 ``synth.pack_q4_0`` / ``synth.pack_q8_0``; the golden fixtures spell their
@@ -337,9 +344,116 @@ def ffn_gate_up(o, n=24, k=512, seed=10):
     assert np.all(np.sign(h2[g2 > 0]) == np.sign(u2[g2 > 0]))   # gelu(g) > 0 for g > 0
 
 
+# ----------------------------------------------------------------------------
+# Q4_K super-blocks (256 weights: d, dmin, 6-bit sub-block scales and
+# minimums, nibbles); the golden fixture pins the byte placement
+# ----------------------------------------------------------------------------
+
+def q4k_dense(d, dmin, sc, mn, q):
+    """f64 dense W[N, K] from logical Q4_K fields (test-side): weight e of a
+    super-block is d * sc[e // 32] * q[e] - dmin * mn[e // 32]."""
+    n, k = q.shape
+    ns = k // 256
+    dsc = d.astype(np.float64)[:, :, None] * sc.astype(np.float64)
+    dmn = dmin.astype(np.float64)[:, :, None] * mn.astype(np.float64)
+    dsc = np.repeat(dsc.reshape(n, ns * 8), 32, axis=1)
+    dmn = np.repeat(dmn.reshape(n, ns * 8), 32, axis=1)
+    return dsc * q.astype(np.float64) - dmn
+
+
+def q4k_random_fields(rng, n, k, fp16_any=True):
+    ns = k // 256
+    if fp16_any:
+        d = random_fp16(rng, (n, ns), allow_negative=True)
+        dmin = random_fp16(rng, (n, ns), allow_negative=True)
+    else:
+        d = (2.0 ** rng.integers(-10, 3, (n, ns))).astype(np.float16)
+        dmin = (2.0 ** rng.integers(-10, 3, (n, ns))).astype(np.float16)
+    sc = rng.integers(0, 64, (n, ns, 8), dtype=np.uint8)
+    mn = rng.integers(0, 64, (n, ns, 8), dtype=np.uint8)
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    return d, dmin, sc, mn, q
+
+
+def q4k_library_matmul(o, shapes=((1, 64, 256), (3, 300, 2048), (2, 40, 8192))):
+    import torch
+
+    for (m, n, k) in shapes:
+        f = synth.q4_k_fields(n, k, seed=11)
+        x = synth.activations(m, k, seed=11)
+        y, s = o.matmul("q4_k", x, synth.pack_q4_k(*f), n, k)
+        wd = torch.from_numpy(q4k_dense(*f))
+        xd = torch.from_numpy(x.astype(np.float64))
+        ref = (xd @ wd.T).numpy()
+        sref = (xd.abs() @ wd.abs().T).numpy()
+        tol = 4 * k * EPS64 * sref
+        assert np.all(np.abs(y - ref) <= tol), f"q4_k {m}x{n}x{k}: max err {np.abs(y - ref).max()}"
+        assert np.all(np.abs(s - sref) <= tol), f"q4_k {m}x{n}x{k}: s disagrees"
+
+
+def q4k_one_hot(o, n=12, k=512, seed=12):
+    rng = np.random.default_rng(seed)
+    f = q4k_random_fields(rng, n, k)
+    w = synth.pack_q4_k(*f)
+    ks = list(range(0, 256, 3)) + [int(v) for v in rng.integers(256, k, 24)]
+    x = np.zeros((len(ks), k), dtype=np.float32)
+    x[np.arange(len(ks)), ks] = 1.0
+    y, _ = o.matmul("q4_k", x, w, n, k)
+    want = q4k_dense(*f)[:, ks].T
+    assert np.array_equal(y, want), "q4_k: one-hot x does not select w[n, k]"
+
+
+def q4k_zero(o, n=6, k=512, seed=13):
+    rng = np.random.default_rng(seed)
+    d, dmin, sc, _, _ = q4k_random_fields(rng, n, k)
+    mn = np.zeros_like(sc)
+    q = np.zeros((n, k), dtype=np.uint8)
+    x = (rng.standard_normal((2, k)) * 1e3).astype(np.float32)
+    y, s = o.matmul("q4_k", x, synth.pack_q4_k(d, dmin, sc, mn, q), n, k)
+    assert np.all(y == 0.0) and np.all(s == 0.0), "q4_k: zero nibbles and minimums must give 0"
+
+
+def q4k_mins_only(o, n=5, k=1024, seed=14):
+    rng = np.random.default_rng(seed)
+    d, dmin, _, mn, q = q4k_random_fields(rng, n, k, fp16_any=False)
+    sc = np.zeros_like(mn)
+    x = np.ones((1, k), dtype=np.float32)
+    y, _ = o.matmul("q4_k", x, synth.pack_q4_k(d, dmin, sc, mn, q), n, k)
+    want = -(32 * dmin.astype(np.float64) * mn.astype(np.float64).sum(axis=2)).sum(axis=1)
+    assert np.array_equal(y[0], want), f"q4_k minimums: {y[0]} != {want}"
+
+
+def q4k_integer_exact(o, n=16, k=2048, seed=15):
+    rng = np.random.default_rng(seed)
+    _, _, sc, mn, q = q4k_random_fields(rng, n, k)
+    ones = np.ones((n, k // 256), dtype=np.float16)
+    x = rng.integers(-8, 9, (2, k)).astype(np.float32)
+    y, _ = o.matmul("q4_k", x, synth.pack_q4_k(ones, ones, sc, mn, q), n, k)
+    sub_sc = np.repeat(sc.reshape(n, -1).astype(np.int64), 32, axis=1)
+    sub_mn = np.repeat(mn.reshape(n, -1).astype(np.int64), 32, axis=1)
+    want = x.astype(np.int64) @ (sub_sc * q.astype(np.int64) - sub_mn).T
+    assert np.array_equal(y, want.astype(np.float64)), "q4_k: integer case not exact"
+
+
+def q4k_linear_and_rows(o, n=40, k=1024, seed=16):
+    rng = np.random.default_rng(seed)
+    d, dmin, sc, mn, q = synth.q4_k_fields(n, k, seed=seed)
+    x = synth.activations(2, k, seed=seed)
+    y, s = o.matmul("q4_k", x, synth.pack_q4_k(d, dmin, sc, mn, q), n, k)
+    d2 = (d.astype(np.float64) * 2).astype(np.float16)
+    m2 = (dmin.astype(np.float64) * 2).astype(np.float16)
+    y2, s2 = o.matmul("q4_k", x, synth.pack_q4_k(d2, m2, sc, mn, q), n, k)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(s2, 2 * s), "q4_k: y(2d, 2dmin) != 2y"
+    rp = rng.permutation(n)
+    yr, _ = o.matmul("q4_k", x, synth.pack_q4_k(d[rp], dmin[rp], sc[rp], mn[rp], q[rp]), n, k)
+    assert np.array_equal(yr, y[:, rp]), "q4_k: row permutation"
+
+
 ALL = [half_decode, golden, exact_rational, library_matmul, one_hot, zero_point,
        extreme_nibbles, subnormal_scale, linear_in_d, integer_exact, q8_min,
-       permutations, special_values, gelu_tanh_form, ffn_gate_up]
+       permutations, special_values, gelu_tanh_form, ffn_gate_up,
+       q4k_library_matmul, q4k_one_hot, q4k_zero, q4k_mins_only, q4k_integer_exact,
+       q4k_linear_and_rows]
 
 
 def failures(o, quick=True):
@@ -351,6 +465,8 @@ def failures(o, quick=True):
                 pin(o, cases=24)
             elif pin is library_matmul and quick:
                 pin(o, shapes=((2, 40, 256),))
+            elif pin is q4k_library_matmul and quick:
+                pin(o, shapes=((2, 40, 512),))
             else:
                 pin(o)
         except Exception:  # an assertion, or a value no pin can even read

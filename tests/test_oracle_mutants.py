@@ -46,6 +46,19 @@ MUTANTS = [
      "h[i] = qmm_oracle_gelu_tanh(g[i]) + u[i];"),
     ("gated_activation_on_up", "h[i] = qmm_oracle_gelu_tanh(g[i]) * u[i];",
      "h[i] = g[i] * qmm_oracle_gelu_tanh(u[i]);"),
+    ("q4k_scale_min_swapped", "sc[j] = b[j] & 63;\n        mn[j] = b[4 + j] & 63;",
+     "sc[j] = b[4 + j] & 63;\n        mn[j] = b[j] & 63;"),
+    ("q4k_scale_high_bits_byte", "((b[j - 4] >> 6) << 4)", "((b[j] >> 6) << 4)"),
+    ("q4k_min_high_bits_byte", "mn[j] = (b[4 + j] >> 4) | ((b[j] >> 6) << 4);",
+     "mn[j] = (b[4 + j] >> 4) | ((b[j - 4] >> 6) << 4);"),
+    ("q4k_scale_low_nibble_high", "sc[j] = (b[4 + j] & 15)", "sc[j] = (b[4 + j] >> 4)"),
+    ("q4k_nibble_halves_swapped", "(byte & 15) : (byte >> 4)", "(byte >> 4) : (byte & 15)"),
+    ("q4k_subblock_index", "const int j = 2 * c + (i >= 32);", "const int j = c + 4 * (i >= 32);"),
+    ("q4k_min_added", "- dmin * (double)mn[j]", "+ dmin * (double)mn[j]"),
+    ("q4k_dmin_is_d", "(uint16_t)(blk[2] | (blk[3] << 8))", "(uint16_t)(blk[0] | (blk[1] << 8))"),
+    ("q4k_nibble_byte_stride", "blk[16 + 32 * c + (i % 32)]", "blk[16 + 16 * c + (i % 32)]"),
+    ("q4k_superblock_144_as_128", "const uint8_t *blk = wrow + b * 144;",
+     "const uint8_t *blk = wrow + b * 128;"),
 ]
 
 

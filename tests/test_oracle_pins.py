@@ -20,7 +20,7 @@ def test_pin(o, pin):
 def test_golden_fixtures_present():
     names = {p.name for p in pins.golden_cases()}
     assert {"q4_0_single_block.txt", "q4_0_two_rows_two_blocks.txt",
-            "q8_0_two_rows.txt"} <= names
+            "q8_0_two_rows.txt", "q4_k_single_superblock.txt"} <= names
 
 
 def test_sampled_matches_full(o):
@@ -29,7 +29,8 @@ def test_sampled_matches_full(o):
 
     x = synth.activations(3, 512, seed=2)
     for fmt, w in (("q4_0", synth.q4_0_weights(40, 512, seed=2)),
-                   ("q8_0", synth.q8_0_weights(40, 512, seed=2))):
+                   ("q8_0", synth.q8_0_weights(40, 512, seed=2)),
+                   ("q4_k", synth.q4_k_weights(40, 512, seed=2))):
         y, s = o.matmul(fmt, x, w, 40, 512)
         ms = np.array([0, 2, 1, 2]); ns = np.array([0, 39, 17, 5])
         ya, sa = o.matmul_at(fmt, x, w, 40, 512, ms, ns)
