@@ -1,16 +1,16 @@
-"""Python binding of libqmm: block-quantized (GGUF Q4_0 / Q8_0) weight
-matmul on AMD Instinct MI355X.
+"""Python binding of libqmm: block-quantized (GGUF Q4_0 / Q8_0, and Q4_K
+super-blocks) weight matmul on AMD Instinct MI355X.
 
 Argument marshalling only: every step of the computation runs in the
 library's gfx950 kernels; PyTorch supplies device memory and the stream.
 
 Two layers:
 * ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0``, ``qmm_gemm_q8_0``,
-  ``qmm_ffn_gate_up_q4_0`` -- the C-ABI entry points of ``include/qmm.h``
+  ``qmm_ffn_gate_up_q4_0``, ``qmm_gemv_q4_k`` -- the C-ABI entry points of ``include/qmm.h``
   with the same names and arguments (device addresses as integers, a HIP
   stream handle); they return the status code.
 * ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0``, ``gemm_q8_0``,
-  ``ffn_gate_up_q4_0`` -- tensor front ends that check dtypes, shapes and
+  ``ffn_gate_up_q4_0``, ``gemv_q4_k`` -- tensor front ends that check dtypes, shapes and
   devices, allocate ``y`` with torch, launch on the current stream and raise
   ``QmmError`` on a non-OK status.
 
@@ -29,11 +29,13 @@ LIBRARY = HERE / "libqmm.so"
 QMM_OK, QMM_EINVAL, QMM_EALIGN, QMM_EUNSUPPORTED, QMM_EHIP = range(5)
 GEMV_MAX_M = 16
 MAX_K = 65536
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+# format -> (weights per block, bytes per block)
+BLOCKS = {"q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144)}
 
 # Every symbol include/qmm.h declares.
 EXPORTS = ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
-           "qmm_ffn_gate_up_q4_0", "qmm_status_string", "qmm_last_error", "qmm_version")
+           "qmm_ffn_gate_up_q4_0", "qmm_gemv_q4_k", "qmm_status_string", "qmm_last_error",
+           "qmm_version")
 
 
 class QmmError(RuntimeError):
@@ -59,7 +61,8 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(str(LIBRARY))
         args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
-        for name in ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0"):
+        for name in ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
+                     "qmm_gemv_q4_k"):
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -99,6 +102,10 @@ def qmm_gemm_q8_0(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 
 def qmm_ffn_gate_up_q4_0(x: int, w_gate: int, w_up: int, h: int, M: int, N: int, K: int,
                          stream: int = 0) -> int:
     return library().qmm_ffn_gate_up_q4_0(x, w_gate, w_up, h, M, N, K, stream)
+
+
+def qmm_gemv_q4_k(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return library().qmm_gemv_q4_k(x, w, y, M, N, K, stream)
 
 
 def qmm_status_string(status: int) -> str:
@@ -144,9 +151,10 @@ def _call(fn, fmt, x, w, n, k, out):
     m = x.shape[0]
     if x.shape[1] != k:
         raise ValueError(f"x has {x.shape[1]} columns, K={k}")
-    if k % 32 or w.numel() != n * (k // 32) * BLOCK_BYTES[fmt]:
+    per, nbytes = BLOCKS[fmt]
+    if k % per or w.numel() != n * (k // per) * nbytes:
         raise ValueError(f"w has {w.numel()} bytes; {fmt} N={n} K={k} needs "
-                         f"{n * (k // 32) * BLOCK_BYTES[fmt]}")
+                         f"{n * (k // per) * nbytes} (K a multiple of {per})")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     elif (out.dtype != torch.float32 or out.shape != (m, n) or not out.is_contiguous()
@@ -178,6 +186,11 @@ def gemm_q8_0(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q8_0 W, any M
     (M <= 4: the f32 GEMV result, bit for bit)."""
     return _call(qmm_gemm_q8_0, "q8_0", x, w, n, k, out)
+
+
+def gemv_q4_k(x, w, n: int, k: int, out=None):
+    """y[1, N] = x[1, K] @ W^T for Q4_K W (super-blocks of 256; M = 1)."""
+    return _call(qmm_gemv_q4_k, "q4_k", x, w, n, k, out)
 
 
 def ffn_gate_up_q4_0(x, w_gate, w_up, n: int, k: int, out=None):

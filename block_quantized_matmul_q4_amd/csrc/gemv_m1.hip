@@ -213,17 +213,6 @@ __device__ __forceinline__ float gelu_tanh(float g)
     return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
 }
 
-// Workgroup barrier that waits only for this wave's LDS operations, not for
-// its weight loads still in flight (__syncthreads() waits for every
-// outstanding memory access first). The scheduling barriers keep the
-// compiler from moving work across it.
-__device__ __forceinline__ void lds_only_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED, int MR>
 __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,

@@ -1,0 +1,176 @@
+// Decode GEMV over Q4_K super-blocks, one activation row:
+// y[n] = sum_k x[k] * w[n][k], f32 arithmetic.
+//
+// Q4_K is the k-quant 4-bit format the pages keep for their CLIP/CLAP path
+// (named without a layout; GGUF's is read here). A super-block of 256
+// weights takes 144 bytes: fp16 d and dmin (bytes 0-3), eight 6-bit
+// sub-block scales sc[j] and minimums mn[j] packed in bytes 4-15, and 128
+// nibble bytes. Weight 64c + i (c < 4, i < 32) is the low nibble of nibble
+// byte 32c + i and weight 64c + 32 + i its high nibble; weight e belongs to
+// sub-block e / 32 and is w = d sc q - dmin mn. For a sub-block j < 4, sc is
+// the low 6 bits of scale byte j and mn of byte 4 + j; for j >= 4, byte
+// 8 + (j - 4) holds the low 4 bits of sc (low nibble) and mn (high nibble)
+// and the top 2 bits of bytes j - 4 and j hold their top 2 bits.
+//
+// A row of K weights is K / 64 "chunks" of 64 weights (a quarter of a
+// super-block: sub-blocks 2c and 2c + 1). A thread owns one chunk of one
+// row per pass; T threads cover a row, a workgroup WG / T rows. A thread
+// loads the super-block's 16-byte header and the chunk's 32 nibble bytes
+// (three aligned 16-byte loads), and the activations of a pass are staged
+// once per workgroup in LDS (coalesced 16-byte loads, one barrier that
+// waits for LDS only, so each wave reads its activations while its weights
+// arrive). Per weight: one conversion of the nibble, one FMA forming
+// w = d sc q - dmin mn (d sc and dmin mn are exact in f32, so w is rounded
+// once), one FMA into the sub-block's sum. The T threads of a row reduce
+// with DPP row operations (and through LDS when a row spans two waves) in a
+// fixed order.
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kQKBytes = 144;       // bytes per super-block of 256 weights
+constexpr int XS = 68;              // padded LDS row of one chunk's activations
+
+// Scale and minimum of sub-block 2c + h from the scale bytes held in the
+// header's dwords 1-3 (b0: bytes 0-3, b1: bytes 4-7, b2: bytes 8-11). The
+// byte index inside b0, b1 and b2 is 2 (c % 2) + h in both halves of the
+// sub-block range.
+__device__ __forceinline__ void sub_block(uint32_t b0, uint32_t b1, uint32_t b2, int c, int h,
+                                          uint32_t &sc, uint32_t &mn)
+{
+    const int sh = 8 * (2 * (c & 1) + h);
+    const uint32_t x0 = (b0 >> sh) & 0xFFu, x1 = (b1 >> sh) & 0xFFu, x2 = (b2 >> sh) & 0xFFu;
+    if (c < 2) {
+        sc = x0 & 63u;
+        mn = x1 & 63u;
+    } else {
+        sc = (x2 & 15u) | ((x0 >> 6) << 4);
+        mn = (x2 >> 4) | ((x1 >> 6) << 4);
+    }
+}
+
+template <int T, int WG>
+__global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__ x,
+                                                       const uint8_t *__restrict__ w,
+                                                       float *__restrict__ y, int N, int C)
+{
+    constexpr int RPAR = WG / T;                // rows per workgroup
+    constexpr int TW = T < 64 ? T : 64;         // chunks per wave per row
+    constexpr int WPR = T / TW;                 // waves per row
+    constexpr int XU = (16 * T + WG - 1) / WG;  // staged float4 per thread and pass
+    __shared__ __attribute__((aligned(16))) float xs[T * XS];
+    __shared__ float red[WPR > 1 ? WG / 64 : 1];
+
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int t = tid % T, r = tid / T;
+    const int n = blockIdx.x * RPAR + r;
+    const int64_t row_bytes = (int64_t)(C / 4) * kQKBytes;
+    const uint8_t *wrow = w + (int64_t)min(n, N - 1) * row_bytes;
+
+    float acc = 0.f;
+    for (int c0 = 0; c0 < C; c0 += T) {
+        // 1. this pass's activations: float4 i is chunk i / 16, part i % 16
+        //    (four scalar arrays: an array of float4 is kept in scratch)
+        float xvx[XU], xvy[XU], xvz[XU], xvw[XU];
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int i = tid + WG * u;
+            const int ch = min(c0 + min(i / 16, T - 1), C - 1);
+            const float4 v = *reinterpret_cast<const float4 *>(x + 64 * ch + 4 * (i % 16));
+            xvx[u] = v.x; xvy[u] = v.y; xvz[u] = v.z; xvw[u] = v.w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 2. the super-block header and the chunk's nibbles
+        const int ch = min(c0 + t, C - 1);
+        const uint8_t *sb = wrow + (int64_t)(ch / 4) * kQKBytes;
+        const int c = ch % 4;
+        const u32x4_a4 hdr = *reinterpret_cast<const u32x4_a4 *>(sb);
+        const u32x4_a4 q0 = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * c);
+        const u32x4_a4 q1 = *reinterpret_cast<const u32x4_a4 *>(sb + 32 + 32 * c);
+        __builtin_amdgcn_sched_barrier(0);
+        // 3. activations to LDS (from the second pass on, after the
+        //    previous pass's readers)
+        if (c0 != 0) __syncthreads();
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int i = tid + WG * u;
+            if (16 * T % WG == 0 || i < 16 * T)
+                *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) =
+                    make_float4(xvx[u], xvy[u], xvz[u], xvw[u]);
+        }
+        lds_only_barrier();
+        // 4. the chunk's 64 weights against its activations
+        const float d = half_lo(hdr.x), dmin = half_hi(hdr.x);
+        const uint32_t nb[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float part = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t sc, mn;
+            sub_block(hdr.y, hdr.z, hdr.w, c, h, sc, mn);
+            const float dsc = d * (float)sc, dmn = dmin * (float)mn;
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t v = h ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
+                // hide the nibble range from the compiler, which would
+                // otherwise extract each nibble with a bit-field op before
+                // converting it; this way each byte converts in one
+                // v_cvt_f32_ubyteN
+                asm("" : "+v"(v));
+                const float4 xa =
+                    *reinterpret_cast<const float4 *>(&xs[t * XS + 32 * h + 4 * i]);
+                s = fmaf(fmaf(dsc, (float)(v & 0xFFu), -dmn), xa.x, s);
+                s = fmaf(fmaf(dsc, (float)((v >> 8) & 0xFFu), -dmn), xa.y, s);
+                s = fmaf(fmaf(dsc, (float)((v >> 16) & 0xFFu), -dmn), xa.z, s);
+                s = fmaf(fmaf(dsc, (float)(v >> 24), -dmn), xa.w, s);
+            }
+            part += s;
+        }
+        acc += c0 + t < C ? part : 0.f;
+    }
+
+    acc = group_sum<TW>(acc);
+    if constexpr (WPR == 1) {
+        if (t == T - 1 && n < N) y[n] = acc;
+    } else {
+        if (lane == 63) red[wave] = acc;
+        __syncthreads();
+        if (tid < RPAR) {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < WPR; ++q) s += red[tid * WPR + q];
+            const int nn = blockIdx.x * RPAR + tid;
+            if (nn < N) y[nn] = s;
+        }
+    }
+}
+
+template <int T, int WG>
+hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int C, hipStream_t stream)
+{
+    constexpr int rows = WG / T;
+    hipLaunchKernelGGL((gemv_q4_k_kernel<T, WG>), dim3((N + rows - 1) / rows), dim3(WG), 0,
+                       stream, x, w, y, N, C);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// C = K / 64 chunks per row (a multiple of 4). T is the smallest of 4, 8,
+// 16, 32, 64 and 128 that covers a row in one pass (rows longer than 128
+// chunks take several passes); the same shapes as the Q4_0 GEMV, whose
+// chunks (pairs of blocks) hold as many weights and bytes.
+hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int N, int K,
+                            hipStream_t stream)
+{
+    const int C = K / 64;
+    if (C <= 4) return launch<4, 256>(x, w, y, N, C, stream);
+    if (C <= 8) return launch<8, 256>(x, w, y, N, C, stream);
+    if (C <= 16) return launch<16, 256>(x, w, y, N, C, stream);
+    if (C <= 32) return launch<32, 256>(x, w, y, N, C, stream);
+    if (C <= 64) return launch<64, 512>(x, w, y, N, C, stream);
+    return launch<128, 512>(x, w, y, N, C, stream);
+}
+
+}  // namespace qmm

@@ -164,6 +164,23 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
                                               stream));
 }
 
+QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    const char *fn = "qmm_gemv_q4_k";
+    if (K % 256 && K > 0)
+        return fail(QMM_EINVAL, "%s: K=%lld is not a multiple of 256 (the super-block size)",
+                    fn, (long long)K);
+    // a super-block row takes 144 bytes per 256 weights, the same bytes per
+    // weight as Q4_0's 18 per 32: the shared size and overlap checks apply
+    int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
+    if (st != QMM_OK) return st;
+    if (M != 1)
+        return fail(QMM_EUNSUPPORTED, "%s: M=%lld unsupported (one activation row: M must be 1)",
+                    fn, (long long)M);
+    return finish(fn, qmm::launch_gemv_q4_k(x, (const uint8_t *)w, y, (int)N, (int)K, stream));
+}
+
 QMM_API const char *qmm_status_string(int status)
 {
     switch (status) {

@@ -35,6 +35,9 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
                               int N, int K, hipStream_t stream);
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                               float *h, int N, int K, hipStream_t stream);
+// Q4_K GEMV, one activation row (K % 256 == 0).
+hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int N, int K,
+                            hipStream_t stream);
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream);
 
@@ -75,6 +78,17 @@ __device__ __forceinline__ uint32_t hi16(uint32_t v)
 __device__ __forceinline__ float sbyte(uint32_t v, int b)
 {
     return (float)(int8_t)(v >> (8 * b));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its global loads still in flight (__syncthreads() waits for every
+// outstanding memory access first). The scheduling barriers keep the
+// compiler from moving work across it.
+__device__ __forceinline__ void lds_only_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int CTRL, int ROW_MASK>

@@ -135,6 +135,27 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
                                  float *h, int64_t M, int64_t N, int64_t K,
                                  hipStream_t stream);
 
+/*
+ * Decode GEMV over Q4_K super-blocks, one activation row (M = 1). Q4_K is the
+ * k-quant 4-bit format the pages ("Add generated quant-kernel JIT and
+ * accelerate Gemma4, BGE-M3, and GLiNER2", section Summary) keep for their
+ * CLIP/CLAP path; they give no layout, and GGUF's is taken. w is N rows of
+ * K/256 super-blocks of 144 bytes each, rows contiguous, no padding:
+ *   bytes 0-1 fp16 d, bytes 2-3 fp16 dmin, bytes 4-15 eight 6-bit sub-block
+ *   scales sc[j] and minimums mn[j] (j < 4: low 6 bits of byte 4+j and
+ *   8+j; j >= 4: low 4 bits from the low / high nibble of byte 8+j, top 2
+ *   bits from the top bits of byte j and 4+j), bytes 16-143 nibbles
+ *   (weight 64c+i, i < 32, is the low nibble of byte 16+32c+i, weight
+ *   64c+32+i its high nibble); weight e is in sub-block e/32 and
+ *   w = d * sc * q - dmin * mn.
+ * x is f32[1][K], y f32[1][N] (overwritten). Errors as for qmm_gemv_q4_0,
+ * plus QMM_EINVAL for K not a multiple of 256 and QMM_EUNSUPPORTED for
+ * M != 1. Accuracy: |y - sum_k x w| <= 1e-4 * sum_k |x w|, each w rounded
+ * once to f32 and each product accumulated in f32.
+ */
+QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
 /* Static English name of a status code ("QMM_OK", ...). */
 QMM_API const char *qmm_status_string(int status);
 

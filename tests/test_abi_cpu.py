@@ -151,3 +151,23 @@ def test_bench_read_kernels_load_and_reject_bad_arguments():
     assert lib.bench_read_plain(A + 4, 16, A, None) == 1      # not 16-byte aligned
     assert lib.bench_read_pairs(A, 40, A, None) == 1          # not a multiple of 36
     assert lib.bench_read_pairs(A, 36, None, None) == 1
+
+
+@pytest.mark.parametrize("args,status,fragment", [
+    ((0, B, C, 1, 8, 256), qmm.QMM_EINVAL, "null pointer"),
+    ((A, B, C, 0, 8, 256), qmm.QMM_EINVAL, ">= 1"),
+    ((A, B, C, 1, 8, 0), qmm.QMM_EINVAL, ">= 1"),
+    ((A, B, C, 1, 8, 384), qmm.QMM_EINVAL, "multiple of 256"),
+    ((A, B, C, 1, 8, 64), qmm.QMM_EINVAL, "multiple of 256"),
+    ((A, B, C, 2, 8, 256), qmm.QMM_EUNSUPPORTED, "M must be 1"),
+    ((A, B, C, 17, 8, 256), qmm.QMM_EINVAL, "exceeds 16"),
+    ((A, B, C, 1, 8, 65536 + 256), qmm.QMM_EUNSUPPORTED, "unsupported"),
+    ((A + 4, B, C, 1, 8, 256), qmm.QMM_EALIGN, "misaligned"),
+    ((A, B + 4, C, 1, 8, 256), qmm.QMM_EALIGN, "misaligned"),
+    ((A, B, B + 64, 1, 8, 256), qmm.QMM_EINVAL, "overlaps"),
+])
+def test_gemv_q4_k_rejected_before_launch(args, status, fragment):
+    got = qmm.qmm_gemv_q4_k(*args, 0)
+    assert got == status, (args, qmm.qmm_last_error())
+    assert fragment in qmm.qmm_last_error()
+    assert "qmm_gemv_q4_k" in qmm.qmm_last_error()

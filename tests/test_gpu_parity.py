@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TAU_GEMV = 1e-4
 TAU_GEMM = 8e-3
-BYTES = {"q4_0": 18, "q8_0": 34}
+BYTES = {"q4_0": 18, "q8_0": 34}      # per 32 weights (Q4_K: 144 per 256, the same rate)
 
 
 @pytest.fixture(scope="module")
@@ -42,6 +42,8 @@ def note(msg):
 
 
 def weights(fmt, n, k, seed=0):
+    if fmt == "q4_k":
+        return synth.q4_k_weights(n, k, seed)
     return synth.q4_0_weights(n, k, seed) if fmt == "q4_0" else synth.q8_0_weights(n, k, seed)
 
 
@@ -49,7 +51,8 @@ def run(entry, fmt, x, w, n, k):
     xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     wt = torch.from_numpy(np.ascontiguousarray(w).reshape(-1)).cuda()
     fn = {"gemv_q4_0": qmm.gemv_q4_0, "gemv_q8_0": qmm.gemv_q8_0,
-          "gemm_q4_0": qmm.gemm_q4_0, "gemm_q8_0": qmm.gemm_q8_0}[f"{entry}_{fmt}"]
+          "gemm_q4_0": qmm.gemm_q4_0, "gemm_q8_0": qmm.gemm_q8_0,
+          "gemv_q4_k": qmm.gemv_q4_k}[f"{entry}_{fmt}"]
     y = fn(xt, wt, n, k)
     torch.cuda.synchronize()
     return y.cpu().numpy()
@@ -230,7 +233,7 @@ def test_q4_0_vs_q8_0_scale_distributions(orc):
 
 def pad_golden(g, k=256):
     """Embed a golden case in K=256 (zero blocks, zero activations)."""
-    bs = BYTES[g["fmt"]]
+    bs = BYTES["q4_0" if g["fmt"] == "q4_k" else g["fmt"]]
     n, k0 = g["N"], g["K"]
     w = np.zeros((n, k // 32 * bs), np.uint8)
     w[:, : k0 // 32 * bs] = g["w"].reshape(n, -1)
@@ -239,8 +242,11 @@ def pad_golden(g, k=256):
     return x, w
 
 
-@pytest.mark.parametrize("path", pins.golden_cases(), ids=lambda p: p.name)
-@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+GOLDEN_RUNS = [(path, entry) for path in pins.golden_cases() for entry in ("gemv", "gemm")
+               if not (entry == "gemm" and path.name.startswith("q4_k"))]
+
+
+@pytest.mark.parametrize("path,entry", GOLDEN_RUNS, ids=lambda v: getattr(v, "name", v))
 def test_golden_on_gpu(orc, path, entry):
     """Hand-derived blocks (embedded in K=256 with zero padding) against their
     exact values: within the contract bound, and bitwise where the exact value
@@ -248,9 +254,14 @@ def test_golden_on_gpu(orc, path, entry):
     g = pins.load_golden(path)
     x, w = pad_golden(g)
     note(f"[golden] {path.name} {entry}")
-    y = run(entry, g["fmt"], x, w, g["N"], 256)
+    if g["fmt"] == "q4_k":   # one activation row per call
+        y = np.concatenate([run(entry, "q4_k", x[i:i + 1], w, g["N"], 256)
+                            for i in range(g["M"])]).reshape(1, -1)
+    else:
+        y = run(entry, g["fmt"], x, w, g["N"], 256)
     exact = np.array([[float(v) for v in g["y"]]])
     _, s = orc.matmul(g["fmt"], x, w, g["N"], 256)
+    s = s.reshape(y.shape)
     assert_parity(y, exact, s, TAU_GEMM if entry == "gemm" else TAU_GEMV, path.name)
     integral = np.array([v.denominator == 1 for v in g["y"]])
     assert np.array_equal(y[0][integral], exact[0][integral])
@@ -477,3 +488,86 @@ def test_randomized_small_shapes(orc):
         n = int(rng.integers(1, 600))
         k = 256 * int(rng.integers(1, 13))
         check(orc, entry, fmt, m, n, k, seed=1000 + case)
+
+
+# ---------------------------------------------------------------------------
+# Q4_K super-blocks (one activation row)
+# ---------------------------------------------------------------------------
+
+Q4_K_SHAPES = [
+    (8192, 2048), (2048, 8192),                      # the FFN decode pair
+    (1, 256), (3, 512), (17, 768), (300, 512), (9000, 1024), (4097, 1280),
+    (257, 2304), (333, 4096), (2049, 4352), (1000, 8192), (4099, 8448),
+    (65, 16384), (50, 65536), (65539, 1280),
+]
+
+
+@pytest.mark.parametrize("n,k", Q4_K_SHAPES)
+def test_gemv_q4_k_shapes(orc, n, k):
+    check(orc, "gemv", "q4_k", 1, n, k, seed=n + k)
+
+
+def q4_k_case(rng, n, k, d_one=False):
+    ns = k // 256
+    if d_one:
+        d = dmin = np.ones((n, ns), np.float16)
+    else:
+        d = np.clip(pins.random_fp16(rng, (n, ns)).astype(np.float32), -60000, 60000)
+        dmin = np.clip(pins.random_fp16(rng, (n, ns)).astype(np.float32), -60000, 60000)
+        d, dmin = d.astype(np.float16), dmin.astype(np.float16)
+    sc = rng.integers(0, 64, (n, ns, 8), dtype=np.uint8)
+    mn = rng.integers(0, 64, (n, ns, 8), dtype=np.uint8)
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    return d, dmin, sc, mn, q
+
+
+def test_gemv_q4_k_one_hot_exact(orc):
+    """x = e_k selects w[n][k] = d sc q - dmin mn, rounded once to f32."""
+    n, k = 96, 1024
+    rng = np.random.default_rng(31)
+    w = synth.pack_q4_k(*q4_k_case(rng, n, k))
+    for k0 in [0, 31, 32, 63, 64, 100, 127, 128, 191, 200, 255, 256, 511, 700, 1023]:
+        x = np.zeros((1, k), np.float32)
+        x[0, k0] = 1.0
+        note(f"[exact] q4_k one-hot k={k0}")
+        y = run("gemv", "q4_k", x, w, n, k).astype(np.float64)
+        yref, _ = orc.matmul("q4_k", x, w, n, k)
+        assert np.array_equal(y, yref.astype(np.float32).astype(np.float64)), k0
+
+
+def test_gemv_q4_k_integer_exact(orc):
+    """d = dmin = 1 and integer x: every partial sum is an integer below 2^24."""
+    n, k = 300, 2048
+    rng = np.random.default_rng(32)
+    w = synth.pack_q4_k(*q4_k_case(rng, n, k, d_one=True))
+    x = rng.integers(-8, 9, (1, k)).astype(np.float32)
+    note("[exact] q4_k integer")
+    y = run("gemv", "q4_k", x, w, n, k)
+    yref, _ = orc.matmul("q4_k", x, w, n, k)
+    assert np.array_equal(y.astype(np.float64), yref)
+
+
+def test_gemv_q4_k_zero_exact():
+    n, k = 100, 1024
+    rng = np.random.default_rng(33)
+    d, dmin, sc, mn, q = q4_k_case(rng, n, k)
+    w = synth.pack_q4_k(d, dmin, sc, np.zeros_like(mn), np.zeros_like(q))
+    x = (rng.standard_normal((1, k)) * 100).astype(np.float32)
+    note("[exact] q4_k zero nibbles and minimums")
+    assert np.all(run("gemv", "q4_k", x, w, n, k) == 0.0)
+
+
+def test_gemv_q4_k_repeatable_and_errors():
+    n, k = 4096, 2048
+    x = synth.activations(1, k, seed=34)
+    w = synth.q4_k_weights(n, k, seed=34)
+    note("[determinism] gemv_q4_k")
+    ys = [run("gemv", "q4_k", x, w, n, k) for _ in range(3)]
+    assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
+    xt = torch.zeros(2, 256, device="cuda")
+    wt = torch.zeros(8 * 144, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.gemv_q4_k(xt, wt, 8, 256)
+    assert e.value.status == qmm.QMM_EUNSUPPORTED
+    with pytest.raises(ValueError):
+        qmm.gemv_q4_k(torch.zeros(1, 384, device="cuda"), wt, 8, 384)
