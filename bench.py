@@ -20,7 +20,8 @@ Timing:
   the cold pool) captured back to back in a HIP graph; each of 5 replays is
   bracketed by HIP events on the launch stream; the per-launch mean
   includes the dispatch gap between consecutive kernels.
-* the same method times the other rows: small-M GEMV (M = 2..16), the Q8_0
+* the same method times the other rows: small-M GEMV (M = 2..16), the gated
+  FFN front half, the Q4_K GEMV at the FFN pair's shapes, the Q8_0
   vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
   GEMM (M = 2048, and short prompts
   M = 16, 64, 128), reported under "rows".
@@ -351,6 +352,20 @@ def main():
                                         vs_two_gemv_us=2 * t_up["mean_us"])
         log(f"[bench] ffn gate+up: {tf['mean_us']:.2f} us (two GEMVs: "
             f"{2 * t_up['mean_us']:.2f} us)")
+        # Q4_K (the k-quant format of the pages' CLIP/CLAP path) at the FFN
+        # pair's shapes, cold pools
+        for name in ("q4_k_gemv_ffn_up", "q4_k_gemv_ffn_down"):
+            wlk = synth.WORKLOADS[name]
+            xk_h, wk_h = synth.workload_inputs(name)
+            wk = pool(wk_h)
+            xk = torch.from_numpy(xk_h).to(dev)
+            yk = torch.empty((1, wlk["N"]), device=dev)
+            tk = time_launches(lib.qmm_gemv_q4_k,
+                               gemv_args(xk, wk, yk, 1, wlk["N"], wlk["K"], n))
+            bk = wk_h.nbytes + xk_h.nbytes + yk.numel() * 4
+            rows[name] = dict(tk, bytes=bk, gbs=bk / (tk["mean_us"] * 1e-6) / 1e9)
+            log(f"[bench] {name}: {tk['mean_us']:.2f} us")
+            del wk
         # Q8_0 vocabulary GEMV
         voc = synth.WORKLOADS["q8_0_gemv_vocab"]
         xv_h, wv_h = synth.workload_inputs("q8_0_gemv_vocab")
