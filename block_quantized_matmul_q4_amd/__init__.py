@@ -6,11 +6,12 @@ library's gfx950 kernels; PyTorch supplies device memory and the stream.
 
 Two layers:
 * ``qmm_gemv_q4_0``, ``qmm_gemv_q8_0``, ``qmm_gemm_q4_0``, ``qmm_gemm_q8_0``,
-  ``qmm_ffn_gate_up_q4_0``, ``qmm_gemv_q4_k`` -- the C-ABI entry points of ``include/qmm.h``
+  ``qmm_ffn_gate_up_q4_0``, ``qmm_gemv_q4_k``, ``qmm_gemm_q4_k`` -- the C-ABI
+  entry points of ``include/qmm.h``
   with the same names and arguments (device addresses as integers, a HIP
   stream handle); they return the status code.
 * ``gemv_q4_0``, ``gemv_q8_0``, ``gemm_q4_0``, ``gemm_q8_0``,
-  ``ffn_gate_up_q4_0``, ``gemv_q4_k`` -- tensor front ends that check dtypes, shapes and
+  ``ffn_gate_up_q4_0``, ``gemv_q4_k``, ``gemm_q4_k`` -- tensor front ends that check dtypes, shapes and
   devices, allocate ``y`` with torch, launch on the current stream and raise
   ``QmmError`` on a non-OK status.
 
@@ -34,8 +35,8 @@ BLOCKS = {"q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144)}
 
 # Every symbol include/qmm.h declares.
 EXPORTS = ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
-           "qmm_ffn_gate_up_q4_0", "qmm_gemv_q4_k", "qmm_status_string", "qmm_last_error",
-           "qmm_version")
+           "qmm_ffn_gate_up_q4_0", "qmm_gemv_q4_k", "qmm_gemm_q4_k", "qmm_status_string",
+           "qmm_last_error", "qmm_version")
 
 
 class QmmError(RuntimeError):
@@ -62,7 +63,7 @@ def library() -> ctypes.CDLL:
         args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         for name in ("qmm_gemv_q4_0", "qmm_gemv_q8_0", "qmm_gemm_q4_0", "qmm_gemm_q8_0",
-                     "qmm_gemv_q4_k"):
+                     "qmm_gemv_q4_k", "qmm_gemm_q4_k"):
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -106,6 +107,10 @@ def qmm_ffn_gate_up_q4_0(x: int, w_gate: int, w_up: int, h: int, M: int, N: int,
 
 def qmm_gemv_q4_k(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
     return library().qmm_gemv_q4_k(x, w, y, M, N, K, stream)
+
+
+def qmm_gemm_q4_k(x: int, w: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return library().qmm_gemm_q4_k(x, w, y, M, N, K, stream)
 
 
 def qmm_status_string(status: int) -> str:
@@ -191,6 +196,12 @@ def gemm_q8_0(x, w, n: int, k: int, out=None):
 def gemv_q4_k(x, w, n: int, k: int, out=None):
     """y[1, N] = x[1, K] @ W^T for Q4_K W (super-blocks of 256; M = 1)."""
     return _call(qmm_gemv_q4_k, "q4_k", x, w, n, k, out)
+
+
+def gemm_q4_k(x, w, n: int, k: int, out=None):
+    """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q4_K W, any M
+    (M = 1: the f32 GEMV result, bit for bit)."""
+    return _call(qmm_gemm_q4_k, "q4_k", x, w, n, k, out)
 
 
 def ffn_gate_up_q4_0(x, w_gate, w_up, n: int, k: int, out=None):

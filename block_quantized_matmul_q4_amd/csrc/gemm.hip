@@ -96,6 +96,13 @@ template <> struct BFmt<FMT_Q4_0> {
     static constexpr int kWin = 5;          // window dwords at pair byte 16 blk
     static constexpr int kWinStride = 16;
 
+    // the window of block blk of K step p, for a weight row at byte row_off
+    __device__ static void load_step(__amdgpu_buffer_rsrc_t r, int row_off, int blk, int p,
+                                     uint32_t (&b)[kWin])
+    {
+        load(r, row_off + kWinStride * blk, p * kPairBytes, b);
+    }
+
     __device__ static void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                 uint32_t (&b)[kWin])
     {
@@ -156,6 +163,12 @@ template <> struct BFmt<FMT_Q8_0> {
     static constexpr int kWin = 9;          // window dwords at pair byte 32 blk
     static constexpr int kWinStride = 32;
 
+    __device__ static void load_step(__amdgpu_buffer_rsrc_t r, int row_off, int blk, int p,
+                                     uint32_t (&b)[kWin])
+    {
+        load(r, row_off + kWinStride * blk, p * kPairBytes, b);
+    }
+
     __device__ static void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                 uint32_t (&b)[kWin])
     {
@@ -207,6 +220,59 @@ template <> struct BFmt<FMT_Q8_0> {
     }
 };
 
+// Q4_K super-blocks (256 weights in 144 bytes: fp16 d and dmin, 6-bit
+// sub-block scales and minimums, 128 nibble bytes; see gemv_q4_k.hip). A K
+// step of 64 is a quarter c of a super-block: sub-block 2c takes the low
+// nibbles of its 32 nibble bytes, sub-block 2c + 1 the high nibbles. The
+// thread with blk holds the super-block's 16-byte header and nibble bytes
+// 16 blk .. 16 blk + 15 of the quarter, i.e. elements 16 blk .. +15 of both
+// sub-blocks; b[8] keeps c. Each weight is formed in f32 with one FMA,
+// d sc q - dmin mn (both products exact), and rounded to bf16 (nearest even).
+template <> struct BFmt<FMT_Q4_K> {
+    static constexpr int kPairBytes = 36;   // per K step, on average (144 per 4 steps)
+    static constexpr int kWin = 9;
+
+    __device__ static void load_step(__amdgpu_buffer_rsrc_t r, int row_off, int blk, int p,
+                                     uint32_t (&b)[kWin])
+    {
+        const int sb = (p / 4) * 144, c = p % 4;
+        const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(r, row_off, sb, 0);
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, row_off + 16 * blk,
+                                                              sb + 16 + 32 * c, 0);
+        b[0] = h.x; b[1] = h.y; b[2] = h.z; b[3] = h.w;
+        b[4] = q.x; b[5] = q.y; b[6] = q.z; b[7] = q.w;
+        b[8] = c;
+    }
+
+    // quarter q: sub-block 2c + q / 2 (low or high nibbles), nibble bytes
+    // 16 blk + 8 (q % 2) .. +7 -> elements 32 (q / 2) + 16 blk + 8 (q % 2) ..
+    // +7 of the K step; dst is the row's base plus 32 blk (as for the block
+    // formats), one 16-byte LDS store
+    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int q,
+                                           __bf16 *dst)
+    {
+        const int h = q / 2, qq = q % 2, c = (int)b[8];
+        const int sh = 8 * (2 * (c & 1) + h);
+        const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
+        const uint32_t x2 = (b[3] >> sh) & 0xFFu;
+        const uint32_t sc = c < 2 ? (x0 & 63u) : ((x2 & 15u) | ((x0 >> 6) << 4));
+        const uint32_t mn = c < 2 ? (x1 & 63u) : ((x2 >> 4) | ((x1 >> 6) << 4));
+        const float dsc = half_lo(b[0]) * (float)sc, dmn = half_hi(b[0]) * (float)mn;
+        uint4 v;
+        uint32_t *o = &v.x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t raw = b[4 + 2 * qq + t];
+            const uint32_t nib = h ? (raw >> 4) & 0x0F0F0F0Fu : raw & 0x0F0F0F0Fu;
+            o[2 * t] = pack_bf16x2(fmaf(dsc, (float)(nib & 0xFFu), -dmn),
+                                   fmaf(dsc, (float)((nib >> 8) & 0xFFu), -dmn));
+            o[2 * t + 1] = pack_bf16x2(fmaf(dsc, (float)((nib >> 16) & 0xFFu), -dmn),
+                                       fmaf(dsc, (float)(nib >> 24), -dmn));
+        }
+        *reinterpret_cast<uint4 *>(dst - 32 * blk + 32 * h + 16 * blk + 8 * qq) = v;
+    }
+};
+
 template <int FMT, class TL>
 __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
@@ -251,7 +317,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     for (int u = 0; u < A_F4; ++u) a_voff[u] = ((tid / 16 + A_ROW_STRIDE * u) * K + a_col) * 4;
     // B staging: thread -> (row tid / 2, block tid % 2) of the tile
     const int b_row = tid / 2, b_blk = tid % 2;
-    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
+    const int b_roff = b_row * row_bytes;
 
     float4 a_reg[A_F4];
     uint32_t b_reg[2][BF::kWin];    // weight windows of two consecutive steps
@@ -266,7 +332,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
         }
     };
     auto load_b = [&](uint32_t (&b)[BF::kWin], int p) {
-        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b);
+        BF::load_step(b_rsrc, b_roff, b_blk, p, b);
     };
 
     // Converts quarter q of a step into LDS buffer buf: activation float4s
@@ -458,7 +524,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
     const int a_voff0 = ((lane / 16) * K + a_col) * 4;
     // weight row lane / 2 of the slice, block lane % 2 of the step's pair
     const int b_row = lane / 2, b_blk = lane % 2;
-    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
+    const int b_roff = b_row * row_bytes;
 
     float4 a_reg[AF4];
     uint32_t b_reg[BF::kWin];
@@ -469,7 +535,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
                 a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
-        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg);
+        BF::load_step(b_rsrc, b_roff, b_blk, p, b_reg);
     };
 
     f32x16 acc[MT];
@@ -700,7 +766,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream)
 {
-    if (M > 16) return hipErrorInvalidValue;
+    if (M > 16 || fmt == FMT_Q4_K) return hipErrorInvalidValue;
     const dim3 grid((N + 31) / 32);
     // Q4_0: 16 waves (more K steps in flight per slice: M = 16, N = 2048,
     // K = 8192 20.3 us against 22.0 with 8); Q8_0: 8 (its wider windows)
@@ -716,6 +782,7 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream)
 {
+    if (fmt == FMT_Q4_K) return launch_fmt<FMT_Q4_K>(x, w, y, M, N, K, stream);
     return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
                            : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }

@@ -325,6 +325,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream)
 {
+    if (fmt == FMT_Q4_K) return hipErrorInvalidValue;
     return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
                            : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }

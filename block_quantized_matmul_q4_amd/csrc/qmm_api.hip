@@ -84,6 +84,11 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
                     "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
                     (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX - 8);
     const uint8_t *wb = (const uint8_t *)w;
+    // Q4_K: one row takes its GEMV (f32, each weight rounded once)
+    if (fmt == qmm::FMT_Q4_K) {
+        if (M == 1) return finish(fn, qmm::launch_gemv_q4_k(x, wb, y, (int)N, (int)K, stream));
+        return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
+    }
     // Up to 4 rows the decode GEMV kernel streams the weights once with
     // f32-exact products: faster than any matrix-core tiling there, and well
     // inside this entry point's bound.
@@ -141,6 +146,17 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream)
 {
     return gemm_entry("qmm_gemm_q8_0", qmm::FMT_Q8_0, qmm::kQ8Bytes, x, w, y, M, N, K, stream);
+}
+
+QMM_API int qmm_gemm_q4_k(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream)
+{
+    if (K % 256 && K > 0)
+        return fail(QMM_EINVAL,
+                    "qmm_gemm_q4_k: K=%lld is not a multiple of 256 (the super-block size)",
+                    (long long)K);
+    // 144 bytes per 256 weights: Q4_0's byte rate, so its size checks apply
+    return gemm_entry("qmm_gemm_q4_k", qmm::FMT_Q4_K, qmm::kQ4Bytes, x, w, y, M, N, K, stream);
 }
 
 QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void *w_up,

@@ -7,7 +7,7 @@
 
 namespace qmm {
 
-enum Format : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1 };
+enum Format : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_Q4_K = 2 };
 
 constexpr int kBlock = 32;           // weights per GGUF block
 constexpr int kQ4Bytes = 18;         // fp16 d + 16 nibble bytes

@@ -156,6 +156,18 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
 QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * Prefill GEMM over Q4_K super-blocks (the layout of qmm_gemv_q4_k; the
+ * pages' CLIP/CLAP path runs whole sequences through it): the contract of
+ * qmm_gemm_q4_0, any M >= 1, with each weight d * sc * q - dmin * mn formed
+ * in f32 (rounded once) and rounded to bf16 (nearest even); x rounded to
+ * bf16, f32 accumulation. M = 1 runs qmm_gemv_q4_k instead (f32). Errors as
+ * for qmm_gemm_q4_0, plus QMM_EINVAL for K not a multiple of 256.
+ * Accuracy: |y - sum_k x w| <= 8e-3 * sum_k |x w|.
+ */
+QMM_API int qmm_gemm_q4_k(const float *x, const void *w, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream);
+
 /* Static English name of a status code ("QMM_OK", ...). */
 QMM_API const char *qmm_status_string(int status);
 

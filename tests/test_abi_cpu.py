@@ -171,3 +171,18 @@ def test_gemv_q4_k_rejected_before_launch(args, status, fragment):
     assert got == status, (args, qmm.qmm_last_error())
     assert fragment in qmm.qmm_last_error()
     assert "qmm_gemv_q4_k" in qmm.qmm_last_error()
+
+
+@pytest.mark.parametrize("args,status,fragment", [
+    ((0, B, C, 4, 8, 256), qmm.QMM_EINVAL, "null pointer"),
+    ((A, B, C, 0, 8, 256), qmm.QMM_EINVAL, ">= 1"),
+    ((A, B, C, 4, 8, 384), qmm.QMM_EINVAL, "multiple of 256"),
+    ((A, B, C, 4, 8, 65536 + 256), qmm.QMM_EUNSUPPORTED, "unsupported"),
+    ((A, B + 4, C, 4, 8, 256), qmm.QMM_EALIGN, "misaligned"),
+    ((A, B, B + 64, 4, 8, 256), qmm.QMM_EINVAL, "overlaps"),
+])
+def test_gemm_q4_k_rejected_before_launch(args, status, fragment):
+    got = qmm.qmm_gemm_q4_k(*args, 0)
+    assert got == status, (args, qmm.qmm_last_error())
+    assert fragment in qmm.qmm_last_error()
+    assert "qmm_gemm_q4_k" in qmm.qmm_last_error()

@@ -52,7 +52,7 @@ def run(entry, fmt, x, w, n, k):
     wt = torch.from_numpy(np.ascontiguousarray(w).reshape(-1)).cuda()
     fn = {"gemv_q4_0": qmm.gemv_q4_0, "gemv_q8_0": qmm.gemv_q8_0,
           "gemm_q4_0": qmm.gemm_q4_0, "gemm_q8_0": qmm.gemm_q8_0,
-          "gemv_q4_k": qmm.gemv_q4_k}[f"{entry}_{fmt}"]
+          "gemv_q4_k": qmm.gemv_q4_k, "gemm_q4_k": qmm.gemm_q4_k}[f"{entry}_{fmt}"]
     y = fn(xt, wt, n, k)
     torch.cuda.synchronize()
     return y.cpu().numpy()
@@ -242,27 +242,29 @@ def pad_golden(g, k=256):
     return x, w
 
 
-GOLDEN_RUNS = [(path, entry) for path in pins.golden_cases() for entry in ("gemv", "gemm")
-               if not (entry == "gemm" and path.name.startswith("q4_k"))]
+GOLDEN_RUNS = [(path, entry) for path in pins.golden_cases() for entry in ("gemv", "gemm")]
 
 
 @pytest.mark.parametrize("path,entry", GOLDEN_RUNS, ids=lambda v: getattr(v, "name", v))
 def test_golden_on_gpu(orc, path, entry):
     """Hand-derived blocks (embedded in K=256 with zero padding) against their
     exact values: within the contract bound, and bitwise where the exact value
-    is an integer (every partial sum is then exact in f32)."""
+    is an integer (every partial sum is then exact in f32) and, for the GEMM,
+    every weight is exact in bf16."""
     g = pins.load_golden(path)
     x, w = pad_golden(g)
     note(f"[golden] {path.name} {entry}")
-    if g["fmt"] == "q4_k":   # one activation row per call
+    if g["fmt"] == "q4_k" and entry == "gemv":   # one activation row per call
         y = np.concatenate([run(entry, "q4_k", x[i:i + 1], w, g["N"], 256)
                             for i in range(g["M"])]).reshape(1, -1)
     else:
-        y = run(entry, g["fmt"], x, w, g["N"], 256)
+        y = run(entry, g["fmt"], x, w, g["N"], 256).reshape(1, -1)
     exact = np.array([[float(v) for v in g["y"]]])
     _, s = orc.matmul(g["fmt"], x, w, g["N"], 256)
     s = s.reshape(y.shape)
     assert_parity(y, exact, s, TAU_GEMM if entry == "gemm" else TAU_GEMV, path.name)
+    if entry == "gemm" and g["fmt"] == "q4_k":
+        return  # weights like 63 * 13 - 1 = 818 need 9 bits: not exact in bf16
     integral = np.array([v.denominator == 1 for v in g["y"]])
     assert np.array_equal(y[0][integral], exact[0][integral])
 
@@ -571,3 +573,58 @@ def test_gemv_q4_k_repeatable_and_errors():
     assert e.value.status == qmm.QMM_EUNSUPPORTED
     with pytest.raises(ValueError):
         qmm.gemv_q4_k(torch.zeros(1, 384, device="cuda"), wt, 8, 384)
+
+
+# Q4_K through the prefill GEMM: M = 1 takes the GEMV (bitwise), 2-128 rows
+# the medium-M kernel, more the tiles (small and large)
+Q4_K_GEMM_SHAPES = [
+    (2048, 8192, 2048),                              # the prefill workload's shape
+    (2, 300, 512), (4, 1000, 2048), (5, 257, 768), (33, 4097, 1024), (64, 8192, 2048),
+    (128, 2049, 8192), (130, 257, 512), (300, 700, 1280), (1000, 2048, 8192),
+    (512, 1024, 2048), (257, 8193, 256),
+]
+
+
+@pytest.mark.parametrize("m,n,k", Q4_K_GEMM_SHAPES)
+def test_gemm_q4_k_shapes(orc, m, n, k):
+    check(orc, "gemm", "q4_k", m, n, k, seed=m + n + k)
+
+
+def test_gemm_q4_k_one_row_is_gemv():
+    n, k = 3000, 2048
+    x = synth.activations(1, k, seed=35)
+    w = synth.q4_k_weights(n, k, seed=35)
+    note("[exact] gemm_q4_k M=1 is the GEMV")
+    assert np.array_equal(run("gemm", "q4_k", x, w, n, k), run("gemv", "q4_k", x, w, n, k))
+
+
+def test_gemm_q4_k_integer_exact(orc):
+    """Weights sc q - mn with sc in {0, 1}, mn <= 15 and integer x are exact in
+    bf16 and every partial sum is an integer below 2^24: the GEMM is exact."""
+    n, k = 200, 2048
+    rng = np.random.default_rng(36)
+    ones = np.ones((n, k // 256), np.float16)
+    sc = rng.integers(0, 2, (n, k // 256, 8), dtype=np.uint8)
+    mn = rng.integers(0, 16, (n, k // 256, 8), dtype=np.uint8)
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    w = synth.pack_q4_k(ones, ones, sc, mn, q)
+    for m in (3, 40, 300):
+        x = rng.integers(-8, 9, (m, k)).astype(np.float32)
+        note(f"[exact] gemm_q4_k integer M={m}")
+        y = run("gemm", "q4_k", x, w, n, k)
+        yref, _ = orc.matmul("q4_k", x, w, n, k)
+        assert np.array_equal(y.astype(np.float64), yref), m
+
+
+def test_gemm_q4_k_one_hot_is_bf16_of_weight(orc):
+    n, k = 96, 1024
+    rng = np.random.default_rng(37)
+    w = synth.pack_q4_k(*q4_k_case(rng, n, k))
+    ks = rng.integers(0, k, 40)
+    x = np.zeros((40, k), np.float32)
+    x[np.arange(40), ks] = 1.0
+    note("[exact] gemm_q4_k one-hot")
+    y = run("gemm", "q4_k", x, w, n, k).astype(np.float64)
+    yref, _ = orc.matmul("q4_k", x, w, n, k)
+    want = torch.from_numpy(yref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(y, want.astype(np.float64))
