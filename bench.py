@@ -23,8 +23,8 @@ Timing:
 * the same method times the other rows: small-M GEMV (M = 2..16), the gated
   FFN front half, the Q4_K GEMV at the FFN pair's shapes, the Q8_0
   vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
-  GEMM (M = 2048, and short prompts
-  M = 16, 64, 128), reported under "rows".
+  GEMM (M = 2048, and short prompts M = 16, 64, 128; the M = 2048 shape also
+  over Q8_0 and Q4_K weights), reported under "rows".
 * HBM read references (bench_read.hip): the same timing over kernels that
   only read, on the same 9.4 MB weight copies (a plain coalesced read and
   the GEMV's 36-byte-pair pattern) and on 512 MiB buffers (the achievable
@@ -472,6 +472,16 @@ def main():
                                          frac_bf16_peak=tfl8 / BF16_PEAK_TFLOPS)
         log(f"[bench] prefill GEMM Q8_0: {t8['mean_us']:.2f} us, {tfl8:.1f} TFLOP/s")
         del w8
+        # and over Q4_K super-blocks (the pages' CLIP/CLAP format)
+        wq_h = synth.q4_k_weights(pre["N"], pre["K"])
+        wq = pool(wq_h)
+        tq = time_launches(lib.qmm_gemm_q4_k,
+                           gemv_args(xp, wq, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
+        tflq = fp / (tq["mean_us"] * 1e-6) / 1e12
+        rows["q4_k_gemm_prefill"] = dict(tq, flops=fp, tflops=tflq,
+                                         frac_bf16_peak=tflq / BF16_PEAK_TFLOPS)
+        log(f"[bench] prefill GEMM Q4_K: {tq['mean_us']:.2f} us, {tflq:.1f} TFLOP/s")
+        del wq
         # decode step model: 342 Q4_0 GEMVs (171 FFN pairs) + 1 Q8_0 GEMV
         t_step = 171 * (t_up["mean_us"] + t_dn["mean_us"]) + tv["mean_us"]
         rows["decode_tok_s_equiv"] = 1e6 / t_step
