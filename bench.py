@@ -29,6 +29,8 @@ Timing:
   only read, on the same 9.4 MB weight copies (a plain coalesced read and
   the GEMV's 36-byte-pair pattern) and on 512 MiB buffers (the achievable
   streaming rate), reported under "hbm_reference" and "rows".
+* gemm_reference (context): the ROCm BLAS library's bf16 GEMM with f32
+  output (torch.mm) at the prefill shape, on weights already held as bf16.
 * decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
   at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
   weight copy, captured in one HIP graph; 5 replays bracketed by HIP events
@@ -145,6 +147,37 @@ def summarize(us):
     q = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
     return {"mean_us": statistics.fmean(s), "median_us": statistics.median(s),
             "p10_us": q(0.1), "p90_us": q(0.9), "n": len(s)}
+
+
+def library_gemm_reference(xp, m, n, k, settle_ms, reps=50):
+    """Context only: torch.mm (the ROCm BLAS library) on bf16 operands with an
+    f32 output, at the prefill shape, on weights held as bf16 in HBM (no
+    quantized format, no dequantization). Timed eagerly between two events on
+    torch's current stream, after settle_ms of untimed calls. None when this
+    torch has no f32-output bf16 product."""
+    import torch
+    xb = xp.to(torch.bfloat16)
+    g = torch.Generator(device="cpu").manual_seed(0)
+    wb = (torch.randn(n, k, generator=g) * 0.05).to(device=xp.device, dtype=torch.bfloat16)
+    try:
+        fn = lambda: torch.mm(xb, wb.t(), out_dtype=torch.float32)  # noqa: E731
+        fn()
+    except (TypeError, RuntimeError):
+        return None
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    torch.cuda.synchronize()
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / reps
+    return {"op": "torch.mm bf16 x bf16 -> f32", "M": m, "N": n, "K": k, "mean_us": us,
+            "tflops": 2.0 * m * n * k / (us * 1e-6) / 1e12, "reps": reps}
 
 
 def main():
@@ -482,9 +515,18 @@ def main():
                                          frac_bf16_peak=tflq / BF16_PEAK_TFLOPS)
         log(f"[bench] prefill GEMM Q4_K: {tq['mean_us']:.2f} us, {tflq:.1f} TFLOP/s")
         del wq
+        # context: the vendor library's plain bf16 GEMM at the same shape with
+        # the same f32 output, on weights already held as bf16
+        gemm_ref = library_gemm_reference(xp, pre["M"], pre["N"], pre["K"], args.settle_ms)
+        if gemm_ref is not None:
+            gemm_ref["q4_0_fused_over_library"] = gemm_ref["mean_us"] / tp["mean_us"]
+            log(f"[bench] library bf16 GEMM (f32 out): {gemm_ref['mean_us']:.2f} us")
         # decode step model: 342 Q4_0 GEMVs (171 FFN pairs) + 1 Q8_0 GEMV
         t_step = 171 * (t_up["mean_us"] + t_dn["mean_us"]) + tv["mean_us"]
         rows["decode_tok_s_equiv"] = 1e6 / t_step
+
+    else:
+        gemm_ref = None
 
     # ------------------------------------------------ counters, if current
     traffic = None
@@ -547,6 +589,7 @@ def main():
             "note": "read-only kernels timed like the GEMVs: a 9.4 MB read per launch "
                     "costs this much before any arithmetic",
         },
+        "gemm_reference": gemm_ref,
         "rows": rows,
         "device": props.name,
     }
