@@ -139,6 +139,8 @@ GEMV_SHAPES = [
     (2, 2049, 8192), (4, 65, 16384), (3, 4099, 8448), (2, 65539, 1280), (3, 65537, 2048),
     # 5-16 rows with N < 8192 (16-row matrix-core workgroups)
     (5, 2048, 8192), (12, 2049, 8448),
+    # K at its maximum on the multi-row kernels
+    (2, 40, 65536), (8, 65, 65536), (16, 33, 65536),
     # one row, wide N, K <= 4096 (32 lanes x 2 chunks per row, ragged K)
     (1, 32769, 3328),
     # 9-16 rows with N >= 8192 (f32-exact 32-row weight slices): ragged M and
@@ -211,6 +213,31 @@ def test_gemm_shapes(orc, fmt, m, n, k):
 @pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512), (4097, 4100, 320)])
 def test_gemm_large_tile_shapes(orc, fmt, m, n, k):
     check(orc, "gemm", fmt, m, n, k, seed=m + n)
+
+
+# K at its maximum (65536) on each GEMM kernel: the medium-M bands and the
+# 128 x 128 tile against the full oracle result, the 256 x 256 tile at the
+# prefill workload's M and N on sampled outputs (corners included).
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k"])
+@pytest.mark.parametrize("m,n", [(40, 257), (130, 257)])
+def test_gemm_max_k(orc, fmt, m, n):
+    check(orc, "gemm", fmt, m, n, 65536, seed=m + n)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k"])
+def test_gemm_max_k_large_tiles_sampled(orc, fmt):
+    m, n, k = 2048, 8192, 65536
+    what = f"gemm_{fmt} M={m} N={n} K={k} seed=5 (sampled)"
+    note(f"[parity] {what}")
+    x = synth.activations(m, k, seed=5)
+    w = weights(fmt, n, k, seed=5)
+    y = run("gemm", fmt, x, w, n, k)
+    assert np.all(np.isfinite(y)), what
+    rng = np.random.default_rng(5)
+    ms = np.concatenate([[0, m - 1, 0, m - 1, 255, 256], rng.integers(0, m, 58)])
+    ns = np.concatenate([[0, n - 1, n - 1, 0, 256, 255], rng.integers(0, n, 58)])
+    yref, s = orc.matmul_at(fmt, x, w, n, k, ms, ns)
+    assert_parity(y[ms, ns], yref, s, TAU_GEMM, what)
 
 
 @pytest.mark.parametrize("m,n,k", [(2048, 2048, 8192), (255, 8191, 1024)])
