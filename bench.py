@@ -21,7 +21,8 @@ Timing:
   bracketed by HIP events on the launch stream; the per-launch mean
   includes the dispatch gap between consecutive kernels.
 * the same method times the other rows: small-M GEMV (M = 2..16), the gated
-  FFN front half, the Q4_K GEMV at the FFN pair's shapes, the Q8_0
+  FFN front half, the Q4_K GEMV at the FFN pair's shapes (and M = 2, 4
+  over the up matrix), the Q8_0
   vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
   GEMM (M = 2048, and short prompts M = 16, 64, 128; the M = 2048 shape also
   over Q8_0 and Q4_K weights), reported under "rows".
@@ -398,6 +399,20 @@ def main():
             bk = wk_h.nbytes + xk_h.nbytes + yk.numel() * 4
             rows[name] = dict(tk, bytes=bk, gbs=bk / (tk["mean_us"] * 1e-6) / 1e9)
             log(f"[bench] {name}: {tk['mean_us']:.2f} us")
+            # two and four activation rows over the up matrix (batched or
+            # speculative decode)
+            for m in ((2, 4) if name == "q4_k_gemv_ffn_up" else ()):
+                xm = torch.from_numpy(synth.activations(m, wlk["K"])).to(dev)
+                ym = torch.empty((m, wlk["N"]), device=dev)
+                t = time_launches(lib.qmm_gemv_q4_k,
+                                  gemv_args(xm, wk, ym, m, wlk["N"], wlk["K"], n))
+                b = wk_h.nbytes + xm.numel() * 4 + ym.numel() * 4
+                fl = 2 * m * wlk["N"] * wlk["K"]
+                rows[f"q4_k_gemv_small_m{m}"] = dict(
+                    t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
+                    tflops=fl / (t["mean_us"] * 1e-6) / 1e12,
+                    tokens_per_s=m / (t["mean_us"] * 1e-6))
+                log(f"[bench] q4_k small M={m}: {t['mean_us']:.2f} us")
             del wk
         # Q8_0 vocabulary GEMV
         voc = synth.WORKLOADS["q8_0_gemv_vocab"]

@@ -194,13 +194,13 @@ def gemm_q8_0(x, w, n: int, k: int, out=None):
 
 
 def gemv_q4_k(x, w, n: int, k: int, out=None):
-    """y[1, N] = x[1, K] @ W^T for Q4_K W (super-blocks of 256; M = 1)."""
+    """y[M, N] = x[M, K] @ W^T for Q4_K W (super-blocks of 256; 1 <= M <= 4)."""
     return _call(qmm_gemv_q4_k, "q4_k", x, w, n, k, out)
 
 
 def gemm_q4_k(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q4_K W, any M
-    (M = 1: the f32 GEMV result, bit for bit)."""
+    (M <= 4: the f32 GEMV result, bit for bit)."""
     return _call(qmm_gemm_q4_k, "q4_k", x, w, n, k, out)
 
 

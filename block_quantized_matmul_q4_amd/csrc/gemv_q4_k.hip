@@ -24,6 +24,11 @@
 // once), one FMA into the sub-block's sum. The T threads of a row reduce
 // with DPP row operations (and through LDS when a row spans two waves) in a
 // fixed order.
+//
+// With MR activation rows (2 or 4; M = 3 runs four, the fourth repeating
+// the third and not stored) each weight is formed once and applied to every
+// row, and each row's operations run in the one-row order, so a row of the
+// result equals the one-row result bit for bit when both use the same T.
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -50,16 +55,18 @@ __device__ __forceinline__ void sub_block(uint32_t b0, uint32_t b1, uint32_t b2,
     }
 }
 
-template <int T, int WG>
+template <int T, int WG, int MR>
 __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__ x,
                                                        const uint8_t *__restrict__ w,
-                                                       float *__restrict__ y, int N, int C)
+                                                       float *__restrict__ y, int M, int N,
+                                                       int C)
 {
     constexpr int RPAR = WG / T;                // rows per workgroup
     constexpr int TW = T < 64 ? T : 64;         // chunks per wave per row
     constexpr int WPR = T / TW;                 // waves per row
-    constexpr int XU = (16 * T + WG - 1) / WG;  // staged float4 per thread and pass
-    __shared__ __attribute__((aligned(16))) float xs[T * XS];
+    constexpr int XU = (16 * T + WG - 1) / WG;  // staged float4 per thread, row and pass
+    static_assert(MR == 1 || WPR == 1, "several activation rows: a weight row within a wave");
+    __shared__ __attribute__((aligned(16))) float xs[MR * T * XS];
     __shared__ float red[WPR > 1 ? WG / 64 : 1];
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -68,17 +75,25 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
     const int64_t row_bytes = (int64_t)(C / 4) * kQKBytes;
     const uint8_t *wrow = w + (int64_t)min(n, N - 1) * row_bytes;
 
-    float acc = 0.f;
-    for (int c0 = 0; c0 < C; c0 += T) {
-        // 1. this pass's activations: float4 i is chunk i / 16, part i % 16
-        //    (four scalar arrays: an array of float4 is kept in scratch)
-        float xvx[XU], xvy[XU], xvz[XU], xvw[XU];
+    float acc[MR];
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int i = tid + WG * u;
-            const int ch = min(c0 + min(i / 16, T - 1), C - 1);
-            const float4 v = *reinterpret_cast<const float4 *>(x + 64 * ch + 4 * (i % 16));
-            xvx[u] = v.x; xvy[u] = v.y; xvz[u] = v.z; xvw[u] = v.w;
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+    for (int c0 = 0; c0 < C; c0 += T) {
+        // 1. this pass's activations: float4 i of a row is chunk i / 16,
+        //    part i % 16 (four scalar arrays: an array of float4 is kept in
+        //    scratch)
+        float xvx[MR * XU], xvy[MR * XU], xvz[MR * XU], xvw[MR * XU];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const float *xr = x + (int64_t)min(r, M - 1) * (64 * (int64_t)C);
+#pragma unroll
+            for (int u = 0; u < XU; ++u) {
+                const int i = tid + WG * u;
+                const int ch = min(c0 + min(i / 16, T - 1), C - 1);
+                const float4 v = *reinterpret_cast<const float4 *>(xr + 64 * ch + 4 * (i % 16));
+                xvx[r * XU + u] = v.x; xvy[r * XU + u] = v.y;
+                xvz[r * XU + u] = v.z; xvw[r * XU + u] = v.w;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // 2. the super-block header and the chunk's nibbles
@@ -93,23 +108,31 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
         //    previous pass's readers)
         if (c0 != 0) __syncthreads();
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int i = tid + WG * u;
-            if (16 * T % WG == 0 || i < 16 * T)
-                *reinterpret_cast<float4 *>(&xs[(i / 16) * XS + 4 * (i % 16)]) =
-                    make_float4(xvx[u], xvy[u], xvz[u], xvw[u]);
+        for (int r = 0; r < MR; ++r) {
+#pragma unroll
+            for (int u = 0; u < XU; ++u) {
+                const int i = tid + WG * u;
+                if (16 * T % WG == 0 || i < 16 * T)
+                    *reinterpret_cast<float4 *>(&xs[(r * T + i / 16) * XS + 4 * (i % 16)]) =
+                        make_float4(xvx[r * XU + u], xvy[r * XU + u], xvz[r * XU + u],
+                                    xvw[r * XU + u]);
+            }
         }
         lds_only_barrier();
         // 4. the chunk's 64 weights against its activations
         const float d = half_lo(hdr.x), dmin = half_hi(hdr.x);
         const uint32_t nb[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        float part = 0.f;
+        float part[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) part[r] = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t sc, mn;
             sub_block(hdr.y, hdr.z, hdr.w, c, h, sc, mn);
             const float dsc = d * (float)sc, dmn = dmin * (float)mn;
-            float s = 0.f;
+            float s[MR];
+#pragma unroll
+            for (int r = 0; r < MR; ++r) s[r] = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 uint32_t v = h ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
@@ -118,23 +141,37 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
                 // converting it; this way each byte converts in one
                 // v_cvt_f32_ubyteN
                 asm("" : "+v"(v));
-                const float4 xa =
-                    *reinterpret_cast<const float4 *>(&xs[t * XS + 32 * h + 4 * i]);
-                s = fmaf(fmaf(dsc, (float)(v & 0xFFu), -dmn), xa.x, s);
-                s = fmaf(fmaf(dsc, (float)((v >> 8) & 0xFFu), -dmn), xa.y, s);
-                s = fmaf(fmaf(dsc, (float)((v >> 16) & 0xFFu), -dmn), xa.z, s);
-                s = fmaf(fmaf(dsc, (float)(v >> 24), -dmn), xa.w, s);
+                const float w0 = fmaf(dsc, (float)(v & 0xFFu), -dmn);
+                const float w1 = fmaf(dsc, (float)((v >> 8) & 0xFFu), -dmn);
+                const float w2 = fmaf(dsc, (float)((v >> 16) & 0xFFu), -dmn);
+                const float w3 = fmaf(dsc, (float)(v >> 24), -dmn);
+#pragma unroll
+                for (int r = 0; r < MR; ++r) {
+                    const float4 xa = *reinterpret_cast<const float4 *>(
+                        &xs[(r * T + t) * XS + 32 * h + 4 * i]);
+                    s[r] = fmaf(w0, xa.x, s[r]);
+                    s[r] = fmaf(w1, xa.y, s[r]);
+                    s[r] = fmaf(w2, xa.z, s[r]);
+                    s[r] = fmaf(w3, xa.w, s[r]);
+                }
             }
-            part += s;
+#pragma unroll
+            for (int r = 0; r < MR; ++r) part[r] += s[r];
         }
-        acc += c0 + t < C ? part : 0.f;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) acc[r] += c0 + t < C ? part[r] : 0.f;
     }
 
-    acc = group_sum<TW>(acc);
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = group_sum<TW>(acc[r]);
     if constexpr (WPR == 1) {
-        if (t == T - 1 && n < N) y[n] = acc;
+        if (t == T - 1 && n < N) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+                if (r < M) y[(int64_t)r * N + n] = acc[r];
+        }
     } else {
-        if (lane == 63) red[wave] = acc;
+        if (lane == 63) red[wave] = acc[0];
         __syncthreads();
         if (tid < RPAR) {
             float s = 0.f;
@@ -146,13 +183,28 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
     }
 }
 
-template <int T, int WG>
-hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int C, hipStream_t stream)
+template <int T, int WG, int MR>
+hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int C,
+                  hipStream_t stream)
 {
     constexpr int rows = WG / T;
-    hipLaunchKernelGGL((gemv_q4_k_kernel<T, WG>), dim3((N + rows - 1) / rows), dim3(WG), 0,
-                       stream, x, w, y, N, C);
+    hipLaunchKernelGGL((gemv_q4_k_kernel<T, WG, MR>), dim3((N + rows - 1) / rows), dim3(WG),
+                       0, stream, x, w, y, M, N, C);
     return hipGetLastError();
+}
+
+// Several activation rows: T up to 64 (rows longer than 64 chunks take
+// several passes), so that a weight row stays within one wave and the
+// staged rows fit twice per compute unit's LDS.
+template <int MR>
+hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N, int C,
+                       hipStream_t stream)
+{
+    if (C <= 4) return launch<4, 256, MR>(x, w, y, M, N, C, stream);
+    if (C <= 8) return launch<8, 256, MR>(x, w, y, M, N, C, stream);
+    if (C <= 16) return launch<16, 256, MR>(x, w, y, M, N, C, stream);
+    if (C <= 32) return launch<32, 256, MR>(x, w, y, M, N, C, stream);
+    return launch<64, 512, MR>(x, w, y, M, N, C, stream);
 }
 
 }  // namespace
@@ -161,16 +213,18 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int N, int C, hipS
 // 16, 32, 64 and 128 that covers a row in one pass (rows longer than 128
 // chunks take several passes); the same shapes as the Q4_0 GEMV, whose
 // chunks (pairs of blocks) hold as many weights and bytes.
-hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int N, int K,
+hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream)
 {
     const int C = K / 64;
-    if (C <= 4) return launch<4, 256>(x, w, y, N, C, stream);
-    if (C <= 8) return launch<8, 256>(x, w, y, N, C, stream);
-    if (C <= 16) return launch<16, 256>(x, w, y, N, C, stream);
-    if (C <= 32) return launch<32, 256>(x, w, y, N, C, stream);
-    if (C <= 64) return launch<64, 512>(x, w, y, N, C, stream);
-    return launch<128, 512>(x, w, y, N, C, stream);
+    if (M == 2) return launch_rows<2>(x, w, y, M, N, C, stream);
+    if (M > 2) return launch_rows<4>(x, w, y, M, N, C, stream);
+    if (C <= 4) return launch<4, 256, 1>(x, w, y, M, N, C, stream);
+    if (C <= 8) return launch<8, 256, 1>(x, w, y, M, N, C, stream);
+    if (C <= 16) return launch<16, 256, 1>(x, w, y, M, N, C, stream);
+    if (C <= 32) return launch<32, 256, 1>(x, w, y, M, N, C, stream);
+    if (C <= 64) return launch<64, 512, 1>(x, w, y, M, N, C, stream);
+    return launch<128, 512, 1>(x, w, y, M, N, C, stream);
 }
 
 }  // namespace qmm

@@ -36,7 +36,7 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                               float *h, int N, int K, hipStream_t stream);
 // Q4_K GEMV, one activation row (K % 256 == 0).
-hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int N, int K,
+hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream);
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t stream);

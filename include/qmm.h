@@ -136,7 +136,7 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
                                  hipStream_t stream);
 
 /*
- * Decode GEMV over Q4_K super-blocks, one activation row (M = 1). Q4_K is the
+ * Decode GEMV over Q4_K super-blocks, 1 <= M <= 4 activation rows. Q4_K is the
  * k-quant 4-bit format the pages ("Add generated quant-kernel JIT and
  * accelerate Gemma4, BGE-M3, and GLiNER2", section Summary) keep for their
  * CLIP/CLAP path; they give no layout, and GGUF's is taken. w is N rows of
@@ -148,9 +148,11 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
  *   (weight 64c+i, i < 32, is the low nibble of byte 16+32c+i, weight
  *   64c+32+i its high nibble); weight e is in sub-block e/32 and
  *   w = d * sc * q - dmin * mn.
- * x is f32[1][K], y f32[1][N] (overwritten). Errors as for qmm_gemv_q4_0,
- * plus QMM_EINVAL for K not a multiple of 256 and QMM_EUNSUPPORTED for
- * M != 1. Accuracy: |y - sum_k x w| <= 1e-4 * sum_k |x w|, each w rounded
+ * x is f32[M][K], y f32[M][N] (overwritten). Each weight is formed once
+ * and applied to every activation row; a row of the result does not depend
+ * on the other rows. Errors as for qmm_gemv_q4_0, plus QMM_EINVAL for K not
+ * a multiple of 256 and QMM_EUNSUPPORTED for M > 4 (qmm_gemm_q4_k takes
+ * any M). Accuracy: |y - sum_k x w| <= 1e-4 * sum_k |x w|, each w rounded
  * once to f32 and each product accumulated in f32.
  */
 QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
@@ -161,7 +163,7 @@ QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
  * pages' CLIP/CLAP path runs whole sequences through it): the contract of
  * qmm_gemm_q4_0, any M >= 1, with each weight d * sc * q - dmin * mn formed
  * in f32 (rounded once) and rounded to bf16 (nearest even); x rounded to
- * bf16, f32 accumulation. M = 1 runs qmm_gemv_q4_k instead (f32). Errors as
+ * bf16, f32 accumulation. M <= 4 runs qmm_gemv_q4_k instead (f32). Errors as
  * for qmm_gemm_q4_0, plus QMM_EINVAL for K not a multiple of 256.
  * Accuracy: |y - sum_k x w| <= 8e-3 * sum_k |x w|.
  */

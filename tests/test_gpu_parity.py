@@ -593,7 +593,7 @@ def test_gemv_q4_k_repeatable_and_errors():
     note("[determinism] gemv_q4_k")
     ys = [run("gemv", "q4_k", x, w, n, k) for _ in range(3)]
     assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
-    xt = torch.zeros(2, 256, device="cuda")
+    xt = torch.zeros(5, 256, device="cuda")
     wt = torch.zeros(8 * 144, dtype=torch.uint8, device="cuda")
     with pytest.raises(qmm.QmmError) as e:
         qmm.gemv_q4_k(xt, wt, 8, 256)
@@ -602,7 +602,32 @@ def test_gemv_q4_k_repeatable_and_errors():
         qmm.gemv_q4_k(torch.zeros(1, 384, device="cuda"), wt, 8, 384)
 
 
-# Q4_K through the prefill GEMM: M = 1 takes the GEMV (bitwise), 2-128 rows
+# Two to four activation rows: every launch shape (one and several passes),
+# ragged N, M = 3 (four rows run, the fourth not stored)
+Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
+                    (2, 17, 256), (3, 4099, 8448), (4, 65, 16384), (2, 50, 65536),
+                    (4, 2049, 4352), (3, 9000, 1024)]
+
+
+@pytest.mark.parametrize("m,n,k", Q4_K_ROWS_SHAPES)
+def test_gemv_q4_k_rows(orc, m, n, k):
+    check(orc, "gemv", "q4_k", m, n, k, seed=m + n + k)
+
+
+# Up to 64 chunks per row (K <= 4096) the multi-row launch uses the one-row
+# launch's threads per row: each row then equals the one-row result bit for bit.
+@pytest.mark.parametrize("m,n,k", [(2, 1000, 1024), (4, 8192, 2048), (3, 333, 4096),
+                                   (4, 300, 256)])
+def test_gemv_q4_k_rows_match_single_row_bitwise(m, n, k):
+    x = synth.activations(m, k, seed=38)
+    w = synth.q4_k_weights(n, k, seed=38)
+    note(f"[bitwise] gemv_q4_k M={m} N={n} K={k} rows against M=1")
+    y = run("gemv", "q4_k", x, w, n, k)
+    for r in range(m):
+        assert np.array_equal(y[r], run("gemv", "q4_k", x[r:r + 1], w, n, k)[0]), r
+
+
+# Q4_K through the prefill GEMM: M <= 4 takes the GEMV (bitwise), 5-128 rows
 # the medium-M kernel, more the tiles (small and large)
 Q4_K_GEMM_SHAPES = [
     (2048, 8192, 2048),                              # the prefill workload's shape
@@ -617,11 +642,12 @@ def test_gemm_q4_k_shapes(orc, m, n, k):
     check(orc, "gemm", "q4_k", m, n, k, seed=m + n + k)
 
 
-def test_gemm_q4_k_one_row_is_gemv():
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_gemm_q4_k_few_rows_is_gemv(m):
     n, k = 3000, 2048
-    x = synth.activations(1, k, seed=35)
+    x = synth.activations(m, k, seed=35)
     w = synth.q4_k_weights(n, k, seed=35)
-    note("[exact] gemm_q4_k M=1 is the GEMV")
+    note(f"[exact] gemm_q4_k M={m} is the GEMV")
     assert np.array_equal(run("gemm", "q4_k", x, w, n, k), run("gemv", "q4_k", x, w, n, k))
 
 
