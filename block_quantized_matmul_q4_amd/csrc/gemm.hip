@@ -251,7 +251,12 @@ template <> struct BFmt<FMT_Q4_K> {
     __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int q,
                                            __bf16 *dst)
     {
-        const int h = q / 2, qq = q % 2, c = (int)b[8];
+        const int h = q / 2, qq = q % 2;
+        // c is the same across the wave; hidden from the compiler, the
+        // choices below stay per-lane selects instead of becoming branches
+        // that would split the K step into many basic blocks
+        int c = (int)b[8];
+        asm("" : "+v"(c));
         const int sh = 8 * (2 * (c & 1) + h);
         const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
         const uint32_t x2 = (b[3] >> sh) & 0xFFu;
@@ -263,7 +268,10 @@ template <> struct BFmt<FMT_Q4_K> {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t raw = b[4 + 2 * qq + t];
-            const uint32_t nib = h ? (raw >> 4) & 0x0F0F0F0Fu : raw & 0x0F0F0F0Fu;
+            uint32_t nib = h ? (raw >> 4) & 0x0F0F0F0Fu : raw & 0x0F0F0F0Fu;
+            // hidden range: each byte converts in one v_cvt_f32_ubyteN
+            // instead of a bit-field extract and a conversion
+            asm("" : "+v"(nib));
             o[2 * t] = pack_bf16x2(fmaf(dsc, (float)(nib & 0xFFu), -dmn),
                                    fmaf(dsc, (float)((nib >> 8) & 0xFFu), -dmn));
             o[2 * t + 1] = pack_bf16x2(fmaf(dsc, (float)((nib >> 16) & 0xFFu), -dmn),
