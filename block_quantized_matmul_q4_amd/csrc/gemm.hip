@@ -230,7 +230,7 @@ template <> struct BFmt<FMT_Q8_0> {
 // d sc q - dmin mn (both products exact), and rounded to bf16 (nearest even).
 template <> struct BFmt<FMT_Q4_K> {
     static constexpr int kPairBytes = 36;   // per K step, on average (144 per 4 steps)
-    static constexpr int kWin = 9;
+    static constexpr int kWin = 11;         // + d sc and dmin mn of the current sub-block
 
     __device__ static void load_step(__amdgpu_buffer_rsrc_t r, int row_off, int blk, int p,
                                      uint32_t (&b)[kWin])
@@ -247,22 +247,32 @@ template <> struct BFmt<FMT_Q4_K> {
     // quarter q: sub-block 2c + q / 2 (low or high nibbles), nibble bytes
     // 16 blk + 8 (q % 2) .. +7 -> elements 32 (q / 2) + 16 blk + 8 (q % 2) ..
     // +7 of the K step; dst is the row's base plus 32 blk (as for the block
-    // formats), one 16-byte LDS store
-    __device__ static void convert_quarter(const uint32_t (&b)[kWin], int blk, int q,
-                                           __bf16 *dst)
+    // formats), one 16-byte LDS store. Callers convert a window's quarters in
+    // order 0..3: the even quarter unpacks its sub-block's scale and minimum
+    // into b[9], b[10] and the odd one reuses them.
+    __device__ static void convert_quarter(uint32_t (&b)[kWin], int blk, int q, __bf16 *dst)
     {
         const int h = q / 2, qq = q % 2;
-        // c is the same across the wave; hidden from the compiler, the
-        // choices below stay per-lane selects instead of becoming branches
-        // that would split the K step into many basic blocks
-        int c = (int)b[8];
-        asm("" : "+v"(c));
-        const int sh = 8 * (2 * (c & 1) + h);
-        const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
-        const uint32_t x2 = (b[3] >> sh) & 0xFFu;
-        const uint32_t sc = c < 2 ? (x0 & 63u) : ((x2 & 15u) | ((x0 >> 6) << 4));
-        const uint32_t mn = c < 2 ? (x1 & 63u) : ((x2 >> 4) | ((x1 >> 6) << 4));
-        const float dsc = half_lo(b[0]) * (float)sc, dmn = half_hi(b[0]) * (float)mn;
+        float dsc, dmn;
+        if (qq == 0) {
+            // c is the same across the wave; hidden from the compiler, the
+            // choices below stay per-lane selects instead of becoming
+            // branches that would split the K step into many basic blocks
+            int c = (int)b[8];
+            asm("" : "+v"(c));
+            const int sh = 8 * (2 * (c & 1) + h);
+            const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
+            const uint32_t x2 = (b[3] >> sh) & 0xFFu;
+            const uint32_t sc = c < 2 ? (x0 & 63u) : ((x2 & 15u) | ((x0 >> 6) << 4));
+            const uint32_t mn = c < 2 ? (x1 & 63u) : ((x2 >> 4) | ((x1 >> 6) << 4));
+            dsc = half_lo(b[0]) * (float)sc;
+            dmn = half_hi(b[0]) * (float)mn;
+            b[9] = __float_as_uint(dsc);
+            b[10] = __float_as_uint(dmn);
+        } else {
+            dsc = __uint_as_float(b[9]);
+            dmn = __uint_as_float(b[10]);
+        }
         uint4 v;
         uint32_t *o = &v.x;
 #pragma unroll
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
     // 2q, 2q+1 (f32 -> bf16, RNE) and quarter q of weight block b_blk (->
     // bf16, RNE), so each of the four substeps' matrix-core work hides the
     // same share of the conversion.
-    auto convert = [&](int buf, int q, const uint32_t (&b)[BF::kWin]) {
+    auto convert = [&](int buf, int q, uint32_t (&b)[BF::kWin]) {
 #pragma unroll
         for (int u = 2 * q; u < 2 * q + 2; ++u) {
             const float4 v = a_reg[u];
