@@ -524,7 +524,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
 
     using BF = BFmt<FMT>;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    // the wave index is the same on every lane; read from one lane, the
+    // compiler knows it (and the K steps derived from it) to be uniform, so
+    // the buffer loads' scalar offsets need no per-lane loop
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int rows = min(BM, M - m0);
     const int P = K / 64;
@@ -640,7 +643,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
 
     using BF = BFmt<FMT>;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    // the wave index is the same on every lane; read from one lane, the
+    // compiler knows it (and the K steps derived from it) to be uniform, so
+    // the buffer loads' scalar offsets need no per-lane loop
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
     const int n0 = blockIdx.x * BN;
     const int P = K / 64;
     const int row_bytes = P * BF::kPairBytes;
