@@ -1,6 +1,6 @@
 // Matrix-core kernels over GGUF Q4_0 / Q8_0 weights: the prefill GEMM's
 // tile kernel (described here), the medium-M GEMM (5-128 rows) and the
-// f32-exact weight-slice GEMV (9-16 rows), each introduced where it starts.
+// weight-slice GEMV to the f32 bound (9-16 rows), each introduced where it starts.
 //
 // Prefill GEMM over GGUF Q4_0 or Q8_0 weights on the bf16 matrix cores:
 // y[m][n] = sum_k bf16(x[m][k]) * bf16(w[n][k]) with f32 accumulation, where
@@ -505,13 +505,6 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
 // MT 32x32x16 MFMAs per 16-wide substep; the next step's loads are issued
 // before this step's matrix-core work. Rows past M and columns past N load
 // zeros through the buffer resources' range checks and are not stored.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int FMT, int MT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
@@ -624,14 +617,14 @@ hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, 
     return hipGetLastError();
 }
 
-// f32-exact variant for 5 .. 16 activation rows (the GEMV entry points'
+// Variant to the f32 bound for 5 .. 16 activation rows (the GEMV entry points'
 // accuracy): the same slices and interleaved K steps, but the 32 A rows
 // hold hi = bf16(x) of the (up to 16) activation rows in rows 0-15 and
 // lo = bf16(x - hi) in rows 16-31, the weight operand holds the integer
 // codes (exact in bf16), and each block's two MFMAs run into a fresh f32
 // tile that is scaled by the block's fp16 d in f32 before it is added to
-// the accumulators. Products are exact; y[m] = (C[m] + C[m + 16]) x the
-// codes' scale.
+// the accumulators. The split represents x to within 2^-17 |x| and each
+// code-term product is exact; y[m] = (C[m] + C[m + 16]) x the codes' scale.
 template <int FMT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         if constexpr (SX) {
             if (c0 != 0) __syncthreads();       // previous pass's readers done
         } else {
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
         }
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         }
         if constexpr (LB) lds_only_barrier();
         else if constexpr (SX) __syncthreads();
-        else __builtin_amdgcn_wave_barrier();
+        else wave_lds_sync();
         // 4. per chunk: FMAs
 #pragma unroll
         for (int h = 0; h < CH; ++h) {

@@ -1,5 +1,5 @@
-// Decode GEMV over Q4_K super-blocks, one activation row:
-// y[n] = sum_k x[k] * w[n][k], f32 arithmetic.
+// Decode GEMV over Q4_K super-blocks, 1 to 4 activation rows:
+// y[m][n] = sum_k x[m][k] * w[n][k], f32 arithmetic.
 //
 // Q4_K is the k-quant 4-bit format the pages keep for their CLIP/CLAP path
 // (named without a layout; GGUF's is read here). A super-block of 256
@@ -209,10 +209,12 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
 
 }  // namespace
 
-// C = K / 64 chunks per row (a multiple of 4). T is the smallest of 4, 8,
-// 16, 32, 64 and 128 that covers a row in one pass (rows longer than 128
-// chunks take several passes); the same shapes as the Q4_0 GEMV, whose
-// chunks (pairs of blocks) hold as many weights and bytes.
+// C = K / 64 chunks per row (a multiple of 4). With one activation row, T
+// is the smallest of 4, 8, 16, 32, 64 and 128 that covers a row in one pass
+// (rows longer than 128 chunks take several passes); the same shapes as the
+// Q4_0 GEMV, whose chunks (pairs of blocks) hold as many weights and bytes.
+// Two to four rows keep T at 64 past 32 chunks (launch_rows), so that the
+// staged rows fit twice per compute unit's LDS.
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream)
 {

@@ -9,14 +9,15 @@
 // With several activation rows the f32 FMA count (M per weight) outgrows
 // the weight stream, so the contraction moves to v_mfma_f32_16x16x32_bf16:
 // one instruction covers 16 A rows x 16 weight rows x one 32-wide block.
-// Exactness is kept where it matters:
+// Accuracy is kept to the f32 bound:
 //  * B operand (weights): the integer codes 16*(q-8) (Q4_0) or q (Q8_0),
 //    exact in bf16. The fp16 scale d is applied in f32 to the block's
 //    result, so no weight is rounded.
 //  * A operand (activations): x = hi + lo with hi = bf16(x) and
-//    lo = bf16(x - hi), both round-to-nearest-even; both products are exact
-//    and accumulate in f32. The representation error is at most 2^-17 |x|
-//    per term, far inside the 1e-4 relative bound. For M <= 8 (PACK) the hi
+//    lo = bf16(x - hi), both round-to-nearest-even; hi + lo represents x to
+//    within 2^-17 |x| (about 16 of its 24 significand bits), each product
+//    of a code and a term is exact, and the products accumulate in f32:
+//    far inside the 1e-4 relative bound. For M <= 8 (PACK) the hi
 //    rows and lo rows share one instruction (A rows m and M + m); for M > 8
 //    they take one instruction each.
 // Within a block the k order is permuted identically in A and B so that
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
                 *reinterpret_cast<const uint32_t *>(src + 4 * (L::kPairDwords - 1));
         }
         // ---- 2. to LDS
-        __builtin_amdgcn_wave_barrier();            // previous pass's reads done
+        wave_lds_sync();            // previous pass's reads done
         {
             const int b = lane / 8, kk = 4 * (lane % 8);
             int g, e0;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
 #pragma unroll
         for (int u = 0; u < PPL; ++u)
             L::relayout(D[u], wl + lrow * WROW + (lp0 + u) * L::kPairDwords);
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
         // ---- 3. matrix cores
         const int col = lane % 16, g = lane / 16;
 #pragma unroll

@@ -93,7 +93,7 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
         return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
     }
     // Up to 4 rows the decode GEMV kernel streams the weights once with
-    // f32-exact products: faster than any matrix-core tiling there, and well
+    // products rounded once in f32: faster than any matrix-core tiling there, and well
     // inside this entry point's bound.
     if (M <= qmm::kGemvRowsMax)
         return finish(fn, qmm::launch_gemv_m1(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));

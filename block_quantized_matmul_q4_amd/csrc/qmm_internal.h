@@ -27,7 +27,8 @@ hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, i
                           int N, int K, hipStream_t stream);
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream);
-// f32-exact GEMV on the matrix cores over 32-row weight slices, M <= 16
+// GEMV to the f32 bound on the matrix cores over 32-row weight slices (x as
+// two bf16 terms, within 2^-17 |x|), M <= 16
 // (taken for 9 <= M <= 16, Q8_0 only from N = 8192: Q4_0 at M = 16,
 // N = 8192, K = 2048 7.9 us against 10.6 us on the small-M kernel; Q8_0 at
 // N = 65536 54 against 79 us)
@@ -35,7 +36,7 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
                               int N, int K, hipStream_t stream);
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                               float *h, int N, int K, hipStream_t stream);
-// Q4_K GEMV, one activation row (K % 256 == 0).
+// Q4_K GEMV, 1 to 4 activation rows (K % 256 == 0).
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream);
 hipError_t launch_gemm(int fmt, const float *x, const uint8_t *w, float *y, int M, int N,
@@ -89,6 +90,17 @@ __device__ __forceinline__ void lds_only_barrier()
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes
+// of the same wave (and reads before later writes). The wave barrier alone
+// carries no memory ordering for the compiler; the wavefront-scope fences
+// keep it from moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int CTRL, int ROW_MASK>

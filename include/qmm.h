@@ -44,6 +44,15 @@
  *   qmm_gemm_q4_0, qmm_gemm_q8_0 (bf16 MFMA, f32 acc): |y - y_exact| <= 8e-3 * s
  * for finite inputs whose f32 products do not underflow. Results are
  * bitwise reproducible from call to call (no atomics, fixed reduction order).
+ *
+ * Non-finite scales: with finite x, y[m][n] is non-finite exactly when
+ * weight row n holds a block whose fp16 scale (Q4_K: d or dmin) is +Inf,
+ * -Inf or NaN; every other output keeps the bound above. Which non-finite
+ * value comes out (NaN, +Inf or -Inf) is not specified and may differ from
+ * the definition evaluated weight by weight: the GEMV kernels apply d to a
+ * block's partial sum, so an infinite scale over a zero code (q = 8) gives
+ * +-Inf where d * (q - 8) * x would give NaN. The gated entry point's h[n] is
+ * non-finite exactly when row n of W_gate or of W_up holds such a scale.
  */
 #ifndef QMM_H
 #define QMM_H
@@ -82,9 +91,11 @@ typedef enum qmm_status {
  * several tokens share one pass over the weights). f32 accumulation; the
  * weights stream from HBM once per call. Up to 4 rows take f32 FMAs on
  * codes converted exactly to f32, and each row rounds as in a one-row call
- * of the same launch shape; 5 to 16 rows take the bf16 matrix cores with
- * exact products (codes exact in bf16, x split into two bf16 terms, the
- * fp16 scale applied per block in f32).
+ * of the same launch shape; 5 to 16 rows take the bf16 matrix cores: the
+ * codes are exact in bf16 and x is carried as two bf16 terms, hi = bf16(x)
+ * and lo = bf16(x - hi), which represent x to within 2^-17 |x| (about 16 of
+ * its 24 significand bits); each code-term product is exact, sums are f32
+ * and the fp16 scale is applied per block in f32.
  */
 QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

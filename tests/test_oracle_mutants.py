@@ -39,6 +39,9 @@ MUTANTS = [
     ("d_applied_twice", "return d * (double)(q - 8);", "return d * d * (double)(q - 8);"),
     ("f32_accumulation", "acc += t;", "acc = (float)(acc + t);"),
     ("gelu_constant_swapped", "sqrt(2.0 / M_PI)", "sqrt(M_PI / 2.0)"),
+    ("gelu_constant_rounded", "const double c = sqrt(2.0 / M_PI);", "const double c = 0.8;"),
+    ("gelu_constant_rounded_3", "const double c = sqrt(2.0 / M_PI);", "const double c = 0.797;"),
+    ("gelu_cubic_off_10pct", "0.044715 * g * g * g", "0.04 * g * g * g"),
     ("gelu_cubic_term", "0.044715 * g * g * g", "0.44715 * g * g * g"),
     ("gelu_half_dropped", "return 0.5 * g * (1.0 +", "return g * (1.0 +"),
     ("gated_uses_up_twice", "full(0, x, w_gate, M, N, K, g, sg);", "full(0, x, w_up, M, N, K, g, sg);"),
