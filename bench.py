@@ -16,31 +16,45 @@ Timing:
   are replayed untimed for --settle-ms (default 50 ms): the shader clock
   rises over the first 20-30 ms of sustained load, and a timing taken right
   after an idle spell or a fresh allocation reads up to 25 % slow.
-* per-kernel durations: --samples launches of one kernel (cycling through
-  the cold pool) captured back to back in a HIP graph; each of 5 replays is
+* per-kernel rows: --samples launches of one kernel (cycling through the
+  cold pool) captured back to back in a HIP graph; each of 5 replays is
   bracketed by HIP events on the launch stream; the per-launch mean
-  includes the dispatch gap between consecutive kernels.
-* the same method times the other rows: small-M GEMV (M = 2..16), the gated
-  FFN front half, the Q4_K GEMV at the FFN pair's shapes (and M = 2, 4
-  over the up matrix), the Q8_0
-  vocabulary GEMV (and the same head over Q4_0 weights) and the Q4_0 prefill
-  GEMM (M = 2048, and short prompts M = 16, 64, 128; the M = 2048 shape also
-  over Q8_0 and Q4_K weights), reported under "rows".
-* HBM read references (bench_read.hip): the same timing over kernels that
-  only read, on the same 9.4 MB weight copies (a plain coalesced read and
-  the GEMV's 36-byte-pair pattern) and on 512 MiB buffers (the achievable
-  streaming rate), reported under "hbm_reference" and "rows".
-* gemm_reference (context): the ROCm BLAS library's bf16 GEMM with f32
-  output (torch.mm) at the prefill shape, on weights already held as bf16.
-* decode_step_replay: one decode step's 343 GEMV dispatches (171 FFN pairs
-  at the shapes above, then the Q8_0 vocabulary GEMV), each on its own cold
-  weight copy, captured in one HIP graph; 5 replays bracketed by HIP events
-  give the measured time per token (gaps between dispatches included).
+  includes the dispatch gap between consecutive kernels. Every row is timed
+  twice, once with the rows in forward order and once in backward order;
+  the row reports both passes and their mean.
+* per-dispatch: the headline GEMVs and the tiny GEMV are also launched
+  eagerly --dispatches times, each launch bracketed by its own pair of HIP
+  events (the GPU's own timestamps; the host's launch gap between dispatches
+  is outside the brackets), and the median, p10 and p90 of those per-launch
+  durations are reported.
+* rows also cover: the tiny GEMV (M=1, K=512, N=256) with the oracle's
+  median of 101 runs on the host, small-M GEMV (M = 2..16), the gated FFN
+  front half, the Q4_K GEMV, the Q8_0 vocabulary GEMV (and M = 2, 4), one
+  GPU's shard of the FFN up and vocabulary GEMVs (N / 8 rows), the same
+  vocabulary head over Q4_0, and the prefill GEMM (M = 2048 over Q4_0, Q8_0
+  and Q4_K weights, short prompts M = 16, 64, 128).
+* HBM references (bench_read.hip): an empty launch, a plain coalesced read
+  and the GEMV's pair pattern on the same 9.4 MB copies, a sweep of read
+  kernels over grid shape, loads per lane and cache policy (the tuned read
+  floor is the fastest of them), and 512 MiB reads (achievable streaming).
+* decode replays, each captured in one HIP graph with every GEMV reading its
+  own cold weights and writing its own output, checked bitwise against an
+  eager run of the same sequence:
+  - decode_step_replay: 171 FFN (up, down) pairs at the shapes above plus
+    the Q8_0 vocabulary GEMV (343 dispatches);
+  - decode_layer_replay: 57 Gemma-class layers of six Q4_0 GEMVs (q
+    2048->2048, k and v 2048->512, o 2048->2048, gate and up stacked as one
+    2048->16384 matrix, down 8192->2048) plus the vocabulary GEMV: the
+    pages' 342 Q4_0 + 1 Q8_0 dispatches at mixed shapes;
+  - decode_layer_replay_gated: the same, the gate/up dispatch running the
+    gated front half (qmm_ffn_gate_up_q4_0) instead.
+* clocks: the GPU's current shader and memory clock levels are read before
+  and after the run (sysfs, else rocm-smi) and reported.
 
 The CPU baseline times the f64 oracle (test infrastructure, plain C with
 OpenMP) on full decode steps for a bounded number of seconds.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 
@@ -48,12 +62,14 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
 import hashlib
 import json
 import math
 import os
 import pathlib
 import statistics
+import subprocess
 import sys
 import time
 
@@ -66,6 +82,7 @@ POOL_BYTES = 1 << 30           # rotating weight pool per shape (>= 1 GiB)
 TRAFFIC_FILE = ROOT / "profiles" / "gemv_q4_0_decode_pair_traffic.json"
 DOMINANT_SOURCES = [ROOT / "block_quantized_matmul_q4_amd" / "csrc" / "gemv_m1.hip",
                     ROOT / "block_quantized_matmul_q4_amd" / "csrc" / "qmm_internal.h"]
+SHARDS = 8                     # GPUs a sharded deployment would split N over
 
 
 def log(*a):
@@ -75,18 +92,20 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="replay the warmup work for at least this long before each "
                          "timing (clocks rise over the first ~20-30 ms of sustained load)")
     ap.add_argument("--samples", type=int, default=100,
                     help="back-to-back launches per timed graph replay")
+    ap.add_argument("--dispatches", type=int, default=256,
+                    help="event-bracketed eager launches for per-dispatch percentiles")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bounded wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
-                    help="time only the decode pair (for profiling runs)")
+                    help="time only the decode pair and its references (for profiling runs)")
     return ap.parse_args()
 
 
@@ -95,6 +114,32 @@ def source_hash(paths) -> str:
     for p in paths:
         h.update(pathlib.Path(p).read_bytes())
     return h.hexdigest()
+
+
+def read_clocks():
+    """Current shader (sclk) and memory (mclk) clock levels of every GPU the
+    kernel driver exposes: the starred level of pp_dpm_sclk / pp_dpm_mclk in
+    sysfs, else rocm-smi's report; None where neither can be read."""
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        rec = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                lines = pathlib.Path(dev, name).read_text().splitlines()
+            except OSError:
+                continue
+            cur = [ln.split(":", 1)[1].strip(" *") for ln in lines if ln.rstrip().endswith("*")]
+            rec[name[-4:]] = cur[0] if cur else None
+        if rec:
+            out[pathlib.Path(dev).parent.name] = rec
+    if out:
+        return {"source": "sysfs", "clocks": out}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        return {"source": "rocm-smi", "clocks": json.loads(r.stdout)}
+    except (OSError, ValueError, subprocess.SubprocessError) as e:
+        return {"source": None, "error": str(e)[:200]}
 
 
 class Hip:
@@ -126,6 +171,10 @@ class Hip:
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return ms.value
 
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
 
 def bench_read_library():
     """bench_read.so (reference read kernels), built by __graft_entry__.build()
@@ -140,14 +189,27 @@ def bench_read_library():
         fn = getattr(lib, f)
         fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.bench_read_var.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.bench_read_var.restype = ctypes.c_int
+    lib.bench_read_var_count.argtypes = []
+    lib.bench_read_var_count.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.bench_read_var_shape.argtypes = [ctypes.c_int, ip, ip, ip]
+    lib.bench_read_var_shape.restype = ctypes.c_int
+    lib.bench_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bench_empty.restype = ctypes.c_int
     return lib
+
+
+def pct(s, f):
+    return s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
 
 
 def summarize(us):
     s = sorted(us)
-    q = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
     return {"mean_us": statistics.fmean(s), "median_us": statistics.median(s),
-            "p10_us": q(0.1), "p90_us": q(0.9), "n": len(s)}
+            "p10_us": pct(s, 0.1), "p90_us": pct(s, 0.9), "n": len(s)}
 
 
 def library_gemm_reference(xp, m, n, k, settle_ms, reps=50):
@@ -195,6 +257,7 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "no GPU visible"
+    clocks_before = read_clocks()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = qmm.library()
@@ -205,13 +268,80 @@ def main():
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
 
-    # ---------------------------------------------------------------- inputs
-    def pool(w_host, min_copies=2):
-        r = max(min_copies, math.ceil(POOL_BYTES / w_host.nbytes))
-        base = torch.from_numpy(w_host.reshape(-1)).to(dev)
-        copies = [base] + [base.clone() for _ in range(r - 1)]
-        return copies
+    def ok(st):
+        if st != 0:
+            raise qmm.QmmError(st, qmm.qmm_last_error())
 
+    def pool(w_host, min_copies=2, bytes_target=POOL_BYTES):
+        r = max(min_copies, math.ceil(bytes_target / w_host.nbytes))
+        base = torch.from_numpy(np.ascontiguousarray(w_host).reshape(-1)).to(dev)
+        return [base] + [base.clone() for _ in range(r - 1)]
+
+    def settle(g, min_ms):
+        """Replays graph g (untimed) until min_ms of wall time have passed."""
+        t_end = time.perf_counter() + min_ms * 1e-3
+        g.replay()
+        torch.cuda.synchronize()
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
+
+    def capture(fn_calls):
+        """One HIP graph of the calls fn(stream) in fn_calls, in order."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for fn in fn_calls:
+                ok(fn(cs))
+        return g
+
+    def time_graph(g, launches, replays=5):
+        """Mean duration per launch over `replays` event-bracketed replays of
+        graph g (after settling it)."""
+        settle(g, args.settle_ms)
+        ev = hip.events(2 * replays)
+        for r in range(replays):
+            hip.lib.hipEventRecord(ev[2 * r], sh)
+            g.replay()
+            hip.lib.hipEventRecord(ev[2 * r + 1], sh)
+        torch.cuda.synchronize()
+        per = [1e3 * hip.elapsed_ms(ev[2 * r], ev[2 * r + 1]) / launches for r in range(replays)]
+        hip.destroy(ev)
+        out = summarize(per)
+        out["launches_per_replay"] = launches
+        return out
+
+    def time_launches(fn, arglists, replays=5):
+        """Mean duration per launch of fn(*arglists[i], stream), the launches
+        captured back to back in one HIP graph."""
+        g = capture([(lambda a: (lambda cs: fn(*a, cs)))(a) for a in arglists])
+        out = time_graph(g, len(arglists), replays)
+        del g
+        return out
+
+    def per_dispatch(fn, arglists, count):
+        """Durations of `count` eager launches of fn(*arglists[i % len], stream),
+        each between its own pair of HIP events on the launch stream."""
+        g = capture([(lambda a: (lambda cs: fn(*a, cs)))(a) for a in arglists])
+        settle(g, args.settle_ms)
+        del g
+        ev = hip.events(2 * count)
+        for i in range(count):
+            hip.lib.hipEventRecord(ev[2 * i], sh)
+            ok(fn(*arglists[i % len(arglists)], sh))
+            hip.lib.hipEventRecord(ev[2 * i + 1], sh)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(count))
+        hip.destroy(ev)
+        return {"median_us": statistics.median(us), "p10_us": pct(us, 0.1),
+                "p90_us": pct(us, 0.9), "min_us": us[0], "max_us": us[-1], "n": count,
+                "method": "eager launches, each between its own pair of HIP events"}
+
+    def gemv_args(x, pool_, y, m, n_, k, count):
+        return [(x.data_ptr(), pool_[i % len(pool_)].data_ptr(), y.data_ptr(), m, n_, k)
+                for i in range(count)]
+
+    # ---------------------------------------------------------------- inputs
     up = synth.WORKLOADS["q4_0_gemv_ffn_up"]
     down = synth.WORKLOADS["q4_0_gemv_ffn_down"]
     log("[bench] generating inputs")
@@ -230,77 +360,31 @@ def main():
     log(f"[bench] pools: {len(w_up)} x {w_up_h.nbytes} B (up), {len(w_dn)} x "
         f"{w_dn_h.nbytes} B (down)")
 
-    def ok(st):
-        if st != 0:
-            raise qmm.QmmError(st, qmm.qmm_last_error())
+    def launch_up(i, s):
+        return lib.qmm_gemv_q4_0(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
+                                 y_up.data_ptr(), 1, up["N"], up["K"], s)
 
-    def launch_up(i, s=sh):
-        ok(lib.qmm_gemv_q4_0(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
-                             y_up.data_ptr(), 1, up["N"], up["K"], s))
-
-    def launch_dn(i, s=sh):
-        ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[i % len(w_dn)].data_ptr(),
-                             y_dn.data_ptr(), 1, down["N"], down["K"], s))
-
-    def settle(g, min_ms):
-        """Replays graph g (untimed) until min_ms of wall time have passed."""
-        t_end = time.perf_counter() + min_ms * 1e-3
-        g.replay()
-        torch.cuda.synchronize()
-        while time.perf_counter() < t_end:
-            g.replay()
-            torch.cuda.synchronize()
-
-    def time_launches(fn, arglists, replays=5):
-        """Mean duration per launch of fn(*arglists[i], stream): the launches
-        are captured back to back in one HIP graph, replayed untimed for
-        --settle-ms (code objects, TLB, clocks), then each of `replays`
-        replays is bracketed by HIP events on the stream it runs on."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream().cuda_stream
-            for a in arglists:
-                ok(fn(*a, cs))
-        settle(g, args.settle_ms)
-        ev = hip.events(2 * replays)
-        rec = hip.lib.hipEventRecord
-        for r in range(replays):
-            rec(ev[2 * r], sh)
-            g.replay()
-            rec(ev[2 * r + 1], sh)
-        torch.cuda.synchronize()
-        per = [1e3 * hip.elapsed_ms(ev[2 * r], ev[2 * r + 1]) / len(arglists)
-               for r in range(replays)]
-        for e in ev:
-            hip.lib.hipEventDestroy(e)
-        del g
-        out = summarize(per)
-        out["launches_per_replay"] = len(arglists)
-        return out
-
-    def gemv_args(x, pool_, y, m, n_, k, count):
-        return [(x.data_ptr(), pool_[i % len(pool_)].data_ptr(), y.data_ptr(), m, n_, k)
-                for i in range(count)]
+    def launch_dn(i, s):
+        return lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[i % len(w_dn)].data_ptr(),
+                                 y_dn.data_ptr(), 1, down["N"], down["K"], s)
 
     # ---------------------------------------------------- eager sanity check
-    launch_up(0)
-    launch_dn(0)
+    ok(launch_up(0, sh))
+    ok(launch_dn(0, sh))
     torch.cuda.synchronize()
     ref_up, ref_dn = y_up.clone(), y_dn.clone()
 
     # ------------------------------------------------ graph-replayed steps
-    def capture(nsteps, offset):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream().cuda_stream
-            for s in range(nsteps):
-                launch_up(offset + s, cs)
-                launch_dn(offset + s, cs)
-        return g
+    def step_calls(nsteps, offset):
+        calls = []
+        for s_ in range(nsteps):
+            calls.append((lambda i: (lambda cs: launch_up(i, cs)))(offset + s_))
+            calls.append((lambda i: (lambda cs: launch_dn(i, cs)))(offset + s_))
+        return calls
 
     log(f"[bench] capturing {args.warmup} warmup + {args.steps} timed steps")
-    g_warm = capture(args.warmup, len(w_up) // 2) if args.warmup > 0 else None
-    g_timed = capture(args.steps, 0)
+    g_warm = capture(step_calls(args.warmup, len(w_up) // 2)) if args.warmup > 0 else None
+    g_timed = capture(step_calls(args.steps, 0))
     if g_warm is not None:
         g_warm.replay()                  # the W warmup steps
         settle(g_warm, args.settle_ms)   # and more of them until clocks settle
@@ -314,234 +398,237 @@ def main():
     t1 = time.perf_counter()
     wall_s = t1 - t0
     gpu_ms = hip.elapsed_ms(ev0, ev1)
+    hip.destroy([ev0, ev1])
     ms_per_step = 1e3 * wall_s / args.steps
-    # the last replayed step read pool copy steps-1; same bytes as copy 0
+    # every pool copy holds the same bytes, so the last step equals the eager one
     graph_ok = bool(torch.equal(y_up, ref_up) and torch.equal(y_dn, ref_dn))
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    del g_timed, g_warm
     log(f"[bench] graph: {ms_per_step * 1e3:.2f} us/step wall, "
         f"{gpu_ms * 1e3 / args.steps:.2f} us/step GPU events, bitwise vs eager: {graph_ok}")
 
-    # ------------------------------------------------ per-kernel durations
+    # ------------------------------------------------ per-kernel rows
+    # Each row: (name, fn, arglists, metadata). Timed in forward then in
+    # backward order; all pools stay allocated across both passes.
     n = args.samples
-    t_up = time_launches(lib.qmm_gemv_q4_0, gemv_args(x_up, w_up, y_up, 1, up["N"], up["K"], n))
-    t_dn = time_launches(lib.qmm_gemv_q4_0, gemv_args(x_dn, w_dn, y_dn, 1, down["N"], down["K"], n))
-    log(f"[bench] up   {t_up['mean_us']:.2f} us mean, {t_up['median_us']:.2f} median")
-    log(f"[bench] down {t_dn['mean_us']:.2f} us mean, {t_dn['median_us']:.2f} median")
-    pair_us = t_up["mean_us"] + t_dn["mean_us"]
-    achieved = bytes_step / (pair_us * 1e-6) / 1e9
+    rows_spec = []
 
-    rows = {
-        "q4_0_gemv_ffn_up": dict(t_up, bytes=bytes_up,
-                                 gbs=bytes_up / (t_up["mean_us"] * 1e-6) / 1e9),
-        "q4_0_gemv_ffn_down": dict(t_dn, bytes=bytes_dn,
-                                   gbs=bytes_dn / (t_dn["mean_us"] * 1e-6) / 1e9),
-    }
+    def add_row(name, fn, arglists, **meta):
+        rows_spec.append((name, fn, arglists, meta))
 
-    # ------------------------------------------------ HBM read references
-    # The same timing method over kernels that only read: one FFN weight
-    # copy (9.4 MB) per launch as a plain coalesced read and in the GEMV's
-    # own 36-byte-pair pattern, and 512 MiB per launch for the achievable
-    # streaming rate.
+    add_row("q4_0_gemv_ffn_up", lib.qmm_gemv_q4_0,
+            gemv_args(x_up, w_up, y_up, 1, up["N"], up["K"], n), bytes=bytes_up)
+    add_row("q4_0_gemv_ffn_down", lib.qmm_gemv_q4_0,
+            gemv_args(x_dn, w_dn, y_dn, 1, down["N"], down["K"], n), bytes=bytes_dn)
+
+    # HBM references on the same 9.4 MB copies
     rd = bench_read_library()
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     nb = w_up_h.nbytes
-    t_rp = time_launches(rd.bench_read_plain,
-                         [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)])
-    t_rq = time_launches(rd.bench_read_pairs,
-                         [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)])
+    add_row("hbm_empty_launch", rd.bench_empty,
+            [(256, sink.data_ptr()) for _ in range(n)], bytes=0)
+    add_row("hbm_read_plain_9mb", rd.bench_read_plain,
+            [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)], bytes=nb)
+    add_row("hbm_read_pairs_9mb", rd.bench_read_pairs,
+            [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)], bytes=nb)
+    var_shapes = {}
+    for v in range(rd.bench_read_var_count()):
+        wg_, u_, nt_ = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert rd.bench_read_var_shape(v, ctypes.byref(wg_), ctypes.byref(u_), ctypes.byref(nt_)) == 0
+        var_shapes[v] = {"threads": wg_.value, "loads_per_lane": u_.value,
+                         "nontemporal": bool(nt_.value),
+                         "workgroups": math.ceil(nb / 16 / (wg_.value * u_.value))}
+        add_row(f"hbm_read_sweep_{v}", (lambda vv: (lambda *a: rd.bench_read_var(vv, *a)))(v),
+                [(w_up[i % len(w_up)].data_ptr(), nb, sink.data_ptr()) for i in range(n)],
+                bytes=nb, shape=var_shapes[v])
     big = [torch.randint(0, 256, (1 << 29,), dtype=torch.uint8, device=dev) for _ in range(2)]
-    t_rb = time_launches(rd.bench_read_plain,
-                         [(big[i % 2].data_ptr(), 1 << 29, sink.data_ptr()) for i in range(20)])
-    del big
-    achievable = (1 << 29) / (t_rb["mean_us"] * 1e-6) / 1e9
-    for key, t, b in (("hbm_read_plain_9mb", t_rp, nb), ("hbm_read_pairs_9mb", t_rq, nb),
-                      ("hbm_read_plain_512mib", t_rb, 1 << 29)):
-        rows[key] = dict(t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9)
-    log(f"[bench] plain read 9.4 MB {t_rp['mean_us']:.2f} us, pair-pattern read "
-        f"{t_rq['mean_us']:.2f} us, 512 MiB {achievable:.0f} GB/s")
+    add_row("hbm_read_plain_512mib", rd.bench_read_plain,
+            [(big[i % 2].data_ptr(), 1 << 29, sink.data_ptr()) for i in range(20)],
+            bytes=1 << 29)
 
+    # config 1: the tiny GEMV
+    tiny = synth.WORKLOADS["q4_0_gemv_tiny"]
+    x_t_h, w_t_h = synth.workload_inputs("q4_0_gemv_tiny")
+    w_t = pool(w_t_h, bytes_target=64 << 20)
+    x_t = torch.from_numpy(x_t_h).to(dev)
+    y_t = torch.empty((1, tiny["N"]), device=dev)
+    bytes_tiny = w_t_h.nbytes + x_t_h.nbytes + y_t.numel() * 4
+    add_row("q4_0_gemv_tiny", lib.qmm_gemv_q4_0,
+            gemv_args(x_t, w_t, y_t, 1, tiny["N"], tiny["K"], n), bytes=bytes_tiny)
+
+    keep = []     # tensors the rows' arguments point into
+    gemm_ref = None
+    voc = synth.WORKLOADS["q8_0_gemv_vocab"]
     if not args.decode_only:
         # small-M GEMV on the up shape (same weight pool)
         for m in (2, 4, 8, 16):
             xm = torch.from_numpy(synth.activations(m, up["K"])).to(dev)
             ym = torch.empty((m, up["N"]), device=dev)
-
-            t = time_launches(lib.qmm_gemv_q4_0, gemv_args(xm, w_up, ym, m, up["N"], up["K"], n))
-            b = w_up_h.nbytes + xm.numel() * 4 + ym.numel() * 4
-            fl = 2 * m * up["N"] * up["K"]
-            rows[f"q4_0_gemv_small_m{m}"] = dict(
-                t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
-                tflops=fl / (t["mean_us"] * 1e-6) / 1e12,
-                tokens_per_s=m / (t["mean_us"] * 1e-6))
-            log(f"[bench] small M={m}: {t['mean_us']:.2f} us")
+            keep += [xm, ym]
+            add_row(f"q4_0_gemv_small_m{m}", lib.qmm_gemv_q4_0,
+                    gemv_args(xm, w_up, ym, m, up["N"], up["K"], n),
+                    bytes=w_up_h.nbytes + xm.numel() * 4 + ym.numel() * 4,
+                    flops=2 * m * up["N"] * up["K"], tokens=m)
         # gated FFN front half (gate + up in one launch), M = 1, the up shape;
         # gate and up read two different cold pool copies per launch
         hf = torch.empty((1, up["N"]), device=dev)
-        ffn_args = [(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
-                     w_up[(i + 1) % len(w_up)].data_ptr(), hf.data_ptr(), 1, up["N"], up["K"])
-                    for i in range(0, 2 * n, 2)]
-        tf = time_launches(lib.qmm_ffn_gate_up_q4_0, ffn_args)
-        bf = 2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4
-        rows["q4_0_ffn_gate_up"] = dict(tf, bytes=bf, gbs=bf / (tf["mean_us"] * 1e-6) / 1e9,
-                                        vs_two_gemv_us=2 * t_up["mean_us"])
-        log(f"[bench] ffn gate+up: {tf['mean_us']:.2f} us (two GEMVs: "
-            f"{2 * t_up['mean_us']:.2f} us)")
+        keep.append(hf)
+        add_row("q4_0_ffn_gate_up", lib.qmm_ffn_gate_up_q4_0,
+                [(x_up.data_ptr(), w_up[i % len(w_up)].data_ptr(),
+                  w_up[(i + 1) % len(w_up)].data_ptr(), hf.data_ptr(), 1, up["N"], up["K"])
+                 for i in range(0, 2 * n, 2)],
+                bytes=2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4)
         # Q4_K (the k-quant format of the pages' CLIP/CLAP path) at the FFN
-        # pair's shapes, cold pools
+        # pair's shapes, cold pools; two and four rows over the up matrix
         for name in ("q4_k_gemv_ffn_up", "q4_k_gemv_ffn_down"):
             wlk = synth.WORKLOADS[name]
             xk_h, wk_h = synth.workload_inputs(name)
             wk = pool(wk_h)
             xk = torch.from_numpy(xk_h).to(dev)
             yk = torch.empty((1, wlk["N"]), device=dev)
-            tk = time_launches(lib.qmm_gemv_q4_k,
-                               gemv_args(xk, wk, yk, 1, wlk["N"], wlk["K"], n))
-            bk = wk_h.nbytes + xk_h.nbytes + yk.numel() * 4
-            rows[name] = dict(tk, bytes=bk, gbs=bk / (tk["mean_us"] * 1e-6) / 1e9)
-            log(f"[bench] {name}: {tk['mean_us']:.2f} us")
-            # two and four activation rows over the up matrix (batched or
-            # speculative decode)
+            keep += wk + [xk, yk]
+            add_row(name, lib.qmm_gemv_q4_k, gemv_args(xk, wk, yk, 1, wlk["N"], wlk["K"], n),
+                    bytes=wk_h.nbytes + xk_h.nbytes + yk.numel() * 4)
             for m in ((2, 4) if name == "q4_k_gemv_ffn_up" else ()):
                 xm = torch.from_numpy(synth.activations(m, wlk["K"])).to(dev)
                 ym = torch.empty((m, wlk["N"]), device=dev)
-                t = time_launches(lib.qmm_gemv_q4_k,
-                                  gemv_args(xm, wk, ym, m, wlk["N"], wlk["K"], n))
-                b = wk_h.nbytes + xm.numel() * 4 + ym.numel() * 4
-                fl = 2 * m * wlk["N"] * wlk["K"]
-                rows[f"q4_k_gemv_small_m{m}"] = dict(
-                    t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
-                    tflops=fl / (t["mean_us"] * 1e-6) / 1e12,
-                    tokens_per_s=m / (t["mean_us"] * 1e-6))
-                log(f"[bench] q4_k small M={m}: {t['mean_us']:.2f} us")
-            del wk
-        # Q8_0 vocabulary GEMV
-        voc = synth.WORKLOADS["q8_0_gemv_vocab"]
+                keep += [xm, ym]
+                add_row(f"q4_k_gemv_small_m{m}", lib.qmm_gemv_q4_k,
+                        gemv_args(xm, wk, ym, m, wlk["N"], wlk["K"], n),
+                        bytes=wk_h.nbytes + xm.numel() * 4 + ym.numel() * 4,
+                        flops=2 * m * wlk["N"] * wlk["K"], tokens=m)
+        # Q8_0 vocabulary GEMV, and over k + 1 tokens (multi-token prediction
+        # verification, k = 1 and 3): one pass over the 570 MB for all rows
         xv_h, wv_h = synth.workload_inputs("q8_0_gemv_vocab")
         wv = pool(wv_h)
         xv = torch.from_numpy(xv_h).to(dev)
         yv = torch.empty((1, voc["N"]), device=dev)
-
-        tv = time_launches(lib.qmm_gemv_q8_0,
-                           gemv_args(xv, wv, yv, 1, voc["N"], voc["K"], max(20, n // 4)))
+        keep += wv + [xv, yv]
         bv = wv_h.nbytes + xv_h.nbytes + yv.numel() * 4
-        rows["q8_0_gemv_vocab"] = dict(tv, bytes=bv, gbs=bv / (tv["mean_us"] * 1e-6) / 1e9)
-        log(f"[bench] q8 vocab: {tv['mean_us']:.2f} us")
-        # the vocabulary head over k + 1 tokens (multi-token prediction
-        # verification, k = 1 and 3): one pass over the 570 MB for all rows
+        nv = max(20, n // 4)
+        add_row("q8_0_gemv_vocab", lib.qmm_gemv_q8_0,
+                gemv_args(xv, wv, yv, 1, voc["N"], voc["K"], nv), bytes=bv)
         for m in (2, 4):
             xm = torch.from_numpy(synth.activations(m, voc["K"])).to(dev)
             ym = torch.empty((m, voc["N"]), device=dev)
-            t = time_launches(lib.qmm_gemv_q8_0,
-                              gemv_args(xm, wv, ym, m, voc["N"], voc["K"], max(20, n // 4)))
-            b = wv_h.nbytes + xm.numel() * 4 + ym.numel() * 4
-            rows[f"q8_0_gemv_vocab_m{m}"] = dict(
-                t, bytes=b, gbs=b / (t["mean_us"] * 1e-6) / 1e9,
-                tokens_per_s=m / (t["mean_us"] * 1e-6))
-            log(f"[bench] q8 vocab M={m}: {t['mean_us']:.2f} us")
-            del xm, ym
-        # measured decode step: the 342 Q4_0 GEMVs as 171 FFN (up, down)
-        # pairs, then the Q8_0 vocabulary GEMV, back to back in one HIP graph;
-        # every GEMV reads its own pool copy (3.8 GB per step: cold HBM)
-        def decode_step(cs):
-            for layer in range(171):
-                ok(lib.qmm_gemv_q4_0(x_up.data_ptr(), w_up[layer % len(w_up)].data_ptr(),
-                                     y_up.data_ptr(), 1, up["N"], up["K"], cs))
-                ok(lib.qmm_gemv_q4_0(x_dn.data_ptr(), w_dn[layer % len(w_dn)].data_ptr(),
-                                     y_dn.data_ptr(), 1, down["N"], down["K"], cs))
-            ok(lib.qmm_gemv_q8_0(xv.data_ptr(), wv[0].data_ptr(), yv.data_ptr(), 1,
-                                 voc["N"], voc["K"], cs))
-
-        g_dec = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_dec):
-            decode_step(torch.cuda.current_stream().cuda_stream)
-        settle(g_dec, args.settle_ms)
-        reps = 5
-        ev = hip.events(2 * reps)
-        for r in range(reps):
-            hip.lib.hipEventRecord(ev[2 * r], sh)
-            g_dec.replay()
-            hip.lib.hipEventRecord(ev[2 * r + 1], sh)
-        torch.cuda.synchronize()
-        per = [1e3 * hip.elapsed_ms(ev[2 * r], ev[2 * r + 1]) for r in range(reps)]
-        for e in ev:
-            hip.lib.hipEventDestroy(e)
-        del g_dec
-        td = summarize(per)
-        b_dec = 171 * bytes_step + bv
-        rows["decode_step_replay"] = dict(
-            td, dispatches=343, bytes=b_dec, gbs=b_dec / (td["mean_us"] * 1e-6) / 1e9,
-            tokens_per_s=1e6 / td["mean_us"])
-        log(f"[bench] decode step replay (343 GEMVs): {td['mean_us']:.1f} us, "
-            f"{1e6 / td['mean_us']:.0f} tok/s")
-        del wv
-        # the same vocabulary head over Q4_0 weights (302 MB): the Q4_0 GEMV at
-        # a size that amortizes launch costs
+            keep += [xm, ym]
+            add_row(f"q8_0_gemv_vocab_m{m}", lib.qmm_gemv_q8_0,
+                    gemv_args(xm, wv, ym, m, voc["N"], voc["K"], nv),
+                    bytes=wv_h.nbytes + xm.numel() * 4 + ym.numel() * 4, tokens=m)
+        # one GPU's shard of an 8-way split along N (the rows a GPU would hold)
+        n_up_shard = up["N"] // SHARDS
+        ws = pool(w_up_h[:n_up_shard])
+        ys = torch.empty((1, n_up_shard), device=dev)
+        keep += ws + [ys]
+        add_row("q4_0_gemv_ffn_up_shard", lib.qmm_gemv_q4_0,
+                gemv_args(x_up, ws, ys, 1, n_up_shard, up["K"], n),
+                bytes=ws[0].numel() + x_up_h.nbytes + ys.numel() * 4, shard=f"1/{SHARDS} of N")
+        n_voc_shard = voc["N"] // SHARDS
+        wvs = pool(wv_h[:n_voc_shard])
+        yvs = torch.empty((1, n_voc_shard), device=dev)
+        keep += wvs + [yvs]
+        add_row("q8_0_gemv_vocab_shard", lib.qmm_gemv_q8_0,
+                gemv_args(xv, wvs, yvs, 1, n_voc_shard, voc["K"], n),
+                bytes=wvs[0].numel() + xv_h.nbytes + yvs.numel() * 4, shard=f"1/{SHARDS} of N")
+        # the vocabulary head over Q4_0 weights (302 MB): the Q4_0 GEMV at a
+        # size that amortizes launch costs
         w4v_h = synth.q4_0_weights(voc["N"], voc["K"])
         w4v = pool(w4v_h)
-        t4 = time_launches(lib.qmm_gemv_q4_0,
-                           gemv_args(xv, w4v, yv, 1, voc["N"], voc["K"], max(20, n // 4)))
-        b4 = w4v_h.nbytes + xv_h.nbytes + yv.numel() * 4
-        g4 = b4 / (t4["mean_us"] * 1e-6) / 1e9
-        rows["q4_0_gemv_vocab"] = dict(t4, bytes=b4, gbs=g4, frac_hbm_peak=g4 / HBM_PEAK_GBS)
-        log(f"[bench] q4 vocab: {t4['mean_us']:.2f} us, {b4 / t4['mean_us'] / 1e3:.0f} GB/s")
-        del w4v, w4v_h
-        # Q4_0 prefill GEMM
+        keep += w4v
+        add_row("q4_0_gemv_vocab", lib.qmm_gemv_q4_0,
+                gemv_args(xv, w4v, yv, 1, voc["N"], voc["K"], nv),
+                bytes=w4v_h.nbytes + xv_h.nbytes + yv.numel() * 4)
+        # prefill GEMM: M = 2048 over Q4_0, Q8_0 and Q4_K; short prompts
         pre = synth.WORKLOADS["q4_0_gemm_prefill"]
         xp = torch.from_numpy(synth.activations(pre["M"], pre["K"])).to(dev)
         yp = torch.empty((pre["M"], pre["N"]), device=dev)
-
-        tp = time_launches(lib.qmm_gemm_q4_0,
-                           gemv_args(xp, w_up, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
+        keep += [xp, yp]
         fp = 2 * pre["M"] * pre["N"] * pre["K"]
-        tfl = fp / (tp["mean_us"] * 1e-6) / 1e12
-        rows["q4_0_gemm_prefill"] = dict(tp, flops=fp, tflops=tfl,
-                                         frac_bf16_peak=tfl / BF16_PEAK_TFLOPS,
-                                         prefill_tokens_per_s=pre["M"] / (tp["mean_us"] * 1e-6))
-        log(f"[bench] prefill GEMM: {tp['mean_us']:.2f} us, {tfl:.1f} TFLOP/s")
-        # short prompts over the same weights (the medium-M kernel), cold pool
+        ng = max(20, n // 4)
+        add_row("q4_0_gemm_prefill", lib.qmm_gemm_q4_0,
+                gemv_args(xp, w_up, yp, pre["M"], pre["N"], pre["K"], ng),
+                flops=fp, tokens=pre["M"])
         for ms in (16, 64, 128):
             xs = torch.from_numpy(synth.activations(ms, pre["K"])).to(dev)
-            ys = torch.empty((ms, pre["N"]), device=dev)
-            ts = time_launches(lib.qmm_gemm_q4_0,
-                               gemv_args(xs, w_up, ys, ms, pre["N"], pre["K"], max(20, n // 2)))
-            fs = 2 * ms * pre["N"] * pre["K"]
-            rows[f"q4_0_gemm_m{ms}"] = dict(ts, flops=fs,
-                                            tflops=fs / (ts["mean_us"] * 1e-6) / 1e12,
-                                            prefill_tokens_per_s=ms / (ts["mean_us"] * 1e-6))
-            log(f"[bench] prefill GEMM M={ms}: {ts['mean_us']:.2f} us")
-        del xs, ys
-        # the same prefill shape over Q8_0 weights
-        w8_h = synth.q8_0_weights(pre["N"], pre["K"])
-        w8 = pool(w8_h)
-        t8 = time_launches(lib.qmm_gemm_q8_0,
-                           gemv_args(xp, w8, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
-        tfl8 = fp / (t8["mean_us"] * 1e-6) / 1e12
-        rows["q8_0_gemm_prefill"] = dict(t8, flops=fp, tflops=tfl8,
-                                         frac_bf16_peak=tfl8 / BF16_PEAK_TFLOPS)
-        log(f"[bench] prefill GEMM Q8_0: {t8['mean_us']:.2f} us, {tfl8:.1f} TFLOP/s")
-        del w8
-        # and over Q4_K super-blocks (the pages' CLIP/CLAP format)
-        wq_h = synth.q4_k_weights(pre["N"], pre["K"])
-        wq = pool(wq_h)
-        tq = time_launches(lib.qmm_gemm_q4_k,
-                           gemv_args(xp, wq, yp, pre["M"], pre["N"], pre["K"], max(20, n // 4)))
-        tflq = fp / (tq["mean_us"] * 1e-6) / 1e12
-        rows["q4_k_gemm_prefill"] = dict(tq, flops=fp, tflops=tflq,
-                                         frac_bf16_peak=tflq / BF16_PEAK_TFLOPS)
-        log(f"[bench] prefill GEMM Q4_K: {tq['mean_us']:.2f} us, {tflq:.1f} TFLOP/s")
-        del wq
-        # context: the vendor library's plain bf16 GEMM at the same shape with
-        # the same f32 output, on weights already held as bf16
+            ys_ = torch.empty((ms, pre["N"]), device=dev)
+            keep += [xs, ys_]
+            add_row(f"q4_0_gemm_m{ms}", lib.qmm_gemm_q4_0,
+                    gemv_args(xs, w_up, ys_, ms, pre["N"], pre["K"], max(20, n // 2)),
+                    flops=2 * ms * pre["N"] * pre["K"], tokens=ms)
+        w8 = pool(synth.q8_0_weights(pre["N"], pre["K"]))
+        wq = pool(synth.q4_k_weights(pre["N"], pre["K"]))
+        keep += w8 + wq
+        add_row("q8_0_gemm_prefill", lib.qmm_gemm_q8_0,
+                gemv_args(xp, w8, yp, pre["M"], pre["N"], pre["K"], ng), flops=fp,
+                tokens=pre["M"])
+        add_row("q4_k_gemm_prefill", lib.qmm_gemm_q4_k,
+                gemv_args(xp, wq, yp, pre["M"], pre["N"], pre["K"], ng), flops=fp,
+                tokens=pre["M"])
+
+    def finish_row(name, meta, passes):
+        fwd, bwd = passes
+        mean = 0.5 * (fwd["mean_us"] + bwd["mean_us"])
+        r = {"mean_us": mean, "forward": fwd, "backward": bwd}
+        if meta.get("bytes"):
+            r["bytes"] = meta["bytes"]
+            r["gbs"] = meta["bytes"] / (mean * 1e-6) / 1e9
+        if meta.get("flops"):
+            r["flops"] = meta["flops"]
+            r["tflops"] = meta["flops"] / (mean * 1e-6) / 1e12
+        if meta.get("tokens"):
+            r["tokens_per_s"] = meta["tokens"] / (mean * 1e-6)
+        for k in ("shape", "shard"):
+            if k in meta:
+                r[k] = meta[k]
+        return r
+
+    results = {name: [] for name, _, _, _ in rows_spec}
+    order = list(range(len(rows_spec)))
+    for pass_no, idx in enumerate((order, order[::-1])):
+        log(f"[bench] rows, {'forward' if pass_no == 0 else 'backward'} order")
+        for i in idx:
+            name, fn, arglists, meta = rows_spec[i]
+            t = time_launches(fn, arglists)
+            results[name].append(t)
+            log(f"[bench]   {name}: {t['mean_us']:.2f} us")
+    rows = {name: finish_row(name, meta, results[name]) for name, _, _, meta in rows_spec}
+    del big
+
+    # per-dispatch percentiles of the headline GEMVs and the tiny GEMV
+    for name in ("q4_0_gemv_ffn_up", "q4_0_gemv_ffn_down", "q4_0_gemv_tiny"):
+        _, fn, arglists, _ = next(r for r in rows_spec if r[0] == name)
+        rows[name]["per_dispatch"] = per_dispatch(fn, arglists, args.dispatches)
+        log(f"[bench] {name} per dispatch: median {rows[name]['per_dispatch']['median_us']:.2f} us")
+
+    t_up, t_dn = rows["q4_0_gemv_ffn_up"]["mean_us"], rows["q4_0_gemv_ffn_down"]["mean_us"]
+    pair_us = t_up + t_dn
+    achieved = bytes_step / (pair_us * 1e-6) / 1e9
+    sweep = {k: v for k, v in rows.items() if k.startswith("hbm_read_sweep_")}
+    best_sweep = min(sweep, key=lambda k: sweep[k]["mean_us"])
+    floor_candidates = dict(sweep, hbm_read_plain_9mb=rows["hbm_read_plain_9mb"])
+    floor_name = min(floor_candidates, key=lambda k: floor_candidates[k]["mean_us"])
+    read_floor_us = floor_candidates[floor_name]["mean_us"]
+    achievable = rows["hbm_read_plain_512mib"]["gbs"]
+
+    # ------------------------------------------------ decode replays
+    if not args.decode_only:
+        rows["decode_step_replay"] = decode_step_replay(
+            torch, hip, sh, ok, capture, time_graph, lib, x_up, x_dn, w_up, w_dn, up, down,
+            xv, wv, voc, bytes_step, bv)
+        for gated in (False, True):
+            key = "decode_layer_replay_gated" if gated else "decode_layer_replay"
+            rows[key] = decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph,
+                                            lib, pool, xv, wv, voc, bv, gated)
+        t_step = 171 * pair_us + rows["q8_0_gemv_vocab"]["mean_us"]
+        rows["decode_tok_s_equiv"] = 1e6 / t_step
         gemm_ref = library_gemm_reference(xp, pre["M"], pre["N"], pre["K"], args.settle_ms)
         if gemm_ref is not None:
-            gemm_ref["q4_0_fused_over_library"] = gemm_ref["mean_us"] / tp["mean_us"]
-            log(f"[bench] library bf16 GEMM (f32 out): {gemm_ref['mean_us']:.2f} us")
-        # decode step model: 342 Q4_0 GEMVs (171 FFN pairs) + 1 Q8_0 GEMV
-        t_step = 171 * (t_up["mean_us"] + t_dn["mean_us"]) + tv["mean_us"]
-        rows["decode_tok_s_equiv"] = 1e6 / t_step
-
-    else:
-        gemm_ref = None
+            gemm_ref["q4_0_fused_over_library"] = (gemm_ref["mean_us"] /
+                                                   rows["q4_0_gemm_prefill"]["mean_us"])
+        for r in (rows["q4_0_gemm_prefill"], rows["q8_0_gemm_prefill"],
+                  rows["q4_k_gemm_prefill"]):
+            r["frac_bf16_peak"] = r["tflops"] / BF16_PEAK_TFLOPS
+        rows["q4_0_gemv_vocab"]["frac_hbm_peak"] = rows["q4_0_gemv_vocab"]["gbs"] / HBM_PEAK_GBS
 
     # ------------------------------------------------ counters, if current
     traffic = None
@@ -555,6 +642,15 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.load()
+        # config 1: median of 101 oracle runs
+        ts = []
+        o.matmul("q4_0", x_t_h, w_t_h, tiny["N"], tiny["K"])
+        for _ in range(101):
+            c0 = time.perf_counter()
+            o.matmul("q4_0", x_t_h, w_t_h, tiny["N"], tiny["K"])
+            ts.append(time.perf_counter() - c0)
+        rows["q4_0_gemv_tiny"]["oracle_median_us_101"] = 1e6 * statistics.median(ts)
+        rows["q4_0_gemv_tiny"]["oracle_threads"] = o.threads()
         reps, t_cpu = 0, 0.0
         log(f"[bench] CPU oracle baseline for ~{args.cpu_seconds:.0f} s")
         while t_cpu < args.cpu_seconds:
@@ -599,16 +695,126 @@ def main():
         "hbm_reference": {
             "achievable_read_gbs": achievable,
             "roofline_achieved_frac_of_achievable": achieved / achievable,
-            "plain_read_us_per_ffn_weight_copy": t_rp["mean_us"],
-            "gemv_pattern_read_us_per_ffn_weight_copy": t_rq["mean_us"],
-            "note": "read-only kernels timed like the GEMVs: a 9.4 MB read per launch "
-                    "costs this much before any arithmetic",
+            "empty_launch_us": rows["hbm_empty_launch"]["mean_us"],
+            "plain_read_us_per_ffn_weight_copy": rows["hbm_read_plain_9mb"]["mean_us"],
+            "gemv_pattern_read_us_per_ffn_weight_copy": rows["hbm_read_pairs_9mb"]["mean_us"],
+            "tuned_read_floor_us": read_floor_us,
+            "tuned_read_floor_kernel": floor_name,
+            "tuned_read_floor_shape": floor_candidates[floor_name].get("shape"),
+            "best_swept_read": best_sweep,
+            "gemv_over_read_floor": {"up": t_up / read_floor_us, "down": t_dn / read_floor_us},
+            "note": "read-only kernels timed like the GEMVs on the same 9.4 MB copies; the "
+                    "tuned floor is the fastest of the plain read and the swept family",
         },
+        "clocks": {"before": clocks_before, "after": read_clocks()},
         "gemm_reference": gemm_ref,
         "rows": rows,
         "device": props.name,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_step_replay(torch, hip, sh, ok, capture, time_graph, lib, x_up, x_dn, w_up, w_dn,
+                       up, down, xv, wv, voc, bytes_step, bv):
+    """171 FFN (up, down) pairs then the Q8_0 vocabulary GEMV in one HIP
+    graph, each GEMV on its own cold pool copy and writing its own output;
+    the replayed outputs are compared bitwise with an eager run."""
+    dev = x_up.device
+    ys_up = torch.empty((171, up["N"]), device=dev)
+    ys_dn = torch.empty((171, down["N"]), device=dev)
+    yv = torch.empty((1, voc["N"]), device=dev)
+    calls = []
+    for layer in range(171):
+        calls.append((lambda l: (lambda cs: lib.qmm_gemv_q4_0(
+            x_up.data_ptr(), w_up[l % len(w_up)].data_ptr(), ys_up[l].data_ptr(), 1, up["N"],
+            up["K"], cs)))(layer))
+        calls.append((lambda l: (lambda cs: lib.qmm_gemv_q4_0(
+            x_dn.data_ptr(), w_dn[l % len(w_dn)].data_ptr(), ys_dn[l].data_ptr(), 1, down["N"],
+            down["K"], cs)))(layer))
+    calls.append(lambda cs: lib.qmm_gemv_q8_0(xv.data_ptr(), wv[0].data_ptr(), yv.data_ptr(), 1,
+                                              voc["N"], voc["K"], cs))
+    for c in calls:
+        ok(c(sh))
+    torch.cuda.synchronize()
+    eager = [ys_up.clone(), ys_dn.clone(), yv.clone()]
+    for t in (ys_up, ys_dn, yv):
+        t.fill_(float("nan"))
+    g = capture(calls)
+    td = time_graph(g, 1)
+    bitwise = bool(torch.equal(ys_up, eager[0]) and torch.equal(ys_dn, eager[1]) and
+                   torch.equal(yv, eager[2]))
+    del g
+    b_dec = 171 * bytes_step + bv
+    log(f"[bench] decode step replay (343 GEMVs): {td['mean_us']:.1f} us, "
+        f"{1e6 / td['mean_us']:.0f} tok/s, bitwise vs eager: {bitwise}")
+    return dict(td, dispatches=len(calls), bytes=b_dec, gbs=b_dec / (td["mean_us"] * 1e-6) / 1e9,
+                tokens_per_s=1e6 / td["mean_us"], bitwise_vs_eager=bitwise)
+
+
+# A Gemma-class decoder layer as six Q4_0 GEMVs (K, N): q, k, v, o, the gate
+# and up matrices stacked as one (2 x 8192 rows), down. 57 such layers give
+# the pages' 342 Q4_0 dispatches per decode step.
+LAYER_SHAPES = (("q", 2048, 2048), ("k", 2048, 512), ("v", 2048, 512), ("o", 2048, 2048),
+                ("gate_up", 2048, 16384), ("down", 8192, 2048))
+LAYERS = 57
+
+
+def decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph, lib, pool, xv, wv, voc,
+                        bv, gated):
+    """LAYERS decoder layers (LAYER_SHAPES, each layer with its own weights)
+    then the Q8_0 vocabulary GEMV, in one HIP graph; with `gated` the
+    gate/up dispatch is the gated front half (h = gelu_tanh(gate) * up,
+    8192 outputs) instead of one 16384-row GEMV. Outputs are compared
+    bitwise with an eager run of the same sequence."""
+    xs = {k: torch.from_numpy(synth.activations(1, k, seed=k + 7)).to(dev) for k in (2048, 8192)}
+    weights, outs, calls = {}, [], []
+    byts = 0
+    for name, k, n_ in LAYER_SHAPES:
+        wh = synth.q4_0_weights(n_, k, seed=n_ + 3)
+        weights[name] = pool(wh, min_copies=LAYERS, bytes_target=0)
+    row_bytes = {name: k // 32 * 18 for name, k, _ in LAYER_SHAPES}
+    for layer in range(LAYERS):
+        for name, k, n_ in LAYER_SHAPES:
+            w_ = weights[name][layer]
+            if name == "gate_up" and gated:
+                h = torch.empty((1, n_ // 2), device=dev)
+                outs.append(h)
+                w_up_ptr = w_.data_ptr() + (n_ // 2) * row_bytes[name]
+                calls.append((lambda w0, wu, h_, kk, nn: (lambda cs: lib.qmm_ffn_gate_up_q4_0(
+                    xs[kk].data_ptr(), w0, wu, h_.data_ptr(), 1, nn, kk, cs)))(
+                        w_.data_ptr(), w_up_ptr, h, k, n_ // 2))
+                byts += w_.numel() + 4 * k + 4 * (n_ // 2)
+            else:
+                y_ = torch.empty((1, n_), device=dev)
+                outs.append(y_)
+                calls.append((lambda w0, y0, kk, nn: (lambda cs: lib.qmm_gemv_q4_0(
+                    xs[kk].data_ptr(), w0, y0.data_ptr(), 1, nn, kk, cs)))(
+                        w_.data_ptr(), y_, k, n_))
+                byts += w_.numel() + 4 * k + 4 * n_
+    yv = torch.empty((1, voc["N"]), device=dev)
+    outs.append(yv)
+    calls.append(lambda cs: lib.qmm_gemv_q8_0(xv.data_ptr(), wv[1 % len(wv)].data_ptr(),
+                                              yv.data_ptr(), 1, voc["N"], voc["K"], cs))
+    byts += bv
+    sh = torch.cuda.current_stream().cuda_stream
+    for c in calls:
+        ok(c(sh))
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    for t in outs:
+        t.fill_(float("nan"))
+    g = capture(calls)
+    td = time_graph(g, 1)
+    bitwise = all(torch.equal(a, b) for a, b in zip(outs, eager))
+    del g
+    name = "decode layer replay (gated front half)" if gated else "decode layer replay"
+    log(f"[bench] {name}, {len(calls)} GEMVs: {td['mean_us']:.1f} us, "
+        f"{1e6 / td['mean_us']:.0f} tok/s, bitwise vs eager: {bitwise}")
+    del weights
+    return dict(td, dispatches=len(calls), layers=LAYERS,
+                layer_shapes=[list(s) for s in LAYER_SHAPES], gated_front_half=gated,
+                bytes=byts, gbs=byts / (td["mean_us"] * 1e-6) / 1e9,
+                tokens_per_s=1e6 / td["mean_us"], bitwise_vs_eager=bitwise)
 
 
 if __name__ == "__main__":

@@ -1,10 +1,16 @@
 // Reference read kernels for bench.py (not part of the library): how fast
 // this GPU streams a buffer from HBM when nothing else is done with the
-// bytes. read_plain gives the achievable read rate (coalesced 16-byte
-// non-temporal loads, one per thread); read_pairs reads the same bytes in
-// the decode GEMV's own pattern (thread t takes the 36-byte pair t as
-// 16 + 16 + 4 bytes through the caches). bench.py reports the GEMV's launch
-// times next to these floors, measured the same way on the same buffers.
+// bytes, and what an empty launch costs. bench.py times them exactly like
+// the GEMVs (back-to-back launches in one HIP graph, cycling through cold
+// copies) and reports the GEMVs' launch times next to these floors.
+//  * read_plain: one coalesced non-temporal 16-byte load per thread;
+//  * read_pairs: the decode GEMV's own pattern (thread t takes the 36-byte
+//    pair t as 16 + 16 + 4 bytes through the caches);
+//  * read_var: the swept family -- WG threads per workgroup, U 16-byte loads
+//    per lane all issued before any is used, cached or non-temporal;
+//    workgroup g reads U * WG * 16 contiguous bytes, so U = 9 with 256
+//    threads gives one workgroup per compute unit for a 9.4 MB buffer;
+//  * empty: workgroups that do nothing (the fixed cost of a launch).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,9 +43,52 @@ __global__ __launch_bounds__(256) void read_pairs(const uint8_t *__restrict__ p,
     if (s == 0x9E3779B9u && c == 0x7F4A7C15u) sink[0] = s;
 }
 
-int launch_check(int64_t grid)
+template <int WG, int U, bool NT>
+__global__ __launch_bounds__(WG) void read_var(const u32x4 *__restrict__ p, int64_t chunks,
+                                               uint32_t *__restrict__ sink)
 {
-    return grid <= INT32_MAX ? 0 : 1;
+    u32x4 v[U];
+    const int64_t base = (int64_t)blockIdx.x * U * WG + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = min(base + (int64_t)u * WG, chunks - 1);
+        if constexpr (NT) v[u] = __builtin_nontemporal_load(p + i);
+        else v[u] = p[i];
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (s == 0x9E3779B9u && v[0].x == 0x7F4A7C15u) sink[0] = s;
+}
+
+__global__ __launch_bounds__(256) void empty(uint32_t *__restrict__ sink, int flag)
+{
+    if (flag == 0x12345 && threadIdx.x == 0) sink[0] = 1;
+}
+
+bool grid_ok(int64_t grid)
+{
+    return grid <= INT32_MAX;
+}
+
+// (threads per workgroup, loads per lane, non-temporal) of read_var
+struct Var {
+    int wg, u;
+    bool nt;
+};
+constexpr Var kVars[] = {
+    {256, 1, true},  {256, 2, true},  {256, 4, true},  {256, 8, true},  {256, 9, true},
+    {256, 1, false}, {256, 2, false}, {256, 4, false}, {256, 9, false}, {512, 4, true},
+    {512, 9, true},  {1024, 4, true}, {1024, 9, true}, {64, 9, false},  {128, 18, false},
+};
+constexpr int kNumVars = sizeof(kVars) / sizeof(kVars[0]);
+
+template <int WG, int U, bool NT>
+void launch_var(const void *buf, int64_t chunks, void *sink, hipStream_t s)
+{
+    const int64_t grid = (chunks + (int64_t)WG * U - 1) / ((int64_t)WG * U);
+    hipLaunchKernelGGL((read_var<WG, U, NT>), dim3((unsigned)grid), dim3(WG), 0, s,
+                       static_cast<const u32x4 *>(buf), chunks, static_cast<uint32_t *>(sink));
 }
 
 }  // namespace
@@ -52,7 +101,7 @@ extern "C" __attribute__((visibility("default"))) int bench_read_plain(const voi
     if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0) return 1;
     const int64_t chunks = bytes / 16;
     const int64_t grid = (chunks + 255) / 256;
-    if (launch_check(grid)) return 1;
+    if (!grid_ok(grid)) return 1;
     hipLaunchKernelGGL(read_plain, dim3((unsigned)grid), dim3(256), 0, s,
                        static_cast<const u32x4 *>(buf), chunks, static_cast<uint32_t *>(sink));
     return hipGetLastError() == hipSuccess ? 0 : 2;
@@ -65,8 +114,59 @@ extern "C" __attribute__((visibility("default"))) int bench_read_pairs(const voi
     if (!buf || !sink || bytes < 36 || bytes % 36 != 0 || (uintptr_t)buf % 4 != 0) return 1;
     const int64_t pairs = bytes / 36;
     const int64_t grid = (pairs + 255) / 256;
-    if (launch_check(grid)) return 1;
+    if (!grid_ok(grid)) return 1;
     hipLaunchKernelGGL(read_pairs, dim3((unsigned)grid), dim3(256), 0, s,
                        static_cast<const uint8_t *>(buf), pairs, static_cast<uint32_t *>(sink));
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Number of read_var variants and the shape of variant v (threads per
+// workgroup, loads per lane, non-temporal flag); returns 1 for a bad v.
+extern "C" __attribute__((visibility("default"))) int bench_read_var_count(void) { return kNumVars; }
+
+extern "C" __attribute__((visibility("default"))) int bench_read_var_shape(int v, int *wg, int *u, int *nt)
+{
+    if (v < 0 || v >= kNumVars || !wg || !u || !nt) return 1;
+    *wg = kVars[v].wg;
+    *u = kVars[v].u;
+    *nt = kVars[v].nt ? 1 : 0;
+    return 0;
+}
+
+// Reads bytes (a positive multiple of 16, 16-byte aligned buf) with read_var
+// variant v. Returns 0, 1 for invalid arguments, 2 for a launch error.
+extern "C" __attribute__((visibility("default"))) int bench_read_var(int v, const void *buf, int64_t bytes, void *sink, hipStream_t s)
+{
+    if (v < 0 || v >= kNumVars || !buf || !sink || bytes < 16 || bytes % 16 != 0 ||
+        (uintptr_t)buf % 16 != 0)
+        return 1;
+    const int64_t chunks = bytes / 16;
+    if (!grid_ok(chunks)) return 1;
+    switch (v) {
+    case 0: launch_var<256, 1, true>(buf, chunks, sink, s); break;
+    case 1: launch_var<256, 2, true>(buf, chunks, sink, s); break;
+    case 2: launch_var<256, 4, true>(buf, chunks, sink, s); break;
+    case 3: launch_var<256, 8, true>(buf, chunks, sink, s); break;
+    case 4: launch_var<256, 9, true>(buf, chunks, sink, s); break;
+    case 5: launch_var<256, 1, false>(buf, chunks, sink, s); break;
+    case 6: launch_var<256, 2, false>(buf, chunks, sink, s); break;
+    case 7: launch_var<256, 4, false>(buf, chunks, sink, s); break;
+    case 8: launch_var<256, 9, false>(buf, chunks, sink, s); break;
+    case 9: launch_var<512, 4, true>(buf, chunks, sink, s); break;
+    case 10: launch_var<512, 9, true>(buf, chunks, sink, s); break;
+    case 11: launch_var<1024, 4, true>(buf, chunks, sink, s); break;
+    case 12: launch_var<1024, 9, true>(buf, chunks, sink, s); break;
+    case 13: launch_var<64, 9, false>(buf, chunks, sink, s); break;
+    case 14: launch_var<128, 18, false>(buf, chunks, sink, s); break;
+    default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// A launch of grid workgroups of 256 threads that do nothing.
+extern "C" __attribute__((visibility("default"))) int bench_empty(int grid, void *sink, hipStream_t s)
+{
+    if (grid < 1 || !sink) return 1;
+    hipLaunchKernelGGL(empty, dim3(grid), dim3(256), 0, s, static_cast<uint32_t *>(sink), 0);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
