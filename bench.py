@@ -479,7 +479,7 @@ def main():
                  for i in range(0, 2 * n, 2)],
                 bytes=2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4)
         # Q4_K (the k-quant format of the pages' CLIP/CLAP path) at the FFN
-        # pair's shapes, cold pools; two and four rows over the up matrix
+        # pair's shapes, cold pools; 2, 4, 8 and 16 rows over the up matrix
         for name in ("q4_k_gemv_ffn_up", "q4_k_gemv_ffn_down"):
             wlk = synth.WORKLOADS[name]
             xk_h, wk_h = synth.workload_inputs(name)
@@ -489,7 +489,7 @@ def main():
             keep += wk + [xk, yk]
             add_row(name, lib.qmm_gemv_q4_k, gemv_args(xk, wk, yk, 1, wlk["N"], wlk["K"], n),
                     bytes=wk_h.nbytes + xk_h.nbytes + yk.numel() * 4)
-            for m in ((2, 4) if name == "q4_k_gemv_ffn_up" else ()):
+            for m in ((2, 4, 8, 16) if name == "q4_k_gemv_ffn_up" else ()):
                 xm = torch.from_numpy(synth.activations(m, wlk["K"])).to(dev)
                 ym = torch.empty((m, wlk["N"]), device=dev)
                 keep += [xm, ym]

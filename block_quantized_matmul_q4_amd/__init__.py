@@ -194,7 +194,7 @@ def gemm_q8_0(x, w, n: int, k: int, out=None):
 
 
 def gemv_q4_k(x, w, n: int, k: int, out=None):
-    """y[M, N] = x[M, K] @ W^T for Q4_K W (super-blocks of 256; 1 <= M <= 4)."""
+    """y[M, N] = x[M, K] @ W^T for Q4_K W (super-blocks of 256; 1 <= M <= 16)."""
     return _call(qmm_gemv_q4_k, "q4_k", x, w, n, k, out)
 
 

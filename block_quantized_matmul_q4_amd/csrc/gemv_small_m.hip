@@ -1,18 +1,23 @@
 // Small-M GEMV (2 <= M <= 16 activation rows: batched or speculative
-// decode) over GGUF Q4_0 / Q8_0 weights, on the bf16 matrix cores. The
-// C-ABI sends 5 <= M <= 8, and Q8_0 with 9 <= M <= 16 and N < 8192, here when
-// K % 256 == 0 (each wave takes K in slices of 256): up to 4
-// rows the f32 FMA kernel that streams the weights for one row is faster
-// (it decodes each pair once for all rows), and from 9 rows over wide
-// matrices the 32-row weight-slice kernel is.
+// decode) over GGUF Q4_0 / Q8_0 weights, and 5 <= M <= 16 over Q4_K
+// super-blocks, on the bf16 matrix cores. The C-ABI sends 5 <= M <= 8, and
+// Q8_0 with 9 <= M <= 16 and N < 8192, here when K % 256 == 0 (each wave
+// takes K in slices of 256), and every Q4_K GEMV of 5 to 16 rows: up to 4
+// rows the f32 FMA kernels that stream the weights for one row are faster
+// (they decode each weight once for all rows), and from 9 rows over wide
+// matrices the 32-row weight-slice kernel is (Q4_0, Q8_0).
 //
 // With several activation rows the f32 FMA count (M per weight) outgrows
 // the weight stream, so the contraction moves to v_mfma_f32_16x16x32_bf16:
 // one instruction covers 16 A rows x 16 weight rows x one 32-wide block.
 // Accuracy is kept to the f32 bound:
-//  * B operand (weights): the integer codes 16*(q-8) (Q4_0) or q (Q8_0),
-//    exact in bf16. The fp16 scale d is applied in f32 to the block's
-//    result, so no weight is rounded.
+//  * B operand (weights): the integer codes 16*(q-8) (Q4_0), q (Q8_0) or
+//    the nibble q in 0..15 (Q4_K), exact in bf16. The fp16 scale d (Q4_0,
+//    Q8_0) or the sub-block scale d*sc (Q4_K) is applied in f32 to the
+//    block's result, so no weight is rounded. A Q4_K sub-block's offset
+//    dmin*mn multiplies the sum of its 32 activations, which one more MFMA
+//    per block forms from the same A operand against a B operand of ones:
+//    per block, acc += d*sc * sum(q x) - dmin*mn * sum(x), in f32.
 //  * A operand (activations): x = hi + lo with hi = bf16(x) and
 //    lo = bf16(x - hi), both round-to-nearest-even; hi + lo represents x to
 //    within 2^-17 |x| (about 16 of its 24 significand bits), each product
@@ -22,13 +27,16 @@
 //    they take one instruction each.
 // Within a block the k order is permuted identically in A and B so that
 // each lane's eight weights come from one qs dword (Q4_0: bytes 4g..4g+3,
-// i.e. elements 4g..4g+3 and 4g+16..4g+19; Q8_0: elements 8g..8g+7).
+// i.e. elements 4g..4g+3 and 4g+16..4g+19) or two (Q8_0: elements
+// 8g..8g+7; Q4_K: the nibbles of bytes 8g..8g+7 of the sub-block's 32).
 //
 // Work split: a workgroup of WAVES waves owns NT x 16 weight rows; each wave
-// takes a 256-wide slice of K (8 blocks) per pass. A wave
+// takes a 256-wide slice of K (8 blocks, or one Q4_K super-block) per pass.
+// A wave
 //  1. loads its activation slice (M rows x 256, one float4 per lane and
-//     row, coalesced) and its weight pairs (whole 36/68-byte pairs with
-//     16-byte loads);
+//     row, coalesced) and its weight bytes (whole 36/68-byte pairs of
+//     blocks with 16-byte loads; a 144-byte Q4_K super-block is four
+//     36-byte pieces);
 //  2. writes both to its own LDS region: activations already split into
 //     hi/lo bf16 and laid out as MFMA A fragments, weight pairs re-aligned
 //     so that every qs dword is dword-aligned;
@@ -67,17 +75,21 @@ template <> struct Fmt<FMT_Q4_0> {
         o[8] = (D[0] & 0xFFFFu) | (D[4] & 0xFFFF0000u);
     }
 
-    // lane group g's eight codes of block h of an LDS pair, and the scale
-    __device__ static void b_operand(const uint32_t *pair, int h, int g, bf16x8 &b, float &d)
+    static constexpr bool kHasMin = false;
+
+    // lane group g's eight codes of block b of an LDS weight row, and the scale
+    __device__ static void b_operand(const uint32_t *row, int b, int g, bf16x8 &bq, float &d)
     {
+        const uint32_t *pair = row + (b / 2) * kPairDwords;
+        const int h = b & 1;
         const uint32_t q = pair[4 * h + g];
         const uint32_t dd = pair[8];
         d = h ? half_hi(dd) : half_lo(dd);
         const uint32_t lo = lo16(q), hi = hi16(q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            b[e] = (__bf16)sbyte(lo, e);
-            b[4 + e] = (__bf16)sbyte(hi, e);
+            bq[e] = (__bf16)sbyte(lo, e);
+            bq[4 + e] = (__bf16)sbyte(hi, e);
         }
     }
 
@@ -106,17 +118,84 @@ template <> struct Fmt<FMT_Q8_0> {
         o[16] = (D[0] & 0xFFFFu) | (D[8] & 0xFFFF0000u);
     }
 
-    __device__ static void b_operand(const uint32_t *pair, int h, int g, bf16x8 &b, float &d)
+    static constexpr bool kHasMin = false;
+
+    __device__ static void b_operand(const uint32_t *row, int b, int g, bf16x8 &bq, float &d)
     {
+        const uint32_t *pair = row + (b / 2) * kPairDwords;
+        const int h = b & 1;
         // two dword reads: an LDS pair of 17 dwords is only dword aligned
         const uint32_t q0 = pair[8 * h + 2 * g], q1 = pair[8 * h + 2 * g + 1];
         const uint32_t dd = pair[16];
         d = h ? half_hi(dd) : half_lo(dd);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            b[e] = (__bf16)sbyte(q0, e);
-            b[4 + e] = (__bf16)sbyte(q1, e);
+            bq[e] = (__bf16)sbyte(q0, e);
+            bq[4 + e] = (__bf16)sbyte(q1, e);
         }
+    }
+
+    __device__ static void slot(int kk, int &g, int &e0)
+    {
+        g = kk >> 3;
+        e0 = kk & 7;
+    }
+};
+
+// Q4_K: one 144-byte super-block (256 weights, eight sub-blocks of 32) per
+// weight row and pass, staged as four 36-byte pieces so that the loads are
+// those of a Q4_0 row of the same K. LDS keeps the global order: dword 0 is
+// d | dmin << 16, dwords 1-3 the twelve 6-bit scale/minimum bytes, dwords
+// 4-35 the nibbles (weight 64c + i, i < 32, low nibble of qs byte 32c + i;
+// weight 64c + 32 + i its high nibble).
+template <> struct Fmt<FMT_Q4_K> {
+    static constexpr int kPairBytes = 36;
+    static constexpr int kPairDwords = 9;
+    static constexpr float kOutScale = 1.0f;
+    static constexpr bool kHasMin = true;
+
+    __device__ static void relayout(const uint32_t *D, uint32_t *o)
+    {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) o[i] = D[i];
+    }
+
+    // sub-block b's 6-bit scale and minimum from the twelve scale bytes
+    // (s0, s1, s2 = bytes 0-3, 4-7, 8-11): for b < 4 the low 6 bits of bytes
+    // b and 4 + b; for b >= 4 the two nibbles of byte 4 + b below the top 2
+    // bits of bytes b - 4 (scale) and b (minimum)
+    __device__ static void scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int b, int &sc,
+                                     int &mn)
+    {
+        if (b < 4) {
+            sc = (s0 >> (8 * b)) & 63;
+            mn = (s1 >> (8 * b)) & 63;
+        } else {
+            const uint32_t lo = s2 >> (8 * (b - 4));
+            sc = (lo & 15) | (((s0 >> (8 * (b - 4) + 6)) & 3) << 4);
+            mn = ((lo >> 4) & 15) | (((s1 >> (8 * (b - 4) + 6)) & 3) << 4);
+        }
+    }
+
+    // lane group g's eight codes of sub-block b: the low (even b) or high
+    // (odd b) nibbles of bytes 8g..8g+7 of the sub-block pair's 32 qs bytes,
+    // i.e. elements 8g..8g+7 of the sub-block; its scale d*sc and offset
+    // dmin*mn
+    __device__ static void b_operand(const uint32_t *row, int b, int g, bf16x8 &bq, float &ds,
+                                     float &dm)
+    {
+        const uint32_t *qs = row + 4 + 8 * (b / 2) + 2 * g;
+        const int sh = 4 * (b & 1);
+        const uint32_t c0 = (qs[0] >> sh) & 0x0F0F0F0Fu, c1 = (qs[1] >> sh) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bq[e] = (__bf16)(float)((c0 >> (8 * e)) & 0xFFu);
+            bq[4 + e] = (__bf16)(float)((c1 >> (8 * e)) & 0xFFu);
+        }
+        int sc, mn;
+        scale_min(row[1], row[2], row[3], b, sc, mn);
+        ds = half_lo(row[0]) * (float)sc;
+        dm = half_hi(row[0]) * (float)mn;
     }
 
     __device__ static void slot(int kk, int &g, int &e0)
@@ -244,17 +323,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
 #pragma unroll
             for (int tt = 0; tt < TERMS; ++tt)
                 a[tt] = *reinterpret_cast<const bf16x8 *>(&af[afrag((b * TERMS + tt) * 64 + lane)]);
+            // Q4_K: sum of block b's activations for each A row, in every column
+            f32x4 xsum = zero;
+            if constexpr (L::kHasMin) {
+                bf16x8 ones;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+                xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], ones, zero, 0, 0, 0);
+                if constexpr (!PACK)
+                    xsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[TERMS - 1], ones, xsum, 0, 0, 0);
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint32_t *pair = wl + (16 * t + col) * WROW + (b / 2) * L::kPairDwords;
+                const uint32_t *row = wl + (16 * t + col) * WROW;
                 bf16x8 bq;
-                float d;
-                L::b_operand(pair, b & 1, g, bq, d);
+                float d, dm = 0.f;
+                if constexpr (L::kHasMin)
+                    L::b_operand(row, b, g, bq, d, dm);
+                else
+                    L::b_operand(row, b, g, bq, d);
                 f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], bq, zero, 0, 0, 0);
                 if constexpr (!PACK)
                     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[TERMS - 1], bq, c, 0, 0, 0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(d, c[e], acc[t][e]);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (L::kHasMin) acc[t][e] = fmaf(-dm, xsum[e], acc[t][e]);
+                    acc[t][e] = fmaf(d, c[e], acc[t][e]);
+                }
             }
         }
     }
@@ -326,7 +421,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
                                int M, int N, int K, hipStream_t stream)
 {
-    if (fmt == FMT_Q4_K) return hipErrorInvalidValue;
+    if (fmt == FMT_Q4_K) return launch_fmt<FMT_Q4_K>(x, w, y, M, N, K, stream);
     return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
                            : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
 }

@@ -194,10 +194,11 @@ QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
     // weight as Q4_0's 18 per 32: the shared size and overlap checks apply
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
+    // up to 4 rows: f32 FMAs on each weight formed once; 5 to 16 rows: the
+    // matrix-core kernel (codes exact in bf16, x as two bf16 terms)
     if (M > qmm::kGemvRowsMax)
-        return fail(QMM_EUNSUPPORTED,
-                    "%s: M=%lld unsupported (at most %d activation rows; qmm_gemm_q4_k takes more)",
-                    fn, (long long)M, qmm::kGemvRowsMax);
+        return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_K, x, (const uint8_t *)w, y,
+                                                   (int)M, (int)N, (int)K, stream));
     return finish(fn, qmm::launch_gemv_q4_k(x, (const uint8_t *)w, y, (int)M, (int)N, (int)K,
                                             stream));
 }

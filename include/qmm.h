@@ -147,7 +147,7 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
                                  hipStream_t stream);
 
 /*
- * Decode GEMV over Q4_K super-blocks, 1 <= M <= 4 activation rows. Q4_K is the
+ * Decode GEMV over Q4_K super-blocks, 1 <= M <= 16 activation rows. Q4_K is the
  * k-quant 4-bit format the pages ("Add generated quant-kernel JIT and
  * accelerate Gemma4, BGE-M3, and GLiNER2", section Summary) keep for their
  * CLIP/CLAP path; they give no layout, and GGUF's is taken. w is N rows of
@@ -159,12 +159,19 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
  *   (weight 64c+i, i < 32, is the low nibble of byte 16+32c+i, weight
  *   64c+32+i its high nibble); weight e is in sub-block e/32 and
  *   w = d * sc * q - dmin * mn.
- * x is f32[M][K], y f32[M][N] (overwritten). Each weight is formed once
- * and applied to every activation row; a row of the result does not depend
- * on the other rows. Errors as for qmm_gemv_q4_0, plus QMM_EINVAL for K not
- * a multiple of 256 and QMM_EUNSUPPORTED for M > 4 (qmm_gemm_q4_k takes
- * any M). Accuracy: |y - sum_k x w| <= 1e-4 * sum_k |x w|, each w rounded
- * once to f32 and each product accumulated in f32.
+ * x is f32[M][K], y f32[M][N] (overwritten); the weights stream from HBM
+ * once per call. Errors as for qmm_gemv_q4_0, plus QMM_EINVAL for K not a
+ * multiple of 256 (qmm_gemm_q4_k takes any M).
+ * Accuracy, 1 to 4 rows: each weight is formed once in f32 (one rounding)
+ * and applied to every activation row in f32; a row of the result does not
+ * depend on the other rows; |y - sum_k x w| <= 1e-4 * sum_k |x w|.
+ * 5 to 16 rows (bf16 matrix cores): the nibbles are exact in bf16, x is
+ * carried as two bf16 terms (within 2^-17 |x|, as in qmm_gemv_q4_0), and
+ * per sub-block the f32 result is d*sc * sum(q x) - dmin*mn * sum(x), the
+ * two sums taken from the same bf16 terms; since the two parts are rounded
+ * apart, the bound is |y - sum_k x w| <= 1e-4 * sum_k (|d sc q| + |dmin mn|) |x|,
+ * which equals the one above where no sub-block has both a scale and a
+ * minimum (and exceeds it only where the two parts cancel).
  */
 QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

@@ -159,7 +159,6 @@ def test_bench_read_kernels_load_and_reject_bad_arguments():
     ((A, B, C, 1, 8, 0), qmm.QMM_EINVAL, ">= 1"),
     ((A, B, C, 1, 8, 384), qmm.QMM_EINVAL, "multiple of 256"),
     ((A, B, C, 1, 8, 64), qmm.QMM_EINVAL, "multiple of 256"),
-    ((A, B, C, 5, 8, 256), qmm.QMM_EUNSUPPORTED, "at most 4 activation rows"),
     ((A, B, C, 17, 8, 256), qmm.QMM_EINVAL, "exceeds 16"),
     ((A, B, C, 1, 8, 65536 + 256), qmm.QMM_EUNSUPPORTED, "unsupported"),
     ((A + 4, B, C, 1, 8, 256), qmm.QMM_EALIGN, "misaligned"),

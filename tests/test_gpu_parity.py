@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import block_quantized_matmul_q4_amd as qmm
+import bounds
 import oracle
 import pins
 import synth
@@ -595,9 +596,10 @@ def test_gemv_q4_k_repeatable_and_errors():
     assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
     xt = torch.zeros(5, 256, device="cuda")
     wt = torch.zeros(8 * 144, dtype=torch.uint8, device="cuda")
+    xt = torch.zeros(17, 256, device="cuda")
     with pytest.raises(qmm.QmmError) as e:
         qmm.gemv_q4_k(xt, wt, 8, 256)
-    assert e.value.status == qmm.QMM_EUNSUPPORTED
+    assert e.value.status == qmm.QMM_EINVAL
     with pytest.raises(ValueError):
         qmm.gemv_q4_k(torch.zeros(1, 384, device="cuda"), wt, 8, 384)
 
@@ -625,6 +627,67 @@ def test_gemv_q4_k_rows_match_single_row_bitwise(m, n, k):
     y = run("gemv", "q4_k", x, w, n, k)
     for r in range(m):
         assert np.array_equal(y[r], run("gemv", "q4_k", x[r:r + 1], w, n, k)[0]), r
+
+
+# Five to sixteen activation rows (matrix-core kernel): every launch branch
+# (N >= 65536 with M <= 8; N < 8192 with hi/lo packed (M <= 8) and apart;
+# wider N packed and apart), ragged N, one pass (K = 256) and the largest K.
+# The contract's bound scale is sum_k (|d sc q| + |dmin mn|) |x|; on these
+# seeded weights the error also stays within 1e-4 sum_k |x w|.
+Q4_K_MANY_ROWS_SHAPES = [
+    (5, 300, 1024), (6, 8192, 2048), (8, 2048, 8192), (7, 65539, 512), (8, 65536, 256),
+    (9, 8192, 2048), (12, 2049, 4352), (16, 8192, 2048), (16, 2048, 8192), (13, 17, 256),
+    (16, 50, 65536), (11, 4099, 8448), (5, 1, 256), (10, 9000, 1024), (14, 65537, 256),
+]
+
+
+@pytest.mark.parametrize("m,n,k", Q4_K_MANY_ROWS_SHAPES)
+def test_gemv_q4_k_many_rows(orc, m, n, k):
+    seed = m + n + k
+    what = f"gemv_q4_k M={m} N={n} K={k} seed={seed}"
+    note(f"[parity] {what}")
+    f = synth.q4_k_fields(n, k, seed)
+    x = synth.activations(m, k, seed)
+    w = synth.pack_q4_k(*f)
+    y = run("gemv", "q4_k", x, w, n, k)
+    yref, s = orc.matmul("q4_k", x, w, n, k)
+    r = assert_parity(y, yref, bounds.q4_k_term_abs_sum(*f, x), TAU_GEMV, what)
+    r1 = assert_parity(y, yref, s, TAU_GEMV, what + " (scale sum |x w|)")
+    note(f"  max err / bound {r:.3g} (two-part scale), {r1:.3g} (sum |x w|)")
+
+
+@pytest.mark.parametrize("m,n", [(5, 300), (8, 300), (9, 300), (16, 300), (8, 8192),
+                                 (16, 8192)])
+def test_gemv_q4_k_many_rows_exact(orc, m, n):
+    """5-16 rows. One-hot x: each output is the weight rounded once to f32
+    (d sc and dmin mn are exact in f32, and the last step is one fused
+    multiply-add). d = dmin = 1 with integer x: every partial sum is an
+    integer below 2^24, so the result is exact. Zero nibbles and minimums
+    give zeros. Three calls agree bit for bit."""
+    k = 1024
+    rng = np.random.default_rng(40 + m + n)
+    w = synth.pack_q4_k(*q4_k_case(rng, n, k))
+    x = np.zeros((m, k), np.float32)
+    ks = rng.integers(0, k, m)
+    x[np.arange(m), ks] = 1.0
+    note(f"[exact] gemv_q4_k one-hot M={m} N={n}")
+    y = run("gemv", "q4_k", x, w, n, k).astype(np.float64)
+    yref, _ = orc.matmul("q4_k", x, w, n, k)
+    assert np.array_equal(y, yref.astype(np.float32).astype(np.float64))
+
+    d, dmin, sc, mn, q = q4_k_case(rng, n, k, d_one=True)
+    w = synth.pack_q4_k(d, dmin, sc, mn, q)
+    x = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    note(f"[exact] gemv_q4_k integer M={m} N={n}")
+    ys = [run("gemv", "q4_k", x, w, n, k) for _ in range(3)]
+    yref, _ = orc.matmul("q4_k", x, w, n, k)
+    assert np.array_equal(ys[0].astype(np.float64), yref)
+    assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
+
+    w = synth.pack_q4_k(d, dmin, sc, np.zeros_like(mn), np.zeros_like(q))
+    x = (rng.standard_normal((m, k)) * 100).astype(np.float32)
+    note(f"[exact] gemv_q4_k zero nibbles and minimums M={m} N={n}")
+    assert np.all(run("gemv", "q4_k", x, w, n, k) == 0.0)
 
 
 # Q4_K through the prefill GEMM: M <= 4 takes the GEMV (bitwise), 5-128 rows

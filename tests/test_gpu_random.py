@@ -2,8 +2,8 @@
 every entry point, each compared element by element with the f64 oracle.
 
 Case i draws, from numpy's generator seeded with i, an entry point and a
-shape: M from the entry point's range (GEMV 1-16, Q4_K GEMV 1-4, GEMM 1-300,
-gated front half 1), N in 1..1200, K a multiple of 64 (Q4_K: of 256) up to
+shape: M from the entry point's range (GEMVs 1-16, GEMM 1-300, gated front
+half 1), N in 1..1200, K a multiple of 64 (Q4_K: of 256) up to
 4096, redrawn while M N K exceeds 2^24 so that the oracle stays fast; the
 weights and activations come from the seeded generators with seed i. The
 bound is the entry point's contract: 1e-4 sum_k |w x| for the GEMVs, 8e-3
@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import block_quantized_matmul_q4_amd as qmm
+import bounds
 import oracle
 import synth
 
@@ -45,9 +46,7 @@ def draw(i):
     entry = ENTRIES[int(rng.integers(0, len(ENTRIES)))]
     fmt = entry.split("_", 1)[1] if entry != "ffn_gate_up_q4_0" else "q4_0"
     while True:
-        if entry.startswith("gemv_q4_k"):
-            m = int(rng.integers(1, 5))
-        elif entry.startswith("gemv"):
+        if entry.startswith("gemv"):
             m = int(rng.integers(1, 17))
         elif entry.startswith("gemm"):
             m = int(rng.integers(1, 301))
@@ -85,6 +84,8 @@ def one_case(o, i):
         y = getattr(qmm, entry)(xt, wt, n, k)
         torch.cuda.synchronize()
         yref, s = o.matmul(fmt, x, w, n, k)
+        if entry == "gemv_q4_k" and m > 4:
+            s = bounds.q4_k_term_abs_sum(*synth.q4_k_fields(n, k, seed=i), x)
         bound = (8e-3 if entry.startswith("gemm") else 1e-4) * s
         y = y.cpu().numpy().astype(np.float64)
     err = np.abs(y - yref)
