@@ -478,6 +478,17 @@ def main():
                   w_up[(i + 1) % len(w_up)].data_ptr(), hf.data_ptr(), 1, up["N"], up["K"])
                  for i in range(0, 2 * n, 2)],
                 bytes=2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4)
+        # the same over 2 and 4 tokens (batched decode)
+        for m in (2, 4):
+            xm = torch.from_numpy(synth.activations(m, up["K"])).to(dev)
+            hm = torch.empty((m, up["N"]), device=dev)
+            keep += [xm, hm]
+            add_row(f"q4_0_ffn_gate_up_m{m}", lib.qmm_ffn_gate_up_q4_0,
+                    [(xm.data_ptr(), w_up[i % len(w_up)].data_ptr(),
+                      w_up[(i + 1) % len(w_up)].data_ptr(), hm.data_ptr(), m, up["N"], up["K"])
+                     for i in range(0, 2 * n, 2)],
+                    bytes=2 * w_up_h.nbytes + xm.numel() * 4 + hm.numel() * 4,
+                    flops=4 * m * up["N"] * up["K"], tokens=m)
         # Q4_K (the k-quant format of the pages' CLIP/CLAP path) at the FFN
         # pair's shapes, cold pools; 2, 4, 8 and 16 rows over the up matrix
         for name in ("q4_k_gemv_ffn_up", "q4_k_gemv_ffn_down"):

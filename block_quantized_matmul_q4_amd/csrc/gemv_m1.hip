@@ -179,11 +179,11 @@ template <> struct Pair<FMT_Q8_0> {
 // loads, MR activation rows (M <= MR; rows past M repeat row M-1 and are not
 // stored). Grid: ceil(N / (WG / T * RPT)) workgroups.
 //
-// GATED (RPT = 2, MR = 1): the gated FFN front half. A thread's two rows are
-// row n of the gate matrix w and row n of the up matrix w2, and the output
-// is y[n] = gelu_tanh(gate) * up with gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi)
-// (g + 0.044715 g^3))), evaluated in f32 once the two sums are complete.
-// Grid: ceil(N / (WG / T)) workgroups.
+// GATED (RPT = 2): the gated FFN front half. A thread's two rows are row n
+// of the gate matrix w and row n of the up matrix w2, and the output is
+// y[m][n] = gelu_tanh(gate) * up for each activation row m, with
+// gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), evaluated in
+// f32 once the two sums are complete. Grid: ceil(N / (WG / T)) workgroups.
 //
 // A wave owns TW = min(T, 64) consecutive pairs of each chunk for its rows
 // (a row wider than one wave is split over T / 64 waves). Per pass of CH
@@ -219,8 +219,7 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const uint8_t *__restrict__ w2, float *__restrict__ y, int M, int N, int P)
 {
     using L = Pair<FMT>;
-    static_assert(!GATED || (RPT == 2 && MR == 1),
-                  "gated: one gate row and one up row per thread, one activation row");
+    static_assert(!GATED || RPT == 2, "gated: one gate row and one up row per thread");
     constexpr int RPAR = WG / T;                // rows in flight per workgroup
     constexpr int TW = T < 64 ? T : 64;         // pairs per wave per chunk
     constexpr int WPR = T / TW;                 // waves per row
@@ -392,8 +391,13 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         for (int m = 0; m < MR; ++m) acc[j][m] = group_sum<TW>(acc[j][m]);
 
     if constexpr (WPR == 1 && GATED) {
-        if (t == T - 1 && n_first < N)
-            y[n_first] = gelu_tanh(acc[0][0] * L::kOutScale) * (acc[1][0] * L::kOutScale);
+        if (t == T - 1 && n_first < N) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                if (m < M)
+                    y[(int64_t)m * N + n_first] =
+                        gelu_tanh(acc[0][m] * L::kOutScale) * (acc[1][m] * L::kOutScale);
+        }
     } else if constexpr (WPR == 1) {
         if (t == T - 1) {
 #pragma unroll
@@ -414,15 +418,17 @@ __global__ __launch_bounds__(WG) void gemv_m1_kernel(
         }
         __syncthreads();
         if constexpr (GATED) {
-            if (tid < RPAR) {
+            if (tid < RPAR * MR) {
+                const int m = tid % MR, rr = tid / MR;
                 float sg = 0.f, su = 0.f;
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) {
-                    sg += red[(tid * WPR + q) * RPT + 0];
-                    su += red[(tid * WPR + q) * RPT + 1];
+                    sg += red[((rr * WPR + q) * RPT + 0) * MR + m];
+                    su += red[((rr * WPR + q) * RPT + 1) * MR + m];
                 }
-                const int n = blockIdx.x * RPAR + tid;
-                if (n < N) y[n] = gelu_tanh(sg * L::kOutScale) * (su * L::kOutScale);
+                const int n = blockIdx.x * RPAR + rr;
+                if (n < N && m < M)
+                    y[(int64_t)m * N + n] = gelu_tanh(sg * L::kOutScale) * (su * L::kOutScale);
             }
         } else if (tid < RPAR * RPT * MR) {
             const int m = tid % MR, rr = (tid / MR) % RPAR, j = tid / (MR * RPAR);
@@ -449,14 +455,14 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int 
     return hipGetLastError();
 }
 
-template <int T, int WG = kThreads, bool SX = false>
-hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, float *h, int N,
-                        int P, hipStream_t stream)
+template <int T, int WG = kThreads, bool SX = false, int MR = 1>
+hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, float *h, int M,
+                        int N, int P, hipStream_t stream)
 {
     constexpr int rows_per_wg = WG / T;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_m1_kernel<FMT_Q4_0, T, 2, 1, WG, SX, false, true, 1>), dim3(grid),
-                       dim3(WG), 0, stream, x, wg, wu, h, 1, N, P);
+    hipLaunchKernelGGL((gemv_m1_kernel<FMT_Q4_0, T, 2, 1, WG, SX, false, true, MR>), dim3(grid),
+                       dim3(WG), 0, stream, x, wg, wu, h, M, N, P);
     return hipGetLastError();
 }
 
@@ -524,17 +530,31 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
 
 // Gated FFN front half: a thread's two rows are one gate row and one up
 // row; from P = 32 on, workgroups share one activation copy (timing sweeps
-// as above).
+// as above). Several activation rows (MR = 2 or 4; M = 3 runs four and
+// stores three) take the same launch shapes, so each row equals the one-row
+// result bit for bit.
+template <int MR>
+hipError_t launch_gated_rows(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
+                             float *h, int M, int N, int P, hipStream_t stream)
+{
+    if (P <= 4) return launch_gated<4, kThreads, false, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 8) return launch_gated<8, kThreads, false, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 16)
+        return launch_gated<16, kThreads, false, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 32) return launch_gated<32, 256, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 64 || N >= 8192)
+        return launch_gated<64, 512, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    return launch_gated<128, 512, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
+}
+
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
-                              float *h, int N, int K, hipStream_t stream)
+                              float *h, int M, int N, int K, hipStream_t stream)
 {
     const int P = K / 64;
-    if (P <= 4) return launch_gated<4>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 8) return launch_gated<8>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 16) return launch_gated<16>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 32) return launch_gated<32, 256, true>(x, w_gate, w_up, h, N, P, stream);
-    if (P <= 64 || N >= 8192) return launch_gated<64, 512, true>(x, w_gate, w_up, h, N, P, stream);
-    return launch_gated<128, 512, true>(x, w_gate, w_up, h, N, P, stream);
+    if (M == 1) return launch_gated_rows<1>(x, w_gate, w_up, h, M, N, P, stream);
+    if (M == 2) return launch_gated_rows<2>(x, w_gate, w_up, h, M, N, P, stream);
+    if (M <= kGemvRowsMax) return launch_gated_rows<4>(x, w_gate, w_up, h, M, N, P, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, int M,

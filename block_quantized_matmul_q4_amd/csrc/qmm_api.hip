@@ -175,11 +175,11 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
     const uint64_t w_len = (uint64_t)N * (uint64_t)(K / 32) * (uint64_t)qmm::kQ4Bytes;
     if (overlaps((uintptr_t)h, (uint64_t)M * (uint64_t)N * 4u, (uintptr_t)w_up, w_len))
         return fail(QMM_EINVAL, "%s: h overlaps w_up", fn);
-    if (M != 1)
-        return fail(QMM_EUNSUPPORTED, "%s: M=%lld unsupported (one token: M must be 1)", fn,
-                    (long long)M);
+    if (M > qmm::kGemvRowsMax)
+        return fail(QMM_EUNSUPPORTED, "%s: M=%lld unsupported (at most %d activation rows)", fn,
+                    (long long)M, qmm::kGemvRowsMax);
     return finish(fn, qmm::launch_ffn_gate_up(x, (const uint8_t *)w_gate,
-                                              (const uint8_t *)w_up, h, (int)N, (int)K,
+                                              (const uint8_t *)w_up, h, (int)M, (int)N, (int)K,
                                               stream));
 }
 

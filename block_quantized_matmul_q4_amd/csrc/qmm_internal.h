@@ -34,8 +34,9 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
 // N = 65536 54 against 79 us)
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream);
+// Gated FFN front half over Q4_0, M <= kGemvRowsMax activation rows.
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
-                              float *h, int N, int K, hipStream_t stream);
+                              float *h, int M, int N, int K, hipStream_t stream);
 // Q4_K GEMV, 1 to 4 activation rows (K % 256 == 0).
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream);

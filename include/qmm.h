@@ -51,7 +51,7 @@
  * value comes out (NaN, +Inf or -Inf) is not specified and may differ from
  * the definition evaluated weight by weight: the GEMV kernels apply d to a
  * block's partial sum, so an infinite scale over a zero code (q = 8) gives
- * +-Inf where d * (q - 8) * x would give NaN. The gated entry point's h[n] is
+ * +-Inf where d * (q - 8) * x would give NaN. The gated entry point's h[m][n] is
  * non-finite exactly when row n of W_gate or of W_up holds such a scale.
  */
 #ifndef QMM_H
@@ -128,17 +128,20 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
 
 /*
- * Gated FFN front half over Q4_0 weights for one token (M = 1; the step
+ * Gated FFN front half over Q4_0 weights for 1 <= M <= 4 tokens (M = 1 for
+ * one decoded token, 2..4 for batched or speculative decode; the step
  * either side of the path):
- *   h[n] = gelu_tanh(g[n]) * u[n],  g = x * W_gate^T,  u = x * W_up^T,
+ *   h[m][n] = gelu_tanh(g[m][n]) * u[m][n],  g = x * W_gate^T,  u = x * W_up^T,
  *   gelu_tanh(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))).
  * The pages ("Add generated quant-kernel JIT and accelerate Gemma4, BGE-M3,
  * and GLiNER2", section Summary) credit fused FFN paths without naming the
  * activation; the tanh form of GELU is the Gemma family's. W_gate and W_up
  * are both N rows of K/32 Q4_0 blocks (same layout as the GEMV's w); both
- * stream in one launch that reads x once. h is f32[1][N], overwritten.
- * Errors as above, plus QMM_EINVAL for a null or overlapping w_up,
- * QMM_EALIGN for a w_up not 16-byte aligned, QMM_EUNSUPPORTED for M != 1.
+ * stream in one launch that reads x once. x is f32[M][K], h f32[M][N],
+ * overwritten; each weight is decoded once for all rows and a row of h
+ * equals the one-row result bit for bit. Errors as above, plus QMM_EINVAL
+ * for a null or overlapping w_up, QMM_EALIGN for a w_up not 16-byte
+ * aligned, QMM_EUNSUPPORTED for M > 4.
  * Accuracy: g and u within the GEMV bound (1e-4 of their abs-sums); the
  * activation and product in f32.
  */

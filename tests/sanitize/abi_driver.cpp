@@ -157,10 +157,16 @@ void gated()
     CHECK(gate_up(A, B, 0, C, 1, 300, 2048) == QMM_EINVAL);       // null w_up
     CHECK(gate_up(A, B, D + 2, C, 1, 300, 2048) == QMM_EALIGN);
     CHECK(gate_up(A, B, D, D + 32, 1, 300, 2048) == QMM_EINVAL);  // h inside w_up
-    CHECK(gate_up(A, B, D, C, 2, 300, 2048) == QMM_EUNSUPPORTED);
+    CHECK(gate_up(A, B, D, C, 5, 300, 2048) == QMM_EUNSUPPORTED);
+    CHECK(gate_up(A, B, D, C, 17, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(0, B, D, C, 1, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(A, B, D, C, 1, 300, 96) == QMM_EUNSUPPORTED);
     CHECK(g_stub.calls == before + 1);
+    for (int64_t m = 2; m <= 4; ++m) {
+        CHECK(gate_up(A, B, D, C, m, 300, 2048) == QMM_OK);
+        CHECK(std::strcmp(g_stub.route, "ffn_gate_up") == 0 && g_stub.M == m && g_stub.N == 300);
+    }
+    CHECK(g_stub.calls == before + 4);
 }
 
 void strings_and_threads()

@@ -38,10 +38,10 @@ hipError_t launch_gemv_slices(int fmt, const float *, const uint8_t *, float *, 
 {
     return record("gemv_slices", fmt, M, N, K);
 }
-hipError_t launch_ffn_gate_up(const float *, const uint8_t *, const uint8_t *, float *, int N,
-                              int K, hipStream_t)
+hipError_t launch_ffn_gate_up(const float *, const uint8_t *, const uint8_t *, float *, int M,
+                              int N, int K, hipStream_t)
 {
-    return record("ffn_gate_up", FMT_Q4_0, 1, N, K);
+    return record("ffn_gate_up", FMT_Q4_0, M, N, K);
 }
 hipError_t launch_gemv_q4_k(const float *, const uint8_t *, float *, int M, int N, int K,
                             hipStream_t)

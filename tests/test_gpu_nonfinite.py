@@ -129,13 +129,14 @@ def test_nonfinite_scales(orc, entry, fmt, m, n, k):
         expect_nonfinite(y, yref, s, TAU_GEMM if entry == "gemm" else TAU_GEMV, planted, what)
 
 
+@pytest.mark.parametrize("m", [1, 3])
 @pytest.mark.parametrize("k", [1024, 2048, 8192])
 @pytest.mark.parametrize("which", ["gate", "up"])
-def test_nonfinite_scales_ffn_gate_up(orc, k, which):
+def test_nonfinite_scales_ffn_gate_up(orc, k, which, m):
     n = 300
-    what = f"ffn_gate_up_q4_0 N={n} K={k} with +-Inf/NaN scales in {which}"
+    what = f"ffn_gate_up_q4_0 M={m} N={n} K={k} with +-Inf/NaN scales in {which}"
     print(f"[nonfinite] {what}", flush=True)
-    x = synth.activations(1, k, seed=k)
+    x = synth.activations(m, k, seed=k)
     wg, wu = synth.q4_0_weights(n, k, seed=k + 1), synth.q4_0_weights(n, k, seed=k + 2)
     if which == "gate":
         wg, planted = plant("q4_0", wg, n, k, seed=k)
@@ -148,7 +149,7 @@ def test_nonfinite_scales_ffn_gate_up(orc, k, which):
         torch.cuda.synchronize()
         h = h.cpu().numpy()
         href = orc.ffn_gate_up(x, wg, wu, n, k)[0]
-    want = np.zeros((1, n), dtype=bool)
+    want = np.zeros((m, n), dtype=bool)
     want[:, planted] = True
     assert np.array_equal(~np.isfinite(href), want), f"{what}: oracle non-finite positions"
     assert np.array_equal(~np.isfinite(h), want), f"{what}: GPU non-finite positions"

@@ -421,10 +421,42 @@ def test_ffn_gate_up(orc, n, k):
                            f"{float(np.max(err / bound)):.3g}")
 
 
+# Two to four tokens: every launch branch of the gated table (K = 64 to
+# 16384, N >= 8192 with K = 8192), ragged N, M = 3 (four rows run, three stored)
+FFN_ROWS_SHAPES = [(2, 8192, 2048), (4, 8192, 2048), (4, 2048, 8192), (3, 1000, 256),
+                   (2, 333, 512), (3, 257, 1024), (4, 100, 4096), (3, 65, 16384),
+                   (2, 8200, 4352), (4, 300, 64), (3, 1, 256), (4, 9000, 8192)]
+
+
+@pytest.mark.parametrize("m,n,k", FFN_ROWS_SHAPES)
+def test_ffn_gate_up_rows(orc, m, n, k):
+    note(f"[parity] ffn_gate_up_q4_0 M={m} N={n} K={k}")
+    x = synth.activations(m, k, seed=m + n)
+    wg, wu = synth.q4_0_weights(n, k, seed=n + 2), synth.q4_0_weights(n, k, seed=n + 3)
+    h = run_ffn(x, wg, wu, n, k)
+    href, g, u, sg, su = orc.ffn_gate_up(x, wg, wu, n, k)
+    err = np.abs(h.astype(np.float64) - href)
+    bound = ffn_bound(g, u, sg, su, href)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{int(bad.sum())} outputs out of bound; worst err/bound "
+                           f"{float(np.max(err / bound)):.3g}")
+
+
+@pytest.mark.parametrize("m,n,k", [(2, 1000, 256), (3, 8192, 2048), (4, 2048, 8192),
+                                   (4, 65, 16384)])
+def test_ffn_gate_up_rows_match_single_row_bitwise(m, n, k):
+    x = synth.activations(m, k, seed=39)
+    wg, wu = synth.q4_0_weights(n, k, seed=39), synth.q4_0_weights(n, k, seed=40)
+    note(f"[bitwise] ffn_gate_up_q4_0 M={m} N={n} K={k} rows against M=1")
+    h = run_ffn(x, wg, wu, n, k)
+    for r in range(m):
+        assert np.array_equal(h[r], run_ffn(x[r:r + 1], wg, wu, n, k)[0]), r
+
+
 def test_ffn_gate_up_exact_cases(orc):
     n, k = 300, 1024
     rng = np.random.default_rng(17)
-    x = synth.activations(1, k, seed=17)
+    x = synth.activations(3, k, seed=17)
     d = pins.random_fp16(rng, (n, k // 32))
     wu = synth.pack_q4_0(d, rng.integers(0, 16, (n, k), dtype=np.uint8))
     note("[exact] ffn gate all-8 nibbles")

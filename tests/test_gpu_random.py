@@ -3,7 +3,7 @@ every entry point, each compared element by element with the f64 oracle.
 
 Case i draws, from numpy's generator seeded with i, an entry point and a
 shape: M from the entry point's range (GEMVs 1-16, GEMM 1-300, gated front
-half 1), N in 1..1200, K a multiple of 64 (Q4_K: of 256) up to
+half 1-4), N in 1..1200, K a multiple of 64 (Q4_K: of 256) up to
 4096, redrawn while M N K exceeds 2^24 so that the oracle stays fast; the
 weights and activations come from the seeded generators with seed i. The
 bound is the entry point's contract: 1e-4 sum_k |w x| for the GEMVs, 8e-3
@@ -51,7 +51,7 @@ def draw(i):
         elif entry.startswith("gemm"):
             m = int(rng.integers(1, 301))
         else:
-            m = 1
+            m = int(rng.integers(1, 5))
         n = int(rng.integers(1, 1201))
         step = 256 if fmt == "q4_k" else 64
         k = step * int(rng.integers(1, 4096 // step + 1))
