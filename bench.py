@@ -47,7 +47,10 @@ Timing:
     2048->16384 matrix, down 8192->2048) plus the vocabulary GEMV: the
     pages' 342 Q4_0 + 1 Q8_0 dispatches at mixed shapes;
   - decode_layer_replay_gated: the same, the gate/up dispatch running the
-    gated front half (qmm_ffn_gate_up_q4_0) instead.
+    gated front half (qmm_ffn_gate_up_q4_0) instead;
+  - decode_layer_replay_stacked: the gated one with q, k and v stored as one
+    3072 x 2048 matrix (they read the same x), so one GEMV replaces three:
+    four dispatches per layer, 229 per step.
 * clocks: the GPU's current shader and memory clock levels are read before
   and after the run (sysfs, else rocm-smi) and reported.
 
@@ -626,10 +629,11 @@ def main():
         rows["decode_step_replay"] = decode_step_replay(
             torch, hip, sh, ok, capture, time_graph, lib, x_up, x_dn, w_up, w_dn, up, down,
             xv, wv, voc, bytes_step, bv)
-        for gated in (False, True):
-            key = "decode_layer_replay_gated" if gated else "decode_layer_replay"
+        for key, gated, shapes in (("decode_layer_replay", False, LAYER_SHAPES),
+                                   ("decode_layer_replay_gated", True, LAYER_SHAPES),
+                                   ("decode_layer_replay_stacked", True, STACKED_SHAPES)):
             rows[key] = decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph,
-                                            lib, pool, xv, wv, voc, bv, gated)
+                                            lib, pool, xv, wv, voc, bv, gated, shapes)
         t_step = 171 * pair_us + rows["q8_0_gemv_vocab"]["mean_us"]
         rows["decode_tok_s_equiv"] = 1e6 / t_step
         gemm_ref = library_gemm_reference(xp, pre["M"], pre["N"], pre["K"], args.settle_ms)
@@ -767,12 +771,16 @@ def decode_step_replay(torch, hip, sh, ok, capture, time_graph, lib, x_up, x_dn,
 # the pages' 342 Q4_0 dispatches per decode step.
 LAYER_SHAPES = (("q", 2048, 2048), ("k", 2048, 512), ("v", 2048, 512), ("o", 2048, 2048),
                 ("gate_up", 2048, 16384), ("down", 8192, 2048))
+# The same layer with q, k and v stored as one matrix (rows of q, then k,
+# then v): the caller's layout choice that turns three launches into one.
+STACKED_SHAPES = (("qkv", 2048, 3072), ("o", 2048, 2048), ("gate_up", 2048, 16384),
+                  ("down", 8192, 2048))
 LAYERS = 57
 
 
 def decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph, lib, pool, xv, wv, voc,
-                        bv, gated):
-    """LAYERS decoder layers (LAYER_SHAPES, each layer with its own weights)
+                        bv, gated, shapes):
+    """LAYERS decoder layers (`shapes`, each layer with its own weights)
     then the Q8_0 vocabulary GEMV, in one HIP graph; with `gated` the
     gate/up dispatch is the gated front half (h = gelu_tanh(gate) * up,
     8192 outputs) instead of one 16384-row GEMV. Outputs are compared
@@ -780,12 +788,12 @@ def decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph, lib, poo
     xs = {k: torch.from_numpy(synth.activations(1, k, seed=k + 7)).to(dev) for k in (2048, 8192)}
     weights, outs, calls = {}, [], []
     byts = 0
-    for name, k, n_ in LAYER_SHAPES:
+    for name, k, n_ in shapes:
         wh = synth.q4_0_weights(n_, k, seed=n_ + 3)
         weights[name] = pool(wh, min_copies=LAYERS, bytes_target=0)
-    row_bytes = {name: k // 32 * 18 for name, k, _ in LAYER_SHAPES}
+    row_bytes = {name: k // 32 * 18 for name, k, _ in shapes}
     for layer in range(LAYERS):
-        for name, k, n_ in LAYER_SHAPES:
+        for name, k, n_ in shapes:
             w_ = weights[name][layer]
             if name == "gate_up" and gated:
                 h = torch.empty((1, n_ // 2), device=dev)
@@ -818,12 +826,13 @@ def decode_layer_replay(torch, np, synth, dev, ok, capture, time_graph, lib, poo
     td = time_graph(g, 1)
     bitwise = all(torch.equal(a, b) for a, b in zip(outs, eager))
     del g
-    name = "decode layer replay (gated front half)" if gated else "decode layer replay"
+    name = "decode layer replay" + (" (gated front half)" if gated else "") + (
+        ", q/k/v stacked" if shapes is STACKED_SHAPES else "")
     log(f"[bench] {name}, {len(calls)} GEMVs: {td['mean_us']:.1f} us, "
         f"{1e6 / td['mean_us']:.0f} tok/s, bitwise vs eager: {bitwise}")
     del weights
     return dict(td, dispatches=len(calls), layers=LAYERS,
-                layer_shapes=[list(s) for s in LAYER_SHAPES], gated_front_half=gated,
+                layer_shapes=[list(s) for s in shapes], gated_front_half=gated,
                 bytes=byts, gbs=byts / (td["mean_us"] * 1e-6) / 1e9,
                 tokens_per_s=1e6 / td["mean_us"], bitwise_vs_eager=bitwise)
 
