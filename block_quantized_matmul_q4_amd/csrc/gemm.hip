@@ -488,7 +488,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
 }
 
 // Medium M: few output tiles, so instead of one tile's K loop per compute
-// unit, a workgroup owns a 32-column slice of y for a band of 32 MT rows
+// unit, a workgroup owns a 32 NT-column slice of y for a band of 32 MT rows
 // (grid: column slices x row bands) and its WAVES waves take interleaved K
 // steps of 64 in parallel (wave w: steps w, w + WAVES, ...), each with its
 // own accumulators, meeting in LDS at the end (summed in wave order). Same
@@ -500,20 +500,23 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(
 // ordering of its LDS writes before its reads (wave_lds_sync).
 //
 // Per step a wave loads its activation rows (16 lanes per row, a float4
-// each) and one weight block per lane (row lane / 2 of the slice, block
-// lane % 2 of the pair), converts both into its own LDS region, then runs
-// MT 32x32x16 MFMAs per 16-wide substep; the next step's loads are issued
-// before this step's matrix-core work. Rows past M and columns past N load
-// zeros through the buffer resources' range checks and are not stored.
-template <int FMT, int MT, int WAVES>
+// each) and NT weight blocks per lane (rows lane / 2 + 32 j of the slice,
+// block lane % 2 of the pair), converts both into its own LDS region, then
+// runs MT x NT 32x32x16 MFMAs per 16-wide substep; the next step's loads are
+// issued before this step's matrix-core work. Rows past M and columns past
+// N load zeros through the buffer resources' range checks and are not
+// stored. Every workgroup reads all of its activation band, so the band is
+// re-read once per column slice: wider slices (NT = 2) halve that L2
+// traffic where there are enough of them to fill the chip.
+template <int FMT, int MT, int NT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
     int M, int N, int K)
 {
-    constexpr int BM = 32 * MT, BN = 32;
+    constexpr int BM = 32 * MT, BN = 32 * NT;
     constexpr int AF4 = BM / 4;                         // activation float4 per lane
     constexpr int REGION = (BM + BN) * LDK;             // bf16 per wave
-    static_assert(MT * 1024 * 4 <= REGION * 2, "wave partials fit the wave's region");
+    static_assert(MT * NT * 1024 * 4 <= REGION * 2, "wave partials fit the wave's region");
     __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
 
     using BF = BFmt<FMT>;
@@ -536,12 +539,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
     // activation row lane / 16 + 4 u, columns 4 (lane % 16) .. +3 of the step
     const int a_col = 4 * (lane % 16);
     const int a_voff0 = ((lane / 16) * K + a_col) * 4;
-    // weight row lane / 2 of the slice, block lane % 2 of the step's pair
+    // weight rows lane / 2 + 32 j of the slice, block lane % 2 of the step's pair
     const int b_row = lane / 2, b_blk = lane % 2;
     const int b_roff = b_row * row_bytes;
 
     float4 a_reg[AF4];
-    uint32_t b_reg[BF::kWin];
+    uint32_t b_reg[NT][BF::kWin];
     auto load = [&](int p) {
 #pragma unroll
         for (int u = 0; u < AF4; ++u) {
@@ -549,14 +552,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
                 a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
-        BF::load_step(b_rsrc, b_roff, b_blk, p, b_reg);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            BF::load_step(b_rsrc, b_roff + 32 * j * row_bytes, b_blk, p, b_reg[j]);
     };
 
-    f32x16 acc[MT];
+    f32x16 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int frow = lane % 32, fk = 8 * (lane / 32);
     // a wave without steps (P < WAVES) loads the last step and never uses it
@@ -571,49 +578,59 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mid_kernel(
             *reinterpret_cast<uint2 *>(&As[(lane / 16 + 4 * u) * LDK + a_col]) = pk;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            BF::convert_quarter(b_reg, b_blk, q, &Bs[b_row * LDK + 32 * b_blk]);
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                BF::convert_quarter(b_reg[j], b_blk, q, &Bs[(b_row + 32 * j) * LDK + 32 * b_blk]);
         load(min(p + WAVES, P - 1));            // registers are free again
         wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[frow * LDK + fk + 16 * s]);
+            bf16x8 b[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(32 * j + frow) * LDK + fk + 16 * s]);
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
                     &As[(32 * i + frow) * LDK + fk + 16 * s]);
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
             }
         }
         wave_lds_sync();                        // fragments read before the next writes
     }
 
-    // partials: red[wave][i][e][lane] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][lane % 32]
+    // partials: red[wave][i][j][e][lane] = C[32 i + 8 (e / 4) + 4 (lane / 32) + e % 4][32 j + lane % 32]
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[((wave * MT + i) * 16 + e) * 64 + lane] = acc[i][e];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                red[(((wave * MT + i) * NT + j) * 16 + e) * 64 + lane] = acc[i][j][e];
     __syncthreads();
-    for (int o = threadIdx.x; o < MT * 16 * 64; o += 64 * WAVES) {
-        const int l = o % 64, e = (o / 64) % 16, i = o / 1024;
+    for (int o = threadIdx.x; o < MT * NT * 16 * 64; o += 64 * WAVES) {
+        const int l = o % 64, e = (o / 64) % 16, j = (o / 1024) % NT, i = o / (1024 * NT);
         const int r = 32 * i + 8 * (e / 4) + 4 * (l / 32) + e % 4;
-        const int n = n0 + l % 32;
+        const int n = n0 + 32 * j + l % 32;
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < WAVES; ++q) s += red[((q * MT + i) * 16 + e) * 64 + l];
+        for (int q = 0; q < WAVES; ++q) s += red[(((q * MT + i) * NT + j) * 16 + e) * 64 + l];
         if (r < rows && n < N) y[(int64_t)(m0 + r) * N + n] = s;
     }
 }
 
-template <int FMT, int MT, int WAVES>
+template <int FMT, int MT, int NT, int WAVES>
 hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_mid_kernel<FMT, MT, WAVES>),
-                       dim3((N + 31) / 32, (M + 32 * MT - 1) / (32 * MT)), dim3(64 * WAVES), 0,
-                       stream, x, w, y, M, N, K);
+    hipLaunchKernelGGL((gemm_mid_kernel<FMT, MT, NT, WAVES>),
+                       dim3((N + 32 * NT - 1) / (32 * NT), (M + 32 * MT - 1) / (32 * MT)),
+                       dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
     return hipGetLastError();
 }
 
@@ -754,24 +771,56 @@ hipError_t launch_tiles(const float *x, const uint8_t *w, float *y, int M, int N
 // 128 x 128 tile (4 x as many workgroups) keeps more of the chip busy.
 constexpr int64_t kComputeUnits = 256;
 
-// Up to kMidRowsMax rows the medium-M kernel: 64-row bands when there are
-// at least 128 column slices (N >= 4096), else 32-row bands for more
-// workgroups (timing sweeps at K = 2048 .. 8192: M = 16, N = 8192 7.3 us and
-// M = 128, N = 2048, K = 8192 22.5 us, against 23 and 88 us on tiles).
+// Up to kMidRowsMax rows the medium-M kernel (timing sweeps at K = 1024 ..
+// 8192: M = 16, N = 8192 7.3 us and M = 128, N = 2048, K = 8192 22.5 us,
+// against 23 and 88 us on tiles). Each workgroup's K loop is short and
+// latency-bound, so the shape that runs best is the one whose workgroups
+// all fit the chip at once: from N = 4096 the launch takes, among 32- or
+// 64-row bands and 32- or 64-column slices, the one with the most
+// workgroups not above the compute unit count (on a tie the wider slices,
+// which re-read the activation band fewer times, then the narrower bands,
+// which compute fewer rows past M), and when every shape has more, 64 x 64
+// tiles with 4 waves (two workgroups per compute unit).
+// Against the former 64 x 32 / 32 x 32 choice: M = 128, N = 8192 20.4 ->
+// 16.3 us; M = 40, N = 4096 11.1 -> 7.2 us; M = 128, N = 16384 39.9 -> 24.6
+// us; M = 64, N = 8192 12.4 -> 11.8 us.
 constexpr int kMidRowsMax = 128;
+
+template <int FMT>
+hipError_t launch_mid_auto(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                           hipStream_t stream)
+{
+    // few column slices: 16 waves keep more K steps in flight per slice
+    // (N = 2048, K = 8192: M = 16 17.0 against 17.9 us, M = 64 18.3 against
+    // 19.4)
+    if (N < 4096) return launch_mid<FMT, 1, 1, 16>(x, w, y, M, N, K, stream);
+    int best = -1;
+    int64_t best_wg = 0;
+    for (int c = 0; c < 4; ++c) {
+        const int mt = 1 + (c & 1), nt = 1 + (c >> 1);
+        const int64_t wg = (int64_t)((N + 32 * nt - 1) / (32 * nt)) * ((M + 32 * mt - 1) / (32 * mt));
+        if (wg > kComputeUnits) continue;
+        const int bnt = 1 + (best >> 1), bmt = 1 + (best & 1);
+        if (best < 0 || wg > best_wg ||
+            (wg == best_wg && (nt > bnt || (nt == bnt && mt < bmt)))) {
+            best = c;
+            best_wg = wg;
+        }
+    }
+    switch (best) {
+    case 0: return launch_mid<FMT, 1, 1, 8>(x, w, y, M, N, K, stream);
+    case 1: return launch_mid<FMT, 2, 1, 8>(x, w, y, M, N, K, stream);
+    case 2: return launch_mid<FMT, 1, 2, 8>(x, w, y, M, N, K, stream);
+    case 3: return launch_mid<FMT, 2, 2, 8>(x, w, y, M, N, K, stream);
+    default: return launch_mid<FMT, 2, 2, 4>(x, w, y, M, N, K, stream);
+    }
+}
 
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
-    if (M <= kMidRowsMax) {
-        if (M > 32 && N >= 4096) return launch_mid<FMT, 2, 8>(x, w, y, M, N, K, stream);
-        // few column slices: 16 waves keep more K steps in flight per slice
-        // (N = 2048, K = 8192: M = 16 17.0 against 17.9 us, M = 64 18.3
-        // against 19.4)
-        if (N < 4096) return launch_mid<FMT, 1, 16>(x, w, y, M, N, K, stream);
-        return launch_mid<FMT, 1, 8>(x, w, y, M, N, K, stream);
-    }
+    if (M <= kMidRowsMax) return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);
     const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (large_tiles < kComputeUnits)
         return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);

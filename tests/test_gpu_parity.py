@@ -199,7 +199,12 @@ GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                # K a multiple of 64 but not of 256: odd step counts on the
                # tile kernels (15, 17, 1), medium M, GEMV routing
                (300, 300, 960), (1000, 520, 1088), (2100, 4100, 1088), (129, 257, 64),
-               (40, 8192, 896), (3, 100, 320)]
+               (40, 8192, 896), (3, 100, 320),
+               # medium M from N = 4096, one shape per launch choice: 32 x 32,
+               # 64 x 32, 32 x 64 and 64 x 64 (8 waves) and 64 x 64 with 4
+               # waves (more than 256 workgroups in every shape), ragged edges
+               (20, 5000, 512), (70, 4090, 512), (64, 4100, 1024), (80, 8150, 512),
+               (100, 8193, 2048)]
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
@@ -237,6 +242,25 @@ def test_gemm_max_k_large_tiles_sampled(orc, fmt):
     rng = np.random.default_rng(5)
     ms = np.concatenate([[0, m - 1, 0, m - 1, 255, 256], rng.integers(0, m, 58)])
     ns = np.concatenate([[0, n - 1, n - 1, 0, 256, 255], rng.integers(0, n, 58)])
+    yref, s = orc.matmul_at(fmt, x, w, n, k, ms, ns)
+    assert_parity(y[ms, ns], yref, s, TAU_GEMM, what)
+
+
+# the medium-M kernel's 64-column slices (8 and 4 waves) at the largest K,
+# on sampled outputs (corners included)
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k"])
+@pytest.mark.parametrize("m,n", [(80, 8150), (100, 8193)])
+def test_gemm_mid_max_k_sampled(orc, fmt, m, n):
+    k = 65536
+    what = f"gemm_{fmt} M={m} N={n} K={k} seed=6 (sampled)"
+    note(f"[parity] {what}")
+    x = synth.activations(m, k, seed=6)
+    w = weights(fmt, n, k, seed=6)
+    y = run("gemm", fmt, x, w, n, k)
+    assert np.all(np.isfinite(y)), what
+    rng = np.random.default_rng(6)
+    ms = np.concatenate([[0, m - 1, 0, m - 1, 63, 64], rng.integers(0, m, 58)])
+    ns = np.concatenate([[0, n - 1, n - 1, 0, 63, 64], rng.integers(0, n, 58)])
     yref, s = orc.matmul_at(fmt, x, w, n, k, ms, ns)
     assert_parity(y[ms, ns], yref, s, TAU_GEMM, what)
 
@@ -475,7 +499,9 @@ def test_ffn_gate_up_exact_cases(orc):
                                              ("gemv", "q4_0", 8, 8192, 2048),
                                              ("gemv", "q8_0", 1, 4096, 2048),
                                              ("gemm", "q4_0", 512, 1024, 2048),
-                                             ("gemm", "q8_0", 300, 700, 1024)])
+                                             ("gemm", "q8_0", 300, 700, 1024),
+                                             ("gemm", "q4_0", 80, 8150, 512),
+                                             ("gemm", "q4_0", 100, 8193, 512)])
 def test_bitwise_repeatable(entry, fmt, m, n, k):
     x = synth.activations(m, k, seed=21)
     w = weights(fmt, n, k, seed=21)
@@ -729,6 +755,8 @@ Q4_K_GEMM_SHAPES = [
     (2, 300, 512), (4, 1000, 2048), (5, 257, 768), (33, 4097, 1024), (64, 8192, 2048),
     (128, 2049, 8192), (130, 257, 512), (300, 700, 1280), (1000, 2048, 8192),
     (512, 1024, 2048), (257, 8193, 256),
+    # the medium-M launch choices from N = 4096 (as for Q4_0)
+    (20, 5000, 512), (70, 4090, 512), (80, 8150, 512), (100, 8193, 1024),
 ]
 
 
