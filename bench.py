@@ -562,7 +562,7 @@ def main():
         add_row("q4_0_gemm_prefill", lib.qmm_gemm_q4_0,
                 gemv_args(xp, w_up, yp, pre["M"], pre["N"], pre["K"], ng),
                 flops=fp, tokens=pre["M"])
-        for ms in (16, 64, 128):
+        for ms in (16, 64, 128, 256):
             xs = torch.from_numpy(synth.activations(ms, pre["K"])).to(dev)
             ys_ = torch.empty((ms, pre["N"]), device=dev)
             keep += [xs, ys_]

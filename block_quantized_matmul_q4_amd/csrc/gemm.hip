@@ -1,5 +1,5 @@
 // Matrix-core kernels over GGUF Q4_0 / Q8_0 weights: the prefill GEMM's
-// tile kernel (described here), the medium-M GEMM (5-128 rows) and the
+// tile kernel (described here), the medium-M GEMM (5-128 rows, and few-tile shapes above) and the
 // weight-slice GEMV to the f32 bound (9-16 rows), each introduced where it starts.
 //
 // Prefill GEMM over GGUF Q4_0 or Q8_0 weights on the bf16 matrix cores:
@@ -816,15 +816,24 @@ hipError_t launch_mid_auto(const float *x, const uint8_t *w, float *y, int M, in
     }
 }
 
+// More rows take the tile kernels: 256 x 256 tiles when there are at least
+// as many as compute units, else 128 x 128 ones. With at most 128 of those
+// (half the chip, each running the whole K loop) and N >= 4096 the
+// medium-M kernel's 64 x 64 tiles are faster (sweep at M = 160-768: N =
+// 8192, K = 2048, M = 160 26.0 -> 21.2 us; N = 4096, K = 4096, M = 256 46.9
+// -> 25.3 us, M = 512 47.7 -> 42.2 us; the tile kernel wins from 192 small
+// tiles on, e.g. N = 8192, M = 384 27.0 against 35.4 us).
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
     if (M <= kMidRowsMax) return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);
     const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (large_tiles < kComputeUnits)
-        return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);
-    return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
+    if (large_tiles >= kComputeUnits) return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
+    const int64_t small_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (N >= 4096 && small_tiles <= kComputeUnits / 2)
+        return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);
+    return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);
 }
 
 }  // namespace

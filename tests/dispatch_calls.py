@@ -51,7 +51,7 @@ CASES = [
     ("gemm_q4_0", 300, 300, 512), ("gemm_q4_0", 2048, 8192, 2048),
     ("gemm_q8_0", 2, 300, 1024), ("gemm_q8_0", 64, 4100, 1024), ("gemm_q8_0", 2048, 8192, 512),
     ("gemm_q4_0", 20, 5000, 512), ("gemm_q4_0", 70, 4090, 512), ("gemm_q4_0", 80, 8150, 512),
-    ("gemm_q4_0", 100, 8193, 512),
+    ("gemm_q4_0", 100, 8193, 512), ("gemm_q4_0", 200, 8150, 512),
     ("gemv_q4_k", 1, 8192, 2048), ("gemv_q4_k", 2, 300, 8192), ("gemv_q4_k", 4, 300, 1024),
     ("gemv_q4_k", 5, 300, 1024), ("gemv_q4_k", 8, 65536, 512), ("gemv_q4_k", 16, 8192, 2048),
     ("gemm_q4_k", 3, 300, 1024), ("gemm_q4_k", 40, 300, 1024), ("gemm_q4_k", 2048, 8192, 2048),

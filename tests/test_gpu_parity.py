@@ -204,7 +204,10 @@ GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                # 64 x 32, 32 x 64 and 64 x 64 (8 waves) and 64 x 64 with 4
                # waves (more than 256 workgroups in every shape), ragged edges
                (20, 5000, 512), (70, 4090, 512), (64, 4100, 1024), (80, 8150, 512),
-               (100, 8193, 2048)]
+               (100, 8193, 2048),
+               # more than 128 rows over at most 128 tiles of 128 x 128 (the
+               # medium-M kernel's 64 x 64 tiles, 8 and 4 waves)
+               (160, 4096, 1024), (200, 8150, 512), (300, 4100, 1024)]
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
@@ -756,7 +759,7 @@ Q4_K_GEMM_SHAPES = [
     (128, 2049, 8192), (130, 257, 512), (300, 700, 1280), (1000, 2048, 8192),
     (512, 1024, 2048), (257, 8193, 256),
     # the medium-M launch choices from N = 4096 (as for Q4_0)
-    (20, 5000, 512), (70, 4090, 512), (80, 8150, 512), (100, 8193, 1024),
+    (20, 5000, 512), (70, 4090, 512), (80, 8150, 512), (100, 8193, 1024), (200, 8150, 512),
 ]
 
 
