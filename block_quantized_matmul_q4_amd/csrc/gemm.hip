@@ -156,6 +156,7 @@ template <> struct BFmt<FMT_Q4_0> {
     {
         return half_lo(b[0] >> (16 * blk));
     }
+    static constexpr bool kHasMin = false;
 };
 
 template <> struct BFmt<FMT_Q8_0> {
@@ -218,6 +219,7 @@ template <> struct BFmt<FMT_Q8_0> {
     {
         return half_lo(b[0] >> (16 * blk));
     }
+    static constexpr bool kHasMin = false;
 };
 
 // Q4_K super-blocks (256 weights in 144 bytes: fp16 d and dmin, 6-bit
@@ -250,23 +252,30 @@ template <> struct BFmt<FMT_Q4_K> {
     // formats), one 16-byte LDS store. Callers convert a window's quarters in
     // order 0..3: the even quarter unpacks its sub-block's scale and minimum
     // into b[9], b[10] and the odd one reuses them.
+    // d sc and dmin mn of sub-block 2c + h of the window's quarter c (both
+    // products exact in f32)
+    __device__ static void sub_scales(const uint32_t (&b)[kWin], int h, float &dsc, float &dmn)
+    {
+        // c is the same across the wave; hidden from the compiler, the
+        // choices below stay per-lane selects instead of becoming
+        // branches that would split the K step into many basic blocks
+        int c = (int)b[8];
+        asm("" : "+v"(c));
+        const int sh = 8 * (2 * (c & 1) + h);
+        const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
+        const uint32_t x2 = (b[3] >> sh) & 0xFFu;
+        const uint32_t sc = c < 2 ? (x0 & 63u) : ((x2 & 15u) | ((x0 >> 6) << 4));
+        const uint32_t mn = c < 2 ? (x1 & 63u) : ((x2 >> 4) | ((x1 >> 6) << 4));
+        dsc = half_lo(b[0]) * (float)sc;
+        dmn = half_hi(b[0]) * (float)mn;
+    }
+
     __device__ static void convert_quarter(uint32_t (&b)[kWin], int blk, int q, __bf16 *dst)
     {
         const int h = q / 2, qq = q % 2;
         float dsc, dmn;
         if (qq == 0) {
-            // c is the same across the wave; hidden from the compiler, the
-            // choices below stay per-lane selects instead of becoming
-            // branches that would split the K step into many basic blocks
-            int c = (int)b[8];
-            asm("" : "+v"(c));
-            const int sh = 8 * (2 * (c & 1) + h);
-            const uint32_t x0 = (b[1] >> sh) & 0xFFu, x1 = (b[2] >> sh) & 0xFFu;
-            const uint32_t x2 = (b[3] >> sh) & 0xFFu;
-            const uint32_t sc = c < 2 ? (x0 & 63u) : ((x2 & 15u) | ((x0 >> 6) << 4));
-            const uint32_t mn = c < 2 ? (x1 & 63u) : ((x2 >> 4) | ((x1 >> 6) << 4));
-            dsc = half_lo(b[0]) * (float)sc;
-            dmn = half_hi(b[0]) * (float)mn;
+            sub_scales(b, h, dsc, dmn);
             b[9] = __float_as_uint(dsc);
             b[10] = __float_as_uint(dmn);
         } else {
@@ -286,6 +295,26 @@ template <> struct BFmt<FMT_Q4_K> {
                                    fmaf(dsc, (float)((nib >> 8) & 0xFFu), -dmn));
             o[2 * t + 1] = pack_bf16x2(fmaf(dsc, (float)((nib >> 16) & 0xFFu), -dmn),
                                        fmaf(dsc, (float)(nib >> 24), -dmn));
+        }
+        *reinterpret_cast<uint4 *>(dst - 32 * blk + 32 * h + 16 * blk + 8 * qq) = v;
+    }
+
+    // The same quarter as the nibbles q (0..15, exact in bf16), for products
+    // kept exact; the sub-block's d sc and dmin mn are applied afterwards.
+    static constexpr float kCodeScale = 1.0f;
+    static constexpr bool kHasMin = true;
+    __device__ static void codes_quarter(const uint32_t (&b)[kWin], int blk, int q, __bf16 *dst)
+    {
+        const int h = q / 2, qq = q % 2;
+        uint4 v;
+        uint32_t *o = &v.x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t raw = b[4 + 2 * qq + t];
+            uint32_t nib = h ? (raw >> 4) & 0x0F0F0F0Fu : raw & 0x0F0F0F0Fu;
+            asm("" : "+v"(nib));
+            o[2 * t] = pack_bf16x2((float)(nib & 0xFFu), (float)((nib >> 8) & 0xFFu));
+            o[2 * t + 1] = pack_bf16x2((float)((nib >> 16) & 0xFFu), (float)(nib >> 24));
         }
         *reinterpret_cast<uint4 *>(dst - 32 * blk + 32 * h + 16 * blk + 8 * qq) = v;
     }
@@ -642,17 +671,22 @@ hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, 
 // tile that is scaled by the block's fp16 d in f32 before it is added to
 // the accumulators. The split represents x to within 2^-17 |x| and each
 // code-term product is exact; y[m] = (C[m] + C[m + 16]) x the codes' scale.
+// Q4_K: a block is a 32-weight sub-block, the codes are its nibbles, the
+// scale is d sc, and dmin mn times the sum of the block's activations (two
+// more MFMAs of the same A operand against a B operand of ones) is
+// subtracted in f32.
 template <int FMT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
     int M, int N, int K)
 {
+    using BF = BFmt<FMT>;
     constexpr int BM = 32, BN = 32;
-    constexpr int REGION = (BM + BN) * LDK + 2 * BN * 2;   // bf16: A, B, then 64 f32 scales
+    constexpr int SC = BF::kHasMin ? 4 : 2;                 // f32 scales per weight row
+    constexpr int REGION = (BM + BN) * LDK + 2 * BN * SC;   // bf16: A, B, then the scales
     static_assert(1024 * 4 <= REGION * 2, "wave partials fit the wave's region");
     __shared__ __attribute__((aligned(16))) __bf16 lds[WAVES * REGION];
 
-    using BF = BFmt<FMT>;
     // the wave index is the same on every lane; read from one lane, the
     // compiler knows it (and the K steps derived from it) to be uniform, so
     // the buffer loads' scalar offsets need no per-lane loop
@@ -662,7 +696,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     const int row_bytes = P * BF::kPairBytes;
     __bf16 *As = lds + wave * REGION;
     __bf16 *Bs = As + BM * LDK;
-    float *ds = reinterpret_cast<float *>(Bs + BN * LDK);  // [BN][2]
+    float *ds = reinterpret_cast<float *>(Bs + BN * LDK);  // [BN][SC]: scales, then offsets
 
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(x), 0, M * K * 4, kBufferWord3);
@@ -673,7 +707,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     const int a_col = 4 * (lane % 16);
     const int a_voff0 = ((lane / 16) * K + a_col) * 4;
     const int b_row = lane / 2, b_blk = lane % 2;
-    const int b_voff = b_row * row_bytes + BF::kWinStride * b_blk;
+    const int b_roff = b_row * row_bytes;
 
     float4 a_reg[4];
     uint32_t b_reg[BF::kWin];
@@ -684,13 +718,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
                 a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
-        BF::load(b_rsrc, b_voff, p * BF::kPairBytes, b_reg);
+        BF::load_step(b_rsrc, b_roff, b_blk, p, b_reg);
     };
 
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
     const f32x16 zero = acc;
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
     const int frow = lane % 32, fk = 8 * (lane / 32);
     load(min(wave, P - 1));
@@ -710,21 +747,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             BF::codes_quarter(b_reg, b_blk, q, &Bs[b_row * LDK + 32 * b_blk]);
-        ds[2 * b_row + b_blk] = BF::scale(b_reg, b_blk);
+        if constexpr (BF::kHasMin) {
+            // the lane with b_blk holds the header: sub-block 2c + b_blk
+            float dsc, dmn;
+            BF::sub_scales(b_reg, b_blk, dsc, dmn);
+            ds[SC * b_row + b_blk] = dsc;
+            ds[SC * b_row + 2 + b_blk] = dmn;
+        } else {
+            ds[SC * b_row + b_blk] = BF::scale(b_reg, b_blk);
+        }
         load(min(p + WAVES, P - 1));            // registers are free again
         wave_lds_sync();
-        const float d0 = ds[2 * frow], d1 = ds[2 * frow + 1];
+        const float d0 = ds[SC * frow], d1 = ds[SC * frow + 1];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            f32x16 c = zero;
+            f32x16 c = zero, xs = zero;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int s = 2 * blk + s2;
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[frow * LDK + fk + 16 * s]);
                 const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[frow * LDK + fk + 16 * s]);
                 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+                if constexpr (BF::kHasMin)
+                    xs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ones, xs, 0, 0, 0);
             }
             const float d = blk ? d1 : d0;
+            if constexpr (BF::kHasMin) {
+                const float dm = ds[SC * frow + 2 + blk];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[e] = fmaf(-dm, xs[e], acc[e]);
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[e] = fmaf(d, c[e], acc[e]);
         }
@@ -841,12 +893,15 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream)
 {
-    if (M > 16 || fmt == FMT_Q4_K) return hipErrorInvalidValue;
+    if (M > 16) return hipErrorInvalidValue;
     const dim3 grid((N + 31) / 32);
     // Q4_0: 16 waves (more K steps in flight per slice: M = 16, N = 2048,
     // K = 8192 20.3 us against 22.0 with 8); Q8_0: 8 (its wider windows)
     if (fmt == FMT_Q4_0)
         hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 16>), grid, dim3(1024), 0, stream, x, w,
+                           y, M, N, K);
+    else if (fmt == FMT_Q4_K)
+        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_K, 16>), grid, dim3(1024), 0, stream, x, w,
                            y, M, N, K);
     else
         hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q8_0, 8>), grid, dim3(512), 0, stream, x, w, y,

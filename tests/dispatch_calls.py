@@ -34,7 +34,7 @@ ROUTES = {
     "gemv_q4_0": GEMV, "gemv_q8_0": GEMV,
     "gemm_q4_0": ("gemv_m1_kernel", "gemm_kernel", "gemm_mid_kernel"),
     "gemm_q8_0": ("gemv_m1_kernel", "gemm_kernel", "gemm_mid_kernel"),
-    "gemv_q4_k": ("gemv_q4_k_kernel", "gemv_small_m_kernel"),
+    "gemv_q4_k": ("gemv_q4_k_kernel", "gemv_small_m_kernel", "gemv_slice_kernel"),
     "gemm_q4_k": ("gemv_q4_k_kernel", "gemm_kernel", "gemm_mid_kernel"),
     "ffn_gate_up_q4_0": ("gemv_m1_kernel",),
 }
@@ -54,6 +54,7 @@ CASES = [
     ("gemm_q4_0", 100, 8193, 512), ("gemm_q4_0", 200, 8150, 512),
     ("gemv_q4_k", 1, 8192, 2048), ("gemv_q4_k", 2, 300, 8192), ("gemv_q4_k", 4, 300, 1024),
     ("gemv_q4_k", 5, 300, 1024), ("gemv_q4_k", 8, 65536, 512), ("gemv_q4_k", 16, 8192, 2048),
+    ("gemv_q4_k", 12, 4096, 1024),
     ("gemm_q4_k", 3, 300, 1024), ("gemm_q4_k", 40, 300, 1024), ("gemm_q4_k", 2048, 8192, 2048),
     ("ffn_gate_up_q4_0", 1, 8192, 2048), ("ffn_gate_up_q4_0", 1, 2048, 8192),
     ("ffn_gate_up_q4_0", 2, 8192, 2048), ("ffn_gate_up_q4_0", 4, 2048, 8192),

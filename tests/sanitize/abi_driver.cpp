@@ -137,6 +137,8 @@ void q4_k_gemv()
     for (int64_t m = 1; m <= 4; ++m) routed(qmm_gemv_q4_k, m, 300, 1280, "gemv_q4_k");
     for (int64_t m = 5; m <= QMM_GEMV_MAX_M; ++m) routed(qmm_gemv_q4_k, m, 300, 1280, "gemv_small_m");
     routed(qmm_gemv_q4_k, 16, 33, QMM_MAX_K, "gemv_small_m");
+    routed(qmm_gemv_q4_k, 8, 8192, 2048, "gemv_small_m");
+    for (int64_t m = 9; m <= QMM_GEMV_MAX_M; ++m) routed(qmm_gemv_q4_k, m, 8192, 2048, "gemv_slices");
 }
 
 int gate_up(uintptr_t x, uintptr_t wg, uintptr_t wu, uintptr_t h, int64_t M, int64_t N,

@@ -106,9 +106,11 @@ CASES = [
     ("gemm", "q8_0", 20, 300, 1024), ("gemm", "q8_0", 300, 300, 512),
     # medium M with 64-column slices (8 and 4 waves)
     ("gemm", "q4_0", 80, 8150, 256), ("gemm", "q8_0", 100, 8193, 256),
-    # Q4_K: GEMV (1 and 3 rows; 8 and 12 on the matrix cores), medium M and tiles
+    # Q4_K: GEMV (1 and 3 rows; 8 and 12 rows on the small-M kernel, 12 on the
+    # weight slices from N = 8192), medium M and tiles
     ("gemv", "q4_k", 1, 300, 2048), ("gemv", "q4_k", 3, 300, 1024),
     ("gemv", "q4_k", 8, 300, 1024), ("gemv", "q4_k", 12, 8200, 512),
+    ("gemv", "q4_k", 12, 4000, 512),
     ("gemm", "q4_k", 20, 300, 1024), ("gemm", "q4_k", 300, 300, 512),
     ("gemm", "q4_k", 80, 8150, 512),
 ]

@@ -690,15 +690,17 @@ def test_gemv_q4_k_rows_match_single_row_bitwise(m, n, k):
         assert np.array_equal(y[r], run("gemv", "q4_k", x[r:r + 1], w, n, k)[0]), r
 
 
-# Five to sixteen activation rows (matrix-core kernel): every launch branch
-# (N >= 65536 with M <= 8; N < 8192 with hi/lo packed (M <= 8) and apart;
-# wider N packed and apart), ragged N, one pass (K = 256) and the largest K.
-# The contract's bound scale is sum_k (|d sc q| + |dmin mn|) |x|; on these
-# seeded weights the error also stays within 1e-4 sum_k |x w|.
+# Five to sixteen activation rows (matrix-core kernels): every launch branch
+# of the small-M kernel (N >= 65536 with M <= 8; N < 8192 with hi/lo packed
+# (M <= 8) and apart) and the 32-row weight slices (9-16 rows from N =
+# 8192), ragged N, one pass (K = 256) and the largest K. The contract's
+# bound scale is sum_k (|d sc q| + |dmin mn|) |x|; on these seeded weights
+# the error also stays within 1e-4 sum_k |x w|.
 Q4_K_MANY_ROWS_SHAPES = [
     (5, 300, 1024), (6, 8192, 2048), (8, 2048, 8192), (7, 65539, 512), (8, 65536, 256),
     (9, 8192, 2048), (12, 2049, 4352), (16, 8192, 2048), (16, 2048, 8192), (13, 17, 256),
     (16, 50, 65536), (11, 4099, 8448), (5, 1, 256), (10, 9000, 1024), (14, 65537, 256),
+    (16, 8200, 65536), (9, 8193, 256), (12, 12000, 1280),
 ]
 
 
@@ -718,7 +720,7 @@ def test_gemv_q4_k_many_rows(orc, m, n, k):
 
 
 @pytest.mark.parametrize("m,n", [(5, 300), (8, 300), (9, 300), (16, 300), (8, 8192),
-                                 (16, 8192)])
+                                 (16, 8192), (9, 8192)])
 def test_gemv_q4_k_many_rows_exact(orc, m, n):
     """5-16 rows. One-hot x: each output is the weight rounded once to f32
     (d sc and dmin mn are exact in f32, and the last step is one fused
