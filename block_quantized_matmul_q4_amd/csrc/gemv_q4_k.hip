@@ -195,11 +195,20 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int 
 
 // Several activation rows: T up to 64 (rows longer than 64 chunks take
 // several passes), so that a weight row stays within one wave and the
-// staged rows fit twice per compute unit's LDS.
+// staged rows fit twice per compute unit's LDS. Four rows over 17-32 chunks
+// and wide matrices take T = 16 (two chunks per thread, twice the rows per
+// workgroup): N = 8192, K = 2048 8.4 -> 6.7 us (512 threads), N = 65536
+// 47.3 -> 34.8 us (256 threads); below N = 8192 it is slower. Those rows then
+// round differently from a one-row call (T = 32).
 template <int MR>
 hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N, int C,
                        hipStream_t stream)
 {
+    if constexpr (MR == 4) {
+        if (C > 16 && C <= 32 && N >= 8192)
+            return N >= 32768 ? launch<16, 256, MR>(x, w, y, M, N, C, stream)
+                              : launch<16, 512, MR>(x, w, y, M, N, C, stream);
+    }
     if (C <= 4) return launch<4, 256, MR>(x, w, y, M, N, C, stream);
     if (C <= 8) return launch<8, 256, MR>(x, w, y, M, N, C, stream);
     if (C <= 16) return launch<16, 256, MR>(x, w, y, M, N, C, stream);
@@ -214,7 +223,8 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
 // (rows longer than 128 chunks take several passes); the same shapes as the
 // Q4_0 GEMV, whose chunks (pairs of blocks) hold as many weights and bytes.
 // Two to four rows keep T at 64 past 32 chunks (launch_rows), so that the
-// staged rows fit twice per compute unit's LDS.
+// staged rows fit twice per compute unit's LDS, and four rows take T = 16
+// over 17-32 chunks from N = 8192.
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream)
 {

@@ -110,7 +110,7 @@ CASES = [
     # weight slices from N = 8192), medium M and tiles
     ("gemv", "q4_k", 1, 300, 2048), ("gemv", "q4_k", 3, 300, 1024),
     ("gemv", "q4_k", 8, 300, 1024), ("gemv", "q4_k", 12, 8200, 512),
-    ("gemv", "q4_k", 12, 4000, 512),
+    ("gemv", "q4_k", 12, 4000, 512), ("gemv", "q4_k", 4, 8200, 1280),
     ("gemm", "q4_k", 20, 300, 1024), ("gemm", "q4_k", 300, 300, 512),
     ("gemm", "q4_k", 80, 8150, 512),
 ]

@@ -669,7 +669,9 @@ def test_gemv_q4_k_repeatable_and_errors():
 # ragged N, M = 3 (four rows run, the fourth not stored)
 Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
                     (2, 17, 256), (3, 4099, 8448), (4, 65, 16384), (2, 50, 65536),
-                    (4, 2049, 4352), (3, 9000, 1024)]
+                    (4, 2049, 4352), (3, 9000, 1024),
+                    # four rows over 17-32 chunks from N = 8192: T = 16, 512 and 256 threads
+                    (4, 8193, 1280), (3, 40000, 2048)]
 
 
 @pytest.mark.parametrize("m,n,k", Q4_K_ROWS_SHAPES)
@@ -678,9 +680,10 @@ def test_gemv_q4_k_rows(orc, m, n, k):
 
 
 # Up to 64 chunks per row (K <= 4096) the multi-row launch uses the one-row
-# launch's threads per row: each row then equals the one-row result bit for bit.
-@pytest.mark.parametrize("m,n,k", [(2, 1000, 1024), (4, 8192, 2048), (3, 333, 4096),
-                                   (4, 300, 256)])
+# launch's threads per row (except four rows over 17-32 chunks from N = 8192,
+# which take 16): each row then equals the one-row result bit for bit.
+@pytest.mark.parametrize("m,n,k", [(2, 1000, 1024), (2, 8192, 2048), (4, 4096, 2048),
+                                   (3, 333, 4096), (4, 300, 256)])
 def test_gemv_q4_k_rows_match_single_row_bitwise(m, n, k):
     x = synth.activations(m, k, seed=38)
     w = synth.q4_k_weights(n, k, seed=38)
