@@ -552,6 +552,19 @@ def main():
         add_row("q4_0_gemv_vocab", lib.qmm_gemv_q4_0,
                 gemv_args(xv, w4v, yv, 1, voc["N"], voc["K"], nv),
                 bytes=w4v_h.nbytes + xv_h.nbytes + yv.numel() * 4)
+        # a deeper FFN's down projection (K = 14336 -> N = 4096, 33 MB of
+        # Q4_0): one and four activation rows over K > 4096
+        wd_h = synth.q4_0_weights(4096, 14336)
+        wd = pool(wd_h)
+        xd = torch.from_numpy(synth.activations(4, 14336)).to(dev)
+        keep += wd + [xd]
+        for m in (1, 4):
+            xdm = xd[:m].contiguous()
+            ydm = torch.empty((m, 4096), device=dev)
+            keep += [xdm, ydm]
+            add_row(f"q4_0_gemv_k14336_m{m}", lib.qmm_gemv_q4_0,
+                    gemv_args(xdm, wd, ydm, m, 4096, 14336, n),
+                    bytes=wd_h.nbytes + xdm.numel() * 4 + ydm.numel() * 4, tokens=m)
         # prefill GEMM: M = 2048 over Q4_0, Q8_0 and Q4_K; short prompts
         pre = synth.WORKLOADS["q4_0_gemm_prefill"]
         xp = torch.from_numpy(synth.activations(pre["M"], pre["K"])).to(dev)

@@ -477,11 +477,14 @@ hipError_t launch_gated(const float *x, const uint8_t *wg, const uint8_t *wu, fl
 //   P <= 64 : T = 64, one row per thread, 512-thread workgroups sharing one
 //             activation copy (MR = 1 with N >= 32768: T = 32 x 2 chunks;
 //             Q4_0, N = 128256, K = 4096: 68-75 -> 57 us)
-//   P > 64  : T = 128 (a row spans two waves), one row per thread, looping
-//             over K in chunks of 128 pairs, workgroups sharing one
-//             activation copy: 512 threads (4 rows; MR = 4: 2 rows per
-//             thread); with MR = 1, 1024 threads (8 rows) from N = 4096
-//             (Q4_0) or N = 2048 (Q8_0)
+//   P > 64  : from N = 4096, T = 64 looping over K in chunks of 64 pairs,
+//             512-thread workgroups sharing one activation copy, 2 rows per
+//             thread with MR = 4, and with MR = 2 from N = 8192 and K = 8192
+//             (N = 28672, K = 8192 against T = 128: Q4_0 43.7 -> 29.9 us at
+//             M = 1, 50.1 -> 35.6 at M = 2, 82.9 -> 56.1 at M = 4; Q8_0
+//             44.3 -> 42.9, 62.8 -> 47.9, 93.6 -> 62.3). Below N = 4096,
+//             T = 128 (a row spans two waves) in 512 threads (MR = 4: 2 rows
+//             per thread; Q8_0 with MR = 1 from N = 2048: 1024 threads)
 template <int FMT, int MR>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
@@ -510,8 +513,17 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
             return launch<FMT, 32, 1, 512, 2, true, false, 1>(x, w, y, M, N, P, stream);
         return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
     }
-    if (MR == 1 && N >= (FMT == FMT_Q4_0 ? 4096 : 2048))
-        return launch<FMT, 128, 1, 1024, 1, true, false, 1>(x, w, y, M, N, P, stream);
+    if (N >= 4096) {
+        if constexpr (MR == 4)
+            return launch<FMT, 64, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+        if constexpr (MR == 2)
+            if (N >= 8192 && P >= 128)
+                return launch<FMT, 64, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+        return launch<FMT, 64, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
+    }
+    if constexpr (FMT == FMT_Q8_0 && MR == 1)
+        if (N >= 2048)
+            return launch<FMT, 128, 1, 1024, 1, true, false, MR>(x, w, y, M, N, P, stream);
     if (MR == 4) return launch<FMT, 128, 2, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
     return launch<FMT, 128, 1, 512, 1, true, false, MR>(x, w, y, M, N, P, stream);
 }

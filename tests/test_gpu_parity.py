@@ -147,6 +147,10 @@ GEMV_SHAPES = [
     # 9-16 rows with N >= 8192 (f32-exact 32-row weight slices): ragged M and
     # N, K steps not a multiple of the waves, wide N
     (9, 8193, 1024), (12, 8192, 8448), (16, 65537, 512), (13, 9000, 256),
+    # K > 4096 from N = 4096 (64 threads per row looping over K; two weight
+    # rows per thread at M = 4, and at M = 2 from N = 8192, K = 8192): ragged
+    # N and a last chunk of 1-8 pairs
+    (1, 8193, 4160), (2, 8200, 8448), (2, 9000, 5120), (4, 4097, 4160), (3, 8193, 8704),
     # K a multiple of 64 but not of 256 (pair counts 1, 5, 14, 17, 47)
     (1, 300, 64), (1, 4097, 896), (2, 1000, 320), (3, 2049, 1088), (4, 65537, 896),
     (6, 500, 896), (8, 8192, 3008), (12, 700, 320), (16, 9000, 1088),
@@ -164,7 +168,8 @@ def test_gemv_shapes(orc, fmt, m, n, k):
 # the same threads per row (every K branch, N < 65536), each row of a
 # multi-row result equals the one-row result bit for bit.
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
-@pytest.mark.parametrize("n,k", [(1000, 1024), (8192, 2048), (333, 4096), (4099, 8448)])
+@pytest.mark.parametrize("n,k", [(1000, 1024), (8192, 2048), (333, 4096), (4099, 8448),
+                                 (8200, 8448), (2049, 8192)])
 def test_gemv_rows_match_single_row_bitwise(fmt, n, k):
     note(f"[bitwise] gemv_{fmt} rows vs single-row calls N={n} K={k}")
     x = synth.activations(4, k, seed=n)
