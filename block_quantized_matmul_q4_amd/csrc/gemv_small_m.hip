@@ -1,11 +1,11 @@
 // Small-M GEMV (2 <= M <= 16 activation rows: batched or speculative
 // decode) over GGUF Q4_0 / Q8_0 weights, and 5 <= M <= 16 over Q4_K
 // super-blocks, on the bf16 matrix cores. The C-ABI sends 5 <= M <= 8, and
-// Q8_0 with 9 <= M <= 16 and N < 8192, here when K % 256 == 0 (each wave
-// takes K in slices of 256), and every Q4_K GEMV of 5 to 16 rows: up to 4
-// rows the f32 FMA kernels that stream the weights for one row are faster
-// (they decode each weight once for all rows), and from 9 rows over wide
-// matrices the 32-row weight-slice kernel is (Q4_0, Q8_0).
+// 9 <= M <= 16 with N < 8192, here when K % 256 == 0 (each wave takes K in
+// slices of 256; always so for Q4_K): up to 4 rows the f32 FMA kernels that
+// stream the weights for one row are faster (they decode each weight once
+// for all rows), and from 9 rows over wide matrices (N >= 8192) the 32-row
+// weight-slice kernel is.
 //
 // With several activation rows the f32 FMA count (M per weight) outgrows
 // the weight stream, so the contraction moves to v_mfma_f32_16x16x32_bf16:
@@ -229,7 +229,7 @@ __device__ __forceinline__ int afrag(int s)
     return 4 * s + 4 * (g + (g >> 3));
 }
 
-template <int FMT, bool PACK, int NT, int WAVES>
+template <int FMT, bool PACK, int NT, int WAVES, bool PF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
     float *__restrict__ y, int M, int N, int K)
@@ -271,13 +271,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = wave * KW; k0 < K; k0 += WAVES * KW) {
-        // ---- 1. loads
-        float4 xv[MMAX];
+    // ---- 1. loads of the slice at k0 into registers
+    float4 xv[MMAX];
+    uint32_t D[PPL][L::kPairDwords];
+    auto load = [&](int k0) {
 #pragma unroll
         for (int m = 0; m < MMAX; ++m)
             if (m < M) xv[m] = *reinterpret_cast<const float4 *>(x + (int64_t)m * K + k0 + 4 * lane);
-        uint32_t D[PPL][L::kPairDwords];
 #pragma unroll
         for (int u = 0; u < PPL; ++u) {
             const uint8_t *src = wsrc + (int64_t)(k0 / 64 + lp0 + u) * L::kPairBytes;
@@ -289,6 +289,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
             D[u][L::kPairDwords - 1] =
                 *reinterpret_cast<const uint32_t *>(src + 4 * (L::kPairDwords - 1));
         }
+    };
+    // PF: a wave's next slice is loaded while its matrix cores work on this
+    // one (the registers are free once this slice sits in LDS)
+    if constexpr (PF)
+        if (wave * KW < K) load(wave * KW);
+    for (int k0 = wave * KW; k0 < K; k0 += WAVES * KW) {
+        if constexpr (!PF) load(k0);
         // ---- 2. to LDS
         wave_lds_sync();            // previous pass's reads done
         {
@@ -314,6 +321,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
 #pragma unroll
         for (int u = 0; u < PPL; ++u)
             L::relayout(D[u], wl + lrow * WROW + (lp0 + u) * L::kPairDwords);
+        if constexpr (PF)
+            if (k0 + WAVES * KW < K) load(k0 + WAVES * KW);
         wave_lds_sync();
         // ---- 3. matrix cores
         const int col = lane % 16, g = lane / 16;
@@ -375,43 +384,71 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     }
 }
 
+template <int FMT, bool PACK, int NT, int WAVES, bool PF>
+void launch_shape(const float *x, const uint8_t *w, float *y, int M, int N, int K,
+                  hipStream_t stream)
+{
+    const int grid = (N + 16 * NT - 1) / (16 * NT);
+    hipLaunchKernelGGL((gemv_small_m_kernel<FMT, PACK, NT, WAVES, PF>), dim3(grid),
+                       dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
+}
+
+// Launch shapes from timing sweeps on MI355X (random weights, cold copies;
+// NT x 16 weight rows and WAVES waves per workgroup, PF = next-slice
+// prefetch). Prefetch measured faster wherever a workgroup holds 16 weight
+// rows (Q4_0, M = 8, N = 2048, K = 16384: 18.6 -> 17.1 us; Q4_K, M = 8,
+// N = 4096, K = 14336: 20.1 -> 18.0 us) and with one slice per wave (its
+// loads then issue before the LDS clearing: FFN up shape, M = 8, 7.18 ->
+// 6.89 us), slightly slower with 32 rows and 8 waves over deeper K (N =
+// 28672, K = 8192: 57.9 -> 58.9 us).
+// For 5-8 rows over wide matrices the fastest shape is, in the sweeps, the
+// one with the most waves resident whose workgroups all fit the chip at
+// once: 32 rows and 8 waves (one workgroup per CU) up to N = 8192; 16 rows
+// and 4 waves (three per CU, 768 in all) up to N = 12288 (Q4_0, N = 10240,
+// K = 4096: 18.0 -> 14.5 us; Q8_0 24.4 -> 18.6 us); 32 rows and 4 waves (two
+// per CU) up to N = 16384 (Q4_0, N = 14336, K = 4096: 18.5 -> 16.6 us).
+// Beyond that Q4_0 runs 32 rows in 2-wave workgroups (N = 28672, K = 8192:
+// 58.0 -> 51.0 us; N = 128256, K = 4096: 116.2 -> 101.6 us), Q4_K 32 rows in
+// 4-wave ones (N = 65536, K = 4096: 73.1 -> 66.2 us), and Q8_0, whose weight
+// rows take more LDS, 16 rows in 4 waves below N = 65536 (N = 28672, K =
+// 8192: 85.8 -> 73.9 us) and 32 rows in 4 waves above (N = 128256, K = 4096:
+// 159.5 -> 154.1 us).
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
-    if (M <= 8 && N >= 65536) {
-        // many small workgroups (16 rows, 2 waves): several per CU hide each
-        // other's load latency (measured on the Q8_0 vocabulary head when this
-        // kernel still served M = 2: 217 -> 123 us)
-        constexpr int NT = 1, WAVES = 2;
-        const int grid = (N + 16 * NT - 1) / (16 * NT);
-        hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, WAVES>), dim3(grid),
-                           dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
-    } else if (N < 8192) {
+    if (N < 8192) {
         // fewer than 256 workgroups of 32 rows: 16 rows per workgroup, eight
-        // waves over K (six for M > 8, whose A fragments take twice the LDS)
-        // (FFN down shape N = 2048, K = 8192: M = 5 14.9 -> 11.6 us, M = 16
-        // 26.4 -> 23.1 us)
-        constexpr int NT = 1;
-        const int grid = (N + 16 * NT - 1) / (16 * NT);
+        // waves over K (seven for M > 8, whose A fragments take twice the
+        // LDS; Q4_0, M = 16, N = 4096, K = 14336: 34.0 us on the 32-row
+        // weight slices, 28.8 with six waves, 24.4 with seven and prefetch)
         if (M <= 8)
-            hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, 8>), dim3(grid),
-                               dim3(64 * 8), 0, stream, x, w, y, M, N, K);
+            launch_shape<FMT, true, 1, 8, true>(x, w, y, M, N, K, stream);
         else
-            hipLaunchKernelGGL((gemv_small_m_kernel<FMT, false, NT, 6>), dim3(grid),
-                               dim3(64 * 6), 0, stream, x, w, y, M, N, K);
-    } else if (M <= 8) {
-        constexpr int NT = 2, WAVES = 8;
-        const int grid = (N + 16 * NT - 1) / (16 * NT);
-        hipLaunchKernelGGL((gemv_small_m_kernel<FMT, true, NT, WAVES>), dim3(grid),
-                           dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
-    } else {
+            launch_shape<FMT, false, 1, 7, true>(x, w, y, M, N, K, stream);
+    } else if (M > 8) {
         // 32 weight rows per workgroup, six waves over K (from a launch
         // sweep at M = 12 and 16, K = 2048, N = 8192)
-        constexpr int NT = 2, WAVES = 6;
-        const int grid = (N + 16 * NT - 1) / (16 * NT);
-        hipLaunchKernelGGL((gemv_small_m_kernel<FMT, false, NT, WAVES>), dim3(grid),
-                           dim3(64 * WAVES), 0, stream, x, w, y, M, N, K);
+        launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
+    } else if (N <= 8192) {
+        if (K <= 8 * KW)
+            launch_shape<FMT, true, 2, 8, true>(x, w, y, M, N, K, stream);
+        else
+            launch_shape<FMT, true, 2, 8, false>(x, w, y, M, N, K, stream);
+    } else if constexpr (FMT == FMT_Q8_0) {
+        if (N < 65536)
+            launch_shape<FMT, true, 1, 4, true>(x, w, y, M, N, K, stream);
+        else
+            launch_shape<FMT, true, 2, 4, true>(x, w, y, M, N, K, stream);
+    } else {
+        if (N <= 12288)
+            launch_shape<FMT, true, 1, 4, true>(x, w, y, M, N, K, stream);
+        else if (N <= 16384)
+            launch_shape<FMT, true, 2, 4, false>(x, w, y, M, N, K, stream);
+        else if constexpr (FMT == FMT_Q4_K)
+            launch_shape<FMT, true, 2, 4, true>(x, w, y, M, N, K, stream);
+        else
+            launch_shape<FMT, true, 2, 2, true>(x, w, y, M, N, K, stream);
     }
     return hipGetLastError();
 }

@@ -115,7 +115,7 @@ QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
         return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N, (int)K,
                                               stream));
     // the 16x16 small-M kernel takes K in slices of 256
-    if (M > 8 || K % 256)
+    if ((M > 8 && N >= 8192) || K % 256)
         return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
                                                   (int)K, stream));
     return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,

@@ -105,12 +105,13 @@ void gemv_entries()
         routed(f, 1, (int64_t)INT_MAX / 2, 64, "gemv_m1");
         routed(f, 12, 300, 320, "gemv_slices");                  // K % 256 != 0
     }
-    routed(qmm_gemv_q4_0, 16, 33, QMM_MAX_K, "gemv_slices");
+    routed(qmm_gemv_q4_0, 16, 33, QMM_MAX_K, "gemv_small_m");
     routed(qmm_gemv_q8_0, 16, 33, QMM_MAX_K, "gemv_small_m");
     routed(qmm_gemv_q4_0, 5, 300, 1024, "gemv_small_m");
     routed(qmm_gemv_q4_0, 8, 8192, 2048, "gemv_small_m");
-    routed(qmm_gemv_q4_0, 9, 300, 1024, "gemv_slices");
-    routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // Q8_0, N < 8192
+    routed(qmm_gemv_q4_0, 9, 300, 1024, "gemv_small_m");         // N < 8192
+    routed(qmm_gemv_q4_0, 9, 8192, 1024, "gemv_slices");
+    routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // N < 8192
     routed(qmm_gemv_q8_0, 12, 8192, 1024, "gemv_slices");
 }
 

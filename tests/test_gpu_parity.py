@@ -151,6 +151,15 @@ GEMV_SHAPES = [
     # rows per thread at M = 4, and at M = 2 from N = 8192, K = 8192): ragged
     # N and a last chunk of 1-8 pairs
     (1, 8193, 4160), (2, 8200, 8448), (2, 9000, 5120), (4, 4097, 4160), (3, 8193, 8704),
+    # 5-16 rows on the 16x16 kernel with next-slice prefetch: 2-wave
+    # workgroups from N = 65536 (several slices per wave), 32 weight rows at
+    # K = 2048 (ragged N) and without prefetch over two slices per wave, and
+    # 9-16 rows below N = 8192 over a ragged number of slices per wave
+    (6, 65537, 1024), (7, 65536, 2560), (8, 8200, 2048), (6, 8192, 4096), (10, 4096, 14336),
+    (16, 2048, 8448),
+    # 5-8 rows over wide matrices: 16 rows in 4 waves up to N = 12288, 32
+    # rows in 4 waves up to 16384, then 2 waves (Q8_0: 16 rows in 4 waves)
+    (6, 10000, 2304), (8, 12289, 2304), (5, 14336, 4096), (7, 20000, 4096),
     # K a multiple of 64 but not of 256 (pair counts 1, 5, 14, 17, 47)
     (1, 300, 64), (1, 4097, 896), (2, 1000, 320), (3, 2049, 1088), (4, 65537, 896),
     (6, 500, 896), (8, 8192, 3008), (12, 700, 320), (16, 9000, 1088),
@@ -708,7 +717,8 @@ Q4_K_MANY_ROWS_SHAPES = [
     (5, 300, 1024), (6, 8192, 2048), (8, 2048, 8192), (7, 65539, 512), (8, 65536, 256),
     (9, 8192, 2048), (12, 2049, 4352), (16, 8192, 2048), (16, 2048, 8192), (13, 17, 256),
     (16, 50, 65536), (11, 4099, 8448), (5, 1, 256), (10, 9000, 1024), (14, 65537, 256),
-    (16, 8200, 65536), (9, 8193, 256), (12, 12000, 1280),
+    (16, 8200, 65536), (9, 8193, 256), (12, 12000, 1280), (6, 65536, 2048), (8, 8192, 4096),
+    (7, 12300, 2048), (8, 10000, 1024),
 ]
 
 
