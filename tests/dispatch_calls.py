@@ -56,7 +56,8 @@ CASES = [
     ("gemm_q4_0", 100, 8193, 512), ("gemm_q4_0", 200, 8150, 512),
     ("gemv_q4_k", 1, 8192, 2048), ("gemv_q4_k", 2, 300, 8192), ("gemv_q4_k", 4, 300, 1024),
     ("gemv_q4_k", 5, 300, 1024), ("gemv_q4_k", 8, 65536, 512), ("gemv_q4_k", 16, 8192, 2048),
-    ("gemv_q4_k", 12, 4096, 1024), ("gemv_q4_k", 4, 8192, 2048),
+    ("gemv_q4_k", 12, 4096, 1024), ("gemv_q4_k", 4, 8192, 2048), ("gemv_q4_k", 4, 8192, 8192),
+    ("gemv_q4_k", 1, 4096, 8192),
     ("gemm_q4_k", 3, 300, 1024), ("gemm_q4_k", 40, 300, 1024), ("gemm_q4_k", 2048, 8192, 2048),
     ("ffn_gate_up_q4_0", 1, 8192, 2048), ("ffn_gate_up_q4_0", 1, 2048, 8192),
     ("ffn_gate_up_q4_0", 2, 8192, 2048), ("ffn_gate_up_q4_0", 4, 2048, 8192),

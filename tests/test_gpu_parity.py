@@ -603,7 +603,7 @@ Q4_K_SHAPES = [
     (8192, 2048), (2048, 8192),                      # the FFN decode pair
     (1, 256), (3, 512), (17, 768), (300, 512), (9000, 1024), (4097, 1280),
     (257, 2304), (333, 4096), (2049, 4352), (1000, 8192), (4099, 8448),
-    (65, 16384), (50, 65536), (65539, 1280),
+    (65, 16384), (50, 65536), (65539, 1280), (8193, 4352),
 ]
 
 
@@ -681,7 +681,7 @@ def test_gemv_q4_k_repeatable_and_errors():
 
 # Two to four activation rows: every launch shape (one and several passes),
 # ragged N, M = 3 (four rows run, the fourth not stored)
-Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
+Q4_K_ROWS_SHAPES = [(4, 8200, 8448), (3, 9000, 5120), (2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
                     (2, 17, 256), (3, 4099, 8448), (4, 65, 16384), (2, 50, 65536),
                     (4, 2049, 4352), (3, 9000, 1024),
                     # four rows over 17-32 chunks from N = 8192: T = 16, 512 and 256 threads
