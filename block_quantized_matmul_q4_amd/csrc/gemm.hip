@@ -844,8 +844,8 @@ hipError_t launch_mid_auto(const float *x, const uint8_t *w, float *y, int M, in
 {
     // few column slices: 16 waves keep more K steps in flight per slice
     // (N = 2048, K = 8192: M = 16 17.0 against 17.9 us, M = 64 18.3 against
-    // 19.4)
-    if (N < 4096) return launch_mid<FMT, 1, 1, 16>(x, w, y, M, N, K, stream);
+    // 19.4); more rows than kMidRowsMax give enough bands for the rule below
+    if (N < 4096 && M <= kMidRowsMax) return launch_mid<FMT, 1, 1, 16>(x, w, y, M, N, K, stream);
     int best = -1;
     int64_t best_wg = 0;
     for (int c = 0; c < 4; ++c) {
@@ -870,11 +870,14 @@ hipError_t launch_mid_auto(const float *x, const uint8_t *w, float *y, int M, in
 
 // More rows take the tile kernels: 256 x 256 tiles when there are at least
 // as many as compute units, else 128 x 128 ones. With at most 128 of those
-// (half the chip, each running the whole K loop) and N >= 4096 the
-// medium-M kernel's 64 x 64 tiles are faster (sweep at M = 160-768: N =
-// 8192, K = 2048, M = 160 26.0 -> 21.2 us; N = 4096, K = 4096, M = 256 46.9
-// -> 25.3 us, M = 512 47.7 -> 42.2 us; the tile kernel wins from 192 small
-// tiles on, e.g. N = 8192, M = 384 27.0 against 35.4 us).
+// (half the chip, each running the whole K loop; below N = 4096 fewer than
+// 128) the medium-M kernel's smaller tiles are faster (sweep at M =
+// 160-768: N = 8192, K = 2048, M = 160 26.0 -> 21.2 us; N = 4096, K = 4096,
+// M = 256 46.9 -> 25.3 us, M = 512 47.7 -> 42.2 us; N = 1024, K = 4096, M =
+// 160 42.7 -> 10.3 us, M = 512 43.1 -> 17.5 us; N = 2048, K = 8192, M = 512
+// 82.1 -> 42.8 us; the tile kernel wins from 192 small tiles on, e.g. N =
+// 8192, M = 384 27.0 against 35.4 us, and below N = 4096 from 128: N = 1024,
+// M = 2048 43.9 against 53.2 us).
 template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
@@ -883,7 +886,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
     const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (large_tiles >= kComputeUnits) return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
     const int64_t small_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (N >= 4096 && small_tiles <= kComputeUnits / 2)
+    if (small_tiles < kComputeUnits / 2 || (N >= 4096 && small_tiles == kComputeUnits / 2))
         return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);
     return launch_tiles<FMT, TileSmall>(x, w, y, M, N, K, stream);
 }

@@ -221,7 +221,11 @@ GEMM_SHAPES = [(1, 1, 256), (5, 100, 768), (127, 129, 256), (129, 300, 2048),
                (100, 8193, 2048),
                # more than 128 rows over at most 128 tiles of 128 x 128 (the
                # medium-M kernel's 64 x 64 tiles, 8 and 4 waves)
-               (160, 4096, 1024), (200, 8150, 512), (300, 4100, 1024)]
+               (160, 4096, 1024), (200, 8150, 512), (300, 4100, 1024),
+               # below N = 4096: fewer than 128 such tiles (the medium-M
+               # kernel's shape rule: 32 x 32 and 64 x 64 tiles) and more
+               # (the 128 x 128 tile kernel)
+               (160, 1000, 4096), (300, 3000, 1024), (2100, 1030, 512)]
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
