@@ -542,9 +542,15 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
 
 // Gated FFN front half: a thread's two rows are one gate row and one up
 // row; from P = 32 on, workgroups share one activation copy (timing sweeps
-// as above). Several activation rows (MR = 2 or 4; M = 3 runs four and
-// stores three) take the same launch shapes, so each row equals the one-row
-// result bit for bit.
+// as above). From N = 4096, rows of more than 32 pairs loop over K in
+// chunks of 32 pairs in 256-thread workgroups (against T = 64 in 512
+// threads: N = 28672, K = 8192 59.8 -> 50.9 us at M = 1, 108.0 -> 90.9 at
+// M = 4; N = 13824, K = 5120 29.0 -> 20.5 and 53.2 -> 38.0 us; against
+// T = 128: N = 4096, K = 14336 19.2 -> 16.0 and 41.9 -> 30.2 us); below
+// N = 4096, T = 128 stays faster (N = 2048, K = 8192: 6.5 against 8.2 us).
+// Several activation rows (MR = 2 or 4; M = 3 runs four and stores three)
+// take the same launch shapes, so each row equals the one-row result bit
+// for bit.
 template <int MR>
 hipError_t launch_gated_rows(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                              float *h, int M, int N, int P, hipStream_t stream)
@@ -553,9 +559,9 @@ hipError_t launch_gated_rows(const float *x, const uint8_t *w_gate, const uint8_
     if (P <= 8) return launch_gated<8, kThreads, false, MR>(x, w_gate, w_up, h, M, N, P, stream);
     if (P <= 16)
         return launch_gated<16, kThreads, false, MR>(x, w_gate, w_up, h, M, N, P, stream);
-    if (P <= 32) return launch_gated<32, 256, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
-    if (P <= 64 || N >= 8192)
-        return launch_gated<64, 512, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 32 || N >= 4096)
+        return launch_gated<32, 256, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
+    if (P <= 64) return launch_gated<64, 512, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
     return launch_gated<128, 512, true, MR>(x, w_gate, w_up, h, M, N, P, stream);
 }
 

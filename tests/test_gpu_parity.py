@@ -452,7 +452,8 @@ def run_ffn(x, wg, wu, n, k):
 
 @pytest.mark.parametrize("n,k", [(8192, 2048), (1, 256), (1000, 256), (333, 512), (257, 1024),
                                  (4097, 1280), (100, 4096), (2048, 8192), (65, 16384),
-                                 (8200, 4352), (1000, 896), (300, 64)])
+                                 (8200, 4352), (1000, 896), (300, 64), (4099, 5120),
+                                 (4096, 14336)])
 def test_ffn_gate_up(orc, n, k):
     note(f"[parity] ffn_gate_up_q4_0 N={n} K={k}")
     x = synth.activations(1, k, seed=n)
@@ -488,7 +489,7 @@ def test_ffn_gate_up_rows(orc, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(2, 1000, 256), (3, 8192, 2048), (4, 2048, 8192),
-                                   (4, 65, 16384)])
+                                   (4, 65, 16384), (4, 4100, 5120)])
 def test_ffn_gate_up_rows_match_single_row_bitwise(m, n, k):
     x = synth.activations(m, k, seed=39)
     wg, wu = synth.q4_0_weights(n, k, seed=39), synth.q4_0_weights(n, k, seed=40)
