@@ -55,22 +55,155 @@ __device__ __forceinline__ void sub_block(uint32_t b0, uint32_t b1, uint32_t b2,
     }
 }
 
-template <int T, int WG, int MR, int RPT>
+template <int T, int WG, int MR>
 __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__ x,
                                                        const uint8_t *__restrict__ w,
                                                        float *__restrict__ y, int M, int N,
                                                        int C)
 {
+    constexpr int RPAR = WG / T;                // rows per workgroup
+    constexpr int TW = T < 64 ? T : 64;         // chunks per wave per row
+    constexpr int WPR = T / TW;                 // waves per row
+    constexpr int XU = (16 * T + WG - 1) / WG;  // staged float4 per thread, row and pass
+    static_assert(MR == 1 || WPR == 1, "several activation rows: a weight row within a wave");
+    __shared__ __attribute__((aligned(16))) float xs[MR * T * XS];
+    __shared__ float red[WPR > 1 ? WG / 64 : 1];
+
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int t = tid % T, r = tid / T;
+    const int n = blockIdx.x * RPAR + r;
+    const int64_t row_bytes = (int64_t)(C / 4) * kQKBytes;
+    const uint8_t *wrow = w + (int64_t)min(n, N - 1) * row_bytes;
+
+    float acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+    for (int c0 = 0; c0 < C; c0 += T) {
+        // 1. this pass's activations: float4 i of a row is chunk i / 16,
+        //    part i % 16 (four scalar arrays: an array of float4 is kept in
+        //    scratch)
+        float xvx[MR * XU], xvy[MR * XU], xvz[MR * XU], xvw[MR * XU];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const float *xr = x + (int64_t)min(r, M - 1) * (64 * (int64_t)C);
+#pragma unroll
+            for (int u = 0; u < XU; ++u) {
+                const int i = tid + WG * u;
+                const int ch = min(c0 + min(i / 16, T - 1), C - 1);
+                const float4 v = *reinterpret_cast<const float4 *>(xr + 64 * ch + 4 * (i % 16));
+                xvx[r * XU + u] = v.x; xvy[r * XU + u] = v.y;
+                xvz[r * XU + u] = v.z; xvw[r * XU + u] = v.w;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 2. the super-block header and the chunk's nibbles
+        const int ch = min(c0 + t, C - 1);
+        const uint8_t *sb = wrow + (int64_t)(ch / 4) * kQKBytes;
+        const int c = ch % 4;
+        const u32x4_a4 hdr = *reinterpret_cast<const u32x4_a4 *>(sb);
+        const u32x4_a4 q0 = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * c);
+        const u32x4_a4 q1 = *reinterpret_cast<const u32x4_a4 *>(sb + 32 + 32 * c);
+        __builtin_amdgcn_sched_barrier(0);
+        // 3. activations to LDS (from the second pass on, after the
+        //    previous pass's readers)
+        if (c0 != 0) __syncthreads();
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+#pragma unroll
+            for (int u = 0; u < XU; ++u) {
+                const int i = tid + WG * u;
+                if (16 * T % WG == 0 || i < 16 * T)
+                    *reinterpret_cast<float4 *>(&xs[(r * T + i / 16) * XS + 4 * (i % 16)]) =
+                        make_float4(xvx[r * XU + u], xvy[r * XU + u], xvz[r * XU + u],
+                                    xvw[r * XU + u]);
+            }
+        }
+        lds_only_barrier();
+        // 4. the chunk's 64 weights against its activations
+        const float d = half_lo(hdr.x), dmin = half_hi(hdr.x);
+        const uint32_t nb[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float part[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) part[r] = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t sc, mn;
+            sub_block(hdr.y, hdr.z, hdr.w, c, h, sc, mn);
+            const float dsc = d * (float)sc, dmn = dmin * (float)mn;
+            float s[MR];
+#pragma unroll
+            for (int r = 0; r < MR; ++r) s[r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t v = h ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
+                // hide the nibble range from the compiler, which would
+                // otherwise extract each nibble with a bit-field op before
+                // converting it; this way each byte converts in one
+                // v_cvt_f32_ubyteN
+                asm("" : "+v"(v));
+                const float w0 = fmaf(dsc, (float)(v & 0xFFu), -dmn);
+                const float w1 = fmaf(dsc, (float)((v >> 8) & 0xFFu), -dmn);
+                const float w2 = fmaf(dsc, (float)((v >> 16) & 0xFFu), -dmn);
+                const float w3 = fmaf(dsc, (float)(v >> 24), -dmn);
+#pragma unroll
+                for (int r = 0; r < MR; ++r) {
+                    const float4 xa = *reinterpret_cast<const float4 *>(
+                        &xs[(r * T + t) * XS + 32 * h + 4 * i]);
+                    s[r] = fmaf(w0, xa.x, s[r]);
+                    s[r] = fmaf(w1, xa.y, s[r]);
+                    s[r] = fmaf(w2, xa.z, s[r]);
+                    s[r] = fmaf(w3, xa.w, s[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < MR; ++r) part[r] += s[r];
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) acc[r] += c0 + t < C ? part[r] : 0.f;
+    }
+
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = group_sum<TW>(acc[r]);
+    if constexpr (WPR == 1) {
+        if (t == T - 1 && n < N) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+                if (r < M) y[(int64_t)r * N + n] = acc[r];
+        }
+    } else {
+        if (lane == 63) red[wave] = acc[0];
+        __syncthreads();
+        if (tid < RPAR) {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < WPR; ++q) s += red[tid * WPR + q];
+            const int nn = blockIdx.x * RPAR + tid;
+            if (nn < N) y[nn] = s;
+        }
+    }
+}
+
+// The same with two weight rows per thread (rows n0 and n0 + WG / T of the
+// workgroup's block), each staged activation float4 read once for both;
+// every row keeps the one-row order of operations. A separate kernel, so
+// that the one-row-per-thread instances keep their own schedule (folded
+// into one template, they were compiled to read LDS one float4 at a time).
+template <int T, int WG, int MR>
+__global__ __launch_bounds__(WG) void gemv_q4_k_pair_kernel(const float *__restrict__ x,
+                                                            const uint8_t *__restrict__ w,
+                                                            float *__restrict__ y, int M,
+                                                            int N, int C)
+{
+    constexpr int RPT = 2;                      // weight rows per thread
     constexpr int RPAR = WG / T;                // rows in flight per workgroup
     constexpr int TW = T < 64 ? T : 64;         // chunks per wave per row
     constexpr int WPR = T / TW;                 // waves per row
     constexpr int XU = (16 * T + WG - 1) / WG;  // staged float4 per thread, row and pass
     static_assert(MR == 1 || WPR == 1, "several activation rows: a weight row within a wave");
-    static_assert(RPT == 1 || WPR == 1, "several weight rows per thread: a row within a wave");
+    static_assert(WPR == 1, "several weight rows per thread: a row within a wave");
     __shared__ __attribute__((aligned(16))) float xs[MR * T * XS];
-    __shared__ float red[WPR > 1 ? WG / 64 : 1];
 
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int tid = threadIdx.x;
     const int t = tid % T, r = tid / T;
     // this thread's weight rows: n0 + RPAR j (j < RPT)
     const int n0 = blockIdx.x * (RPAR * RPT) + r;
@@ -131,6 +264,15 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
         lds_only_barrier();
         // 4. the chunk's 64 weights of each row against its activations;
         //    every activation float4 is read once for the thread's rows
+        float d[RPT], dmin[RPT];
+        uint32_t nb[RPT][8];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            d[j] = half_lo(hdr[j].x);
+            dmin[j] = half_hi(hdr[j].x);
+            nb[j][0] = q0[j].x; nb[j][1] = q0[j].y; nb[j][2] = q0[j].z; nb[j][3] = q0[j].w;
+            nb[j][4] = q1[j].x; nb[j][5] = q1[j].y; nb[j][6] = q1[j].z; nb[j][7] = q1[j].w;
+        }
         float part[RPT][MR];
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
@@ -143,8 +285,8 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
             for (int j = 0; j < RPT; ++j) {
                 uint32_t sc, mn;
                 sub_block(hdr[j].y, hdr[j].z, hdr[j].w, c, h, sc, mn);
-                dsc[j] = half_lo(hdr[j].x) * (float)sc;
-                dmn[j] = half_hi(hdr[j].x) * (float)mn;
+                dsc[j] = d[j] * (float)sc;
+                dmn[j] = dmin[j] * (float)mn;
             }
             float s[RPT][MR];
 #pragma unroll
@@ -156,8 +298,7 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
                 float wv[RPT][4];
 #pragma unroll
                 for (int j = 0; j < RPT; ++j) {
-                    const uint32_t nw = i < 4 ? q0[j][i] : q1[j][i - 4];
-                    uint32_t v = h ? (nw >> 4) & 0x0F0F0F0Fu : nw & 0x0F0F0F0Fu;
+                    uint32_t v = h ? (nb[j][i] >> 4) & 0x0F0F0F0Fu : nb[j][i] & 0x0F0F0F0Fu;
                     // hide the nibble range from the compiler, which would
                     // otherwise extract each nibble with a bit-field op
                     // before converting it; this way each byte converts in
@@ -196,27 +337,15 @@ __global__ __launch_bounds__(WG) void gemv_q4_k_kernel(const float *__restrict__
     for (int j = 0; j < RPT; ++j)
 #pragma unroll
         for (int r = 0; r < MR; ++r) acc[j][r] = group_sum<TW>(acc[j][r]);
-    if constexpr (WPR == 1) {
-        if (t == T - 1) {
+    if (t == T - 1) {
 #pragma unroll
-            for (int j = 0; j < RPT; ++j) {
-                const int n = n0 + RPAR * j;
-                if (n < N) {
+        for (int j = 0; j < RPT; ++j) {
+            const int n = n0 + RPAR * j;
+            if (n < N) {
 #pragma unroll
-                    for (int r = 0; r < MR; ++r)
-                        if (r < M) y[(int64_t)r * N + n] = acc[j][r];
-                }
+                for (int r = 0; r < MR; ++r)
+                    if (r < M) y[(int64_t)r * N + n] = acc[j][r];
             }
-        }
-    } else {
-        if (lane == 63) red[wave] = acc[0][0];
-        __syncthreads();
-        if (tid < RPAR) {
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < WPR; ++q) s += red[tid * WPR + q];
-            const int nn = blockIdx.x * RPAR + tid;
-            if (nn < N) y[nn] = s;
         }
     }
 }
@@ -225,33 +354,49 @@ template <int T, int WG, int MR, int RPT = 1>
 hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int C,
                   hipStream_t stream)
 {
+    static_assert(RPT == 1 || RPT == 2, "one or two weight rows per thread");
     constexpr int rows = WG / T * RPT;
-    hipLaunchKernelGGL((gemv_q4_k_kernel<T, WG, MR, RPT>), dim3((N + rows - 1) / rows),
-                       dim3(WG), 0, stream, x, w, y, M, N, C);
+    if constexpr (RPT == 1)
+        hipLaunchKernelGGL((gemv_q4_k_kernel<T, WG, MR>), dim3((N + rows - 1) / rows), dim3(WG),
+                           0, stream, x, w, y, M, N, C);
+    else
+        hipLaunchKernelGGL((gemv_q4_k_pair_kernel<T, WG, MR>), dim3((N + rows - 1) / rows),
+                           dim3(WG), 0, stream, x, w, y, M, N, C);
     return hipGetLastError();
 }
 
 // Several activation rows: T up to 64 (rows longer than 64 chunks take
 // several passes), so that a weight row stays within one wave and the
-// staged rows fit twice per compute unit's LDS. Four rows over 17-32 chunks
-// and wide matrices take T = 16 (two chunks per thread, twice the rows per
-// workgroup): N = 8192, K = 2048 8.4 -> 6.7 us (512 threads), N = 65536
-// 47.3 -> 34.8 us (256 threads); below N = 8192 it is slower. Over more than
-// 64 chunks from N = 8192 they take T = 32 with two weight rows per thread,
-// which read each staged activation once for both (the activation reads
-// from LDS set the pace at four rows): N = 28672, K = 8192 64.0 -> 58.4 us;
-// N = 8192, K = 28672 62 -> 54.3 us; N = 13824, K = 5120 29.0 -> 24.7 us
-// (3 % slower at 64 chunks). Those rows then round differently from a
-// one-row call (its T).
+// staged rows fit twice per compute unit's LDS. From timing sweeps on random
+// weights over matrix shapes from N = 2048 to 65536 and K = 2048 to 28672:
+//  * two rows past 32 chunks from N = 4096 loop over T = 32 in 256 threads
+//    (N = 13824, K = 5120: 25.2 -> 19.0 us; N = 28672, K = 8192: 51.6 ->
+//    45.4 us);
+//  * four rows take two weight rows per thread (the pair kernel: each
+//    staged activation float4 read once for both, since at four rows those
+//    LDS reads set the pace) with T = 16 and 512 threads where that gives at
+//    least 192 workgroups (N >= 12288) and a row has 17-128 chunks (N =
+//    14336, K = 4096: 26.8 -> 16.1 us; N = 13824, K = 5120: 43.5 -> 19.3 us;
+//    N = 28672, K = 8192: 89.5 -> 57.6 us; N = 16384, K = 2048: 11.4 -> 9.9
+//    us), else past 32 chunks from N = 8192 T = 32 in 256 threads (N = 8192,
+//    K = 8192: 27.3 -> 18.5 us; K = 28672: 81.1 -> 59.2 us) and past 64
+//    chunks at N = 4096-8191 T = 64 in 512 threads (N = 4096, K = 14336:
+//    25.5 -> 19.6 us); 17-32 chunks at N = 8192-16383 keep one row per
+//    thread with T = 16 (FFN up shape 8.4 -> 6.7 us against T = 32).
+// Rows of a multi-row call round differently from a one-row call wherever
+// the two take different T.
 template <int MR>
 hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N, int C,
                        hipStream_t stream)
 {
     if constexpr (MR == 4) {
-        if (C > 16 && C <= 32 && N >= 8192)
-            return N >= 32768 ? launch<16, 256, MR>(x, w, y, M, N, C, stream)
-                              : launch<16, 512, MR>(x, w, y, M, N, C, stream);
-        if (C > 64 && N >= 8192) return launch<32, 256, MR, 2>(x, w, y, M, N, C, stream);
+        if (N >= 12288 && C > 16 && C <= 128)
+            return launch<16, 512, MR, 2>(x, w, y, M, N, C, stream);
+        if (N >= 8192 && C > 32) return launch<32, 256, MR, 2>(x, w, y, M, N, C, stream);
+        if (N >= 8192 && C > 16 && C <= 32) return launch<16, 512, MR>(x, w, y, M, N, C, stream);
+        if (N >= 4096 && C > 64) return launch<64, 512, MR, 2>(x, w, y, M, N, C, stream);
+    } else {
+        if (N >= 4096 && C > 32) return launch<32, 256, MR>(x, w, y, M, N, C, stream);
     }
     if (C <= 4) return launch<4, 256, MR>(x, w, y, M, N, C, stream);
     if (C <= 8) return launch<8, 256, MR>(x, w, y, M, N, C, stream);
@@ -265,14 +410,11 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
 // C = K / 64 chunks per row (a multiple of 4). With one activation row, T
 // is the smallest of 4, 8, 16, 32, 64 and 128 that covers a row in one pass
 // (rows longer than 128 chunks take several passes), except that from
-// N = 4096 rows of more than 64 chunks loop over T = 64 as the Q4_0 GEMV
-// does (N = 8192, K = 28672: 36.9 -> 30.5 us; N = 28672, K = 8192: 32.9 ->
-// 29.9 us; at the FFN down shape, N = 2048, T = 128 stays faster); the same
-// shapes as the Q4_0 GEMV, whose chunks (pairs of blocks) hold as many
-// weights and bytes. Two to four rows keep T at 64 past 32 chunks
-// (launch_rows), so that the staged rows fit twice per compute unit's LDS;
-// four rows take T = 16 over 17-32 chunks and T = 32 with two weight rows
-// per thread past 64 chunks, from N = 8192.
+// N = 4096 rows of more than 64 chunks loop over T = 32 in 256 threads
+// (N = 13824, K = 5120: 17.4 -> 14.7 us; N = 8192, K = 28672: 40.7 -> 36.9
+// us; at the FFN down shape, N = 2048, T = 128 stays faster); otherwise the
+// shapes of the Q4_0 GEMV, whose chunks (pairs of blocks) hold as many
+// weights and bytes. Two to four rows: launch_rows.
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream)
 {
@@ -283,7 +425,8 @@ hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, i
     if (C <= 8) return launch<8, 256, 1>(x, w, y, M, N, C, stream);
     if (C <= 16) return launch<16, 256, 1>(x, w, y, M, N, C, stream);
     if (C <= 32) return launch<32, 256, 1>(x, w, y, M, N, C, stream);
-    if (C <= 64 || N >= 4096) return launch<64, 512, 1>(x, w, y, M, N, C, stream);
+    if (C <= 64) return launch<64, 512, 1>(x, w, y, M, N, C, stream);
+    if (N >= 4096) return launch<32, 256, 1>(x, w, y, M, N, C, stream);
     return launch<128, 512, 1>(x, w, y, M, N, C, stream);
 }
 

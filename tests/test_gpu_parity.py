@@ -686,11 +686,19 @@ def test_gemv_q4_k_repeatable_and_errors():
 
 # Two to four activation rows: every launch shape (one and several passes),
 # ragged N, M = 3 (four rows run, the fourth not stored)
-Q4_K_ROWS_SHAPES = [(4, 8200, 8448), (3, 9000, 5120), (2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
+Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
                     (2, 17, 256), (3, 4099, 8448), (4, 65, 16384), (2, 50, 65536),
                     (4, 2049, 4352), (3, 9000, 1024),
-                    # four rows over 17-32 chunks from N = 8192: T = 16, 512 and 256 threads
-                    (4, 8193, 1280), (3, 40000, 2048)]
+                    # four rows over 17-32 chunks at N = 8192-12287: T = 16, one row
+                    # per thread
+                    (4, 8193, 1280),
+                    # four rows, two weight rows per thread: T = 16 from N = 12288
+                    # (17-128 chunks), T = 32 past 32 chunks from N = 8192, T = 64
+                    # past 64 chunks from N = 4096; ragged N
+                    (3, 40000, 2048), (4, 12289, 2304), (3, 12300, 5120), (4, 16385, 2048),
+                    (4, 8200, 8448), (3, 9000, 5120), (4, 4100, 4608),
+                    # two rows past 32 chunks from N = 4096: T = 32
+                    (2, 4097, 2304), (2, 8192, 8448)]
 
 
 @pytest.mark.parametrize("m,n,k", Q4_K_ROWS_SHAPES)
