@@ -2,8 +2,9 @@
 // decode) over GGUF Q4_0 / Q8_0 weights, and 5 <= M <= 16 over Q4_K
 // super-blocks, on the bf16 matrix cores. The C-ABI sends 5 <= M <= 8, and
 // 9 <= M <= 16 with N < 8192, here when K % 256 == 0 (each wave takes K in
-// slices of 256; always so for Q4_K): up to 4 rows the f32 FMA kernels that
-// stream the weights for one row are faster (they decode each weight once
+// slices of 256; always so for Q4_K), and for Q4_0 and Q8_0 also 3-4 rows
+// where K and N >= 4096: up to 4 rows the f32 FMA kernels that stream the
+// weights for one row are faster elsewhere (they decode each weight once
 // for all rows), and from 9 rows over wide matrices (N >= 8192) the 32-row
 // weight-slice kernel is.
 //

@@ -72,6 +72,27 @@ int finish(const char *fn, hipError_t err)
     return QMM_OK;
 }
 
+// The Q4_0 / Q8_0 GEMV for 1 <= M <= 16 (validated). Up to 4 rows take the
+// f32 FMA kernel, which streams the weights once and decodes each weight
+// once for all rows; from 3 rows over large matrices (K and N >= 4096) its
+// four FMAs per weight make it VALU-bound and the matrix-core kernel is
+// faster (Q4_0, N = 13824, K = 5120, M = 4: 30.3 -> 17.9 us; N = 4096,
+// K = 14336: 18.9 -> 13.5 us; N = 14336, K = 4096: 18.1 -> 15.3 us; at the
+// FFN shapes, N = 8192, K = 2048 and N = 2048, K = 8192, the two are level
+// or the FMA kernel is faster). 9-16 rows over wide matrices take the
+// 32-row weight-slice kernel, and so does any K that is not a multiple of
+// 256 (the 16x16 kernel takes K in slices of 256).
+hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream)
+{
+    const bool matrix_cores = M > 2 && N >= 4096 && K >= 4096 && K % 256 == 0;
+    if (M <= qmm::kGemvRowsMax && !matrix_cores)
+        return qmm::launch_gemv_m1(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
+    if ((M > 8 && N >= 8192) || K % 256)
+        return qmm::launch_gemv_slices(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
+    return qmm::launch_gemv_small_m(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
+}
+
 int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const void *w,
                float *y, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
@@ -92,11 +113,9 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
             return finish(fn, qmm::launch_gemv_q4_k(x, wb, y, (int)M, (int)N, (int)K, stream));
         return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
     }
-    // Up to 4 rows the decode GEMV kernel streams the weights once with
-    // products rounded once in f32: faster than any matrix-core tiling there, and well
-    // inside this entry point's bound.
-    if (M <= qmm::kGemvRowsMax)
-        return finish(fn, qmm::launch_gemv_m1(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
+    // Up to 4 rows the GEMV's kernels (one pass over the weights): faster than
+    // any prefill tiling there, and well inside this entry point's bound.
+    if (M <= qmm::kGemvRowsMax) return finish(fn, gemv_launch(fmt, x, wb, y, M, N, K, stream));
     return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
 }
 
@@ -110,16 +129,7 @@ QMM_API int qmm_gemv_q4_0(const float *x, const void *w, float *y, int64_t M,
     const char *fn = "qmm_gemv_q4_0";
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
-    const uint8_t *wb = (const uint8_t *)w;
-    if (M <= qmm::kGemvRowsMax)
-        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N, (int)K,
-                                              stream));
-    // the 16x16 small-M kernel takes K in slices of 256
-    if ((M > 8 && N >= 8192) || K % 256)
-        return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
-                                                  (int)K, stream));
-    return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_0, x, wb, y, (int)M, (int)N,
-                                               (int)K, stream));
+    return finish(fn, gemv_launch(qmm::FMT_Q4_0, x, (const uint8_t *)w, y, M, N, K, stream));
 }
 
 QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
@@ -128,15 +138,7 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
     const char *fn = "qmm_gemv_q8_0";
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ8Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
-    const uint8_t *wb = (const uint8_t *)w;
-    if (M <= qmm::kGemvRowsMax)
-        return finish(fn, qmm::launch_gemv_m1(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N, (int)K,
-                                              stream));
-    if ((M > 8 && N >= 8192) || K % 256)
-        return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
-                                                  (int)K, stream));
-    return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q8_0, x, wb, y, (int)M, (int)N,
-                                               (int)K, stream));
+    return finish(fn, gemv_launch(qmm::FMT_Q8_0, x, (const uint8_t *)w, y, M, N, K, stream));
 }
 
 QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,

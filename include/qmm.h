@@ -91,7 +91,8 @@ typedef enum qmm_status {
  * several tokens share one pass over the weights). f32 accumulation; the
  * weights stream from HBM once per call. Up to 4 rows take f32 FMAs on
  * codes converted exactly to f32, and each row rounds as in a one-row call
- * of the same launch shape; 5 to 16 rows take the bf16 matrix cores: the
+ * of the same launch shape; 5 to 16 rows, and 3 or 4 rows where K >= 4096,
+ * N >= 4096 and K is a multiple of 256, take the bf16 matrix cores: the
  * codes are exact in bf16 and x is carried as two bf16 terms, hi = bf16(x)
  * and lo = bf16(x - hi), which represent x to within 2^-17 |x| (about 16 of
  * its 24 significand bits); each code-term product is exact, sums are f32
@@ -112,9 +113,8 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
  * Prefill GEMM over Q4_0 weights, any M >= 1 (M = prompt tokens). x is
  * rounded to bf16 (round-to-nearest-even) and each weight d * (q - 8) to
  * bf16 inside the kernel; products accumulate in f32 on the matrix cores.
- * M <= 4 runs the decode GEMV kernel instead (the same results as
- * qmm_gemv_q4_0, bit for bit), which is faster there and well inside this
- * bound.
+ * M <= 4 runs qmm_gemv_q4_0's kernels instead (the same results, bit for
+ * bit), which are faster there and well inside this bound.
  */
 QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

@@ -113,6 +113,15 @@ void gemv_entries()
     routed(qmm_gemv_q4_0, 9, 8192, 1024, "gemv_slices");
     routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // N < 8192
     routed(qmm_gemv_q8_0, 12, 8192, 1024, "gemv_slices");
+    // 3-4 rows over large matrices (K, N >= 4096, K % 256 == 0): matrix cores
+    for (Entry f : {qmm_gemv_q4_0, qmm_gemv_q8_0}) {
+        routed(f, 2, 4096, 4096, "gemv_m1");
+        routed(f, 3, 4096, 4096, "gemv_small_m");
+        routed(f, 4, 14336, 4096, "gemv_small_m");
+        routed(f, 4, 4095, 4096, "gemv_m1");
+        routed(f, 4, 4096, 4032, "gemv_m1");
+        routed(f, 4, 4096, 4160, "gemv_m1");                      // K % 256 != 0
+    }
 }
 
 void gemm_entries()
@@ -120,6 +129,7 @@ void gemm_entries()
     for (Entry f : {qmm_gemm_q4_0, qmm_gemm_q8_0}) {
         common_rejections(f, (int64_t)INT_MAX / 2);
         for (int64_t m = 1; m <= 4; ++m) routed(f, m, 257, 512, "gemv_m1");
+        routed(f, 4, 4096, 4096, "gemv_small_m");                 // as the GEMV
         routed(f, 5, 257, 512, "gemm");
         routed(f, 2048, 8192, 2048, "gemm");
         routed(f, (int64_t)INT_MAX / 2, 16, 64, "gemm");
