@@ -369,20 +369,21 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int 
 // several passes), so that a weight row stays within one wave and the
 // staged rows fit twice per compute unit's LDS. From timing sweeps on random
 // weights over matrix shapes from N = 2048 to 65536 and K = 2048 to 28672:
-//  * two rows past 32 chunks from N = 4096 loop over T = 32 in 256 threads
+//  * two rows past 32 chunks above N = 4096 loop over T = 32 in 256 threads
 //    (N = 13824, K = 5120: 25.2 -> 19.0 us; N = 28672, K = 8192: 51.6 ->
-//    45.4 us);
+//    45.4 us; at N = 4096, T = 64 in 512 threads stays faster);
 //  * four rows take two weight rows per thread (the pair kernel: each
 //    staged activation float4 read once for both, since at four rows those
 //    LDS reads set the pace) with T = 16 and 512 threads where that gives at
 //    least 192 workgroups (N >= 12288) and a row has 17-128 chunks (N =
 //    14336, K = 4096: 26.8 -> 16.1 us; N = 13824, K = 5120: 43.5 -> 19.3 us;
 //    N = 28672, K = 8192: 89.5 -> 57.6 us; N = 16384, K = 2048: 11.4 -> 9.9
-//    us), else past 32 chunks from N = 8192 T = 32 in 256 threads (N = 8192,
-//    K = 8192: 27.3 -> 18.5 us; K = 28672: 81.1 -> 59.2 us) and past 64
-//    chunks at N = 4096-8191 T = 64 in 512 threads (N = 4096, K = 14336:
-//    25.5 -> 19.6 us); 17-32 chunks at N = 8192-16383 keep one row per
-//    thread with T = 16 (FFN up shape 8.4 -> 6.7 us against T = 32).
+//    us), else past 32 chunks T = 32 in 256 threads above N = 4096 (N =
+//    8192, K = 8192: 27.3 -> 18.5 us; K = 28672: 81.1 -> 59.2 us; N = 6144,
+//    K = 4096: 12.6 -> 10.1 us) and T = 64 in 512 threads at N = 4096
+//    (exactly one 16-row workgroup per compute unit: K = 4096 8.9 -> 7.3 us;
+//    K = 14336 25.5 -> 19.1 us); 17-32 chunks at N = 8192-12287 keep one
+//    row per thread with T = 16 (FFN up shape 8.4 -> 6.7 us against T = 32).
 // Rows of a multi-row call round differently from a one-row call wherever
 // the two take different T.
 template <int MR>
@@ -392,11 +393,11 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
     if constexpr (MR == 4) {
         if (N >= 12288 && C > 16 && C <= 128)
             return launch<16, 512, MR, 2>(x, w, y, M, N, C, stream);
-        if (N >= 8192 && C > 32) return launch<32, 256, MR, 2>(x, w, y, M, N, C, stream);
         if (N >= 8192 && C > 16 && C <= 32) return launch<16, 512, MR>(x, w, y, M, N, C, stream);
-        if (N >= 4096 && C > 64) return launch<64, 512, MR, 2>(x, w, y, M, N, C, stream);
+        if (N > 4096 && C > 32) return launch<32, 256, MR, 2>(x, w, y, M, N, C, stream);
+        if (N == 4096 && C > 32) return launch<64, 512, MR, 2>(x, w, y, M, N, C, stream);
     } else {
-        if (N >= 4096 && C > 32) return launch<32, 256, MR>(x, w, y, M, N, C, stream);
+        if (N > 4096 && C > 32) return launch<32, 256, MR>(x, w, y, M, N, C, stream);
     }
     if (C <= 4) return launch<4, 256, MR>(x, w, y, M, N, C, stream);
     if (C <= 8) return launch<8, 256, MR>(x, w, y, M, N, C, stream);

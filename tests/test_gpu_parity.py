@@ -698,12 +698,13 @@ Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8
                     # per thread
                     (4, 8193, 1280),
                     # four rows, two weight rows per thread: T = 16 from N = 12288
-                    # (17-128 chunks), T = 32 past 32 chunks from N = 8192, T = 64
-                    # past 64 chunks from N = 4096; ragged N
+                    # (17-128 chunks), T = 32 past 32 chunks above N = 4096, T = 64
+                    # at N = 4096; ragged N
                     (3, 40000, 2048), (4, 12289, 2304), (3, 12300, 5120), (4, 16385, 2048),
-                    (4, 8200, 8448), (3, 9000, 5120), (4, 4100, 4608),
-                    # two rows past 32 chunks from N = 4096: T = 32
-                    (2, 4097, 2304), (2, 8192, 8448)]
+                    (4, 8200, 8448), (3, 9000, 5120), (4, 4100, 4608), (4, 4096, 3072),
+                    (3, 4096, 8448),
+                    # two rows past 32 chunks above N = 4096: T = 32; at N = 4096: T = 64
+                    (2, 4097, 2304), (2, 8192, 8448), (2, 4096, 4352)]
 
 
 @pytest.mark.parametrize("m,n,k", Q4_K_ROWS_SHAPES)
