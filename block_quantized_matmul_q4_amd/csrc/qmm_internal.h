@@ -21,7 +21,8 @@ inline constexpr int block_bytes(int fmt) { return fmt == FMT_Q4_0 ? kQ4Bytes : 
 // range; launch_gemv_small_m also needs K % 256 == 0. Each returns the
 // hipGetLastError() of its launch.
 // GEMV with f32 FMAs for M <= kGemvRowsMax activation rows (the weights
-// streamed once per launch); more rows take the matrix-core small-M kernel.
+// streamed once per launch); more rows, and for Q4_0 and Q8_0 three or four
+// rows over large matrices (K, N >= 4096), take the matrix-core kernels.
 constexpr int kGemvRowsMax = 4;
 hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, int M,
                           int N, int K, hipStream_t stream);
@@ -29,9 +30,9 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
                                int M, int N, int K, hipStream_t stream);
 // GEMV to the f32 bound on the matrix cores over 32-row weight slices (x as
 // two bf16 terms, within 2^-17 |x|), M <= 16
-// (taken for 9 <= M <= 16, Q8_0 and Q4_K only from N = 8192: Q4_0 at M = 16,
-// N = 8192, K = 2048 7.9 us against 10.6 us on the small-M kernel; Q8_0 at
-// N = 65536 54 against 79 us)
+// (taken for 9 <= M <= 16 from N = 8192, and for Q4_0 and Q8_0 wherever
+// K % 256 != 0: Q4_0 at M = 16, N = 8192, K = 2048 7.9 us against 10.6 us
+// on the small-M kernel; Q8_0 at N = 65536 54 against 79 us)
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream);
 // Gated FFN front half over Q4_0, M <= kGemvRowsMax activation rows.
