@@ -868,8 +868,11 @@ hipError_t launch_mid_auto(const float *x, const uint8_t *w, float *y, int M, in
     }
 }
 
-// More rows take the tile kernels: 256 x 256 tiles when there are at least
-// as many as compute units, else 128 x 128 ones. With at most 128 of those
+// More rows take the tile kernels: 256 x 256 tiles when they fill at least
+// three quarters of the compute units in one round (M = 1024, N = 14336,
+// K = 4096, 224 tiles: 169.6 -> 117.4 us against 128 x 128 tiles; M = 512,
+// N = 28672, K = 8192: 325.7 -> 229.6 us; at 112 tiles the two are level,
+// at 96 the smaller tiles are faster), else 128 x 128 ones. With at most 128 of those
 // (half the chip, each running the whole K loop; below N = 4096 fewer than
 // 128) the medium-M kernel's smaller tiles are faster (sweep at M =
 // 160-768: N = 8192, K = 2048, M = 160 26.0 -> 21.2 us; N = 4096, K = 4096,
@@ -884,7 +887,8 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
 {
     if (M <= kMidRowsMax) return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);
     const int64_t large_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (large_tiles >= kComputeUnits) return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
+    if (large_tiles >= kComputeUnits * 3 / 4)
+        return launch_tiles<FMT, TileLarge>(x, w, y, M, N, K, stream);
     const int64_t small_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     if (small_tiles < kComputeUnits / 2 || (N >= 4096 && small_tiles == kComputeUnits / 2))
         return launch_mid_auto<FMT>(x, w, y, M, N, K, stream);

@@ -56,7 +56,7 @@ CASES = [
     ("gemm_q8_0", 2, 300, 1024), ("gemm_q8_0", 64, 4100, 1024), ("gemm_q8_0", 2048, 8192, 512),
     ("gemm_q4_0", 20, 5000, 512), ("gemm_q4_0", 70, 4090, 512), ("gemm_q4_0", 80, 8150, 512),
     ("gemm_q4_0", 100, 8193, 512), ("gemm_q4_0", 200, 8150, 512),
-    ("gemm_q4_0", 512, 1024, 4096), ("gemm_q4_0", 2100, 1030, 512),
+    ("gemm_q4_0", 512, 1024, 4096), ("gemm_q4_0", 2100, 1030, 512), ("gemm_q4_0", 1024, 14336, 512),
     ("gemv_q4_k", 1, 8192, 2048), ("gemv_q4_k", 2, 300, 8192), ("gemv_q4_k", 4, 300, 1024),
     ("gemv_q4_k", 5, 300, 1024), ("gemv_q4_k", 8, 65536, 512), ("gemv_q4_k", 16, 8192, 2048),
     ("gemv_q4_k", 12, 4096, 1024), ("gemv_q4_k", 4, 8192, 2048), ("gemv_q4_k", 4, 8192, 8192),

@@ -239,10 +239,12 @@ def test_gemm_shapes(orc, fmt, m, n, k):
     check(orc, "gemm", fmt, m, n, k, seed=m + n)
 
 
-# Shapes with at least 256 tiles of 256 x 256 (the large-tile kernel; the
-# shapes above use the 128 x 128 one), with ragged M and N edges.
+# Shapes with at least 192 tiles of 256 x 256 (the large-tile kernel; the
+# shapes above use the 128 x 128 one), with ragged M and N edges; 220 tiles
+# (fewer than compute units) in the last.
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
-@pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512), (4097, 4100, 320)])
+@pytest.mark.parametrize("m,n,k", [(4097, 4100, 256), (4000, 4353, 512), (4097, 4100, 320),
+                                   (1000, 14000, 256)])
 def test_gemm_large_tile_shapes(orc, fmt, m, n, k):
     check(orc, "gemm", fmt, m, n, k, seed=m + n)
 

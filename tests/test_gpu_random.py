@@ -131,7 +131,7 @@ def draw_wide(i):
 def route_wide(m, n):
     """The GEMM's launch choice for 4 < M, N >= 4096 (its launch table, restated)."""
     if m > 128:
-        if -(-m // 256) * -(-n // 256) >= 256:
+        if -(-m // 256) * -(-n // 256) >= 192:
             return "tiles_256"
         if -(-m // 128) * -(-n // 128) > 128:
             return "tiles_128"

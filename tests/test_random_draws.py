@@ -10,7 +10,7 @@ def test_draw_covers_every_entry_point():
 
 
 def test_draw_wide_reaches_every_route():
-    # 256 x 256 tiles need at least 256 of them (M >= 2048 at these N): the
+    # 256 x 256 tiles need at least 192 of them (M >= 1536 at these N): the
     # fixed prefill shapes cover those
     seen = {route_wide(*draw_wide(i)[2:4]) for i in range(WIDE_CASES)}
     assert seen == {"mid_1x1", "mid_2x1", "mid_1x2", "mid_2x2", "mid_2x2_4waves", "tiles_128"}, seen
