@@ -113,6 +113,22 @@ CASES = [
     ("gemv", "q4_k", 12, 4000, 512), ("gemv", "q4_k", 4, 8200, 1280),
     ("gemm", "q4_k", 20, 300, 1024), ("gemm", "q4_k", 300, 300, 512),
     ("gemm", "q4_k", 80, 8150, 512),
+    # wide-matrix branches: one row with 64 threads per row past 64 pairs,
+    # two rows with two weight rows per thread, three and four rows on the
+    # matrix cores, 5-8 rows in 4- and 2-wave workgroups, 9-16 rows on the
+    # 16x16 kernel below N = 8192
+    ("gemv", "q4_0", 1, 4100, 8192), ("gemv", "q8_0", 2, 8200, 8448),
+    ("gemv", "q4_0", 4, 4100, 4352), ("gemv", "q8_0", 3, 4100, 4352),
+    ("gemv", "q4_0", 6, 10000, 1024), ("gemv", "q4_0", 7, 20000, 1024),
+    ("gemv", "q8_0", 6, 10000, 1024), ("gemv", "q4_0", 12, 4096, 2048),
+    # Q4_K: one and two rows with T = 32 past 64 / 32 chunks, four rows with
+    # two weight rows per thread (T = 16, 32, 64)
+    ("gemv", "q4_k", 1, 4100, 4352), ("gemv", "q4_k", 2, 4100, 2304),
+    ("gemv", "q4_k", 4, 12300, 2304), ("gemv", "q4_k", 4, 8200, 4352),
+    ("gemv", "q4_k", 4, 4096, 4352),
+    # GEMM: more than 128 rows over few tiles below N = 4096 (medium-M
+    # kernel), 256 x 256 tiles short of one per compute unit
+    ("gemm", "q4_0", 512, 1000, 1024), ("gemm", "q8_0", 1000, 14000, 128),
 ]
 
 
@@ -138,7 +154,7 @@ def test_nonfinite_scales(orc, entry, fmt, m, n, k):
 @pytest.mark.parametrize("k", [1024, 2048, 8192])
 @pytest.mark.parametrize("which", ["gate", "up"])
 def test_nonfinite_scales_ffn_gate_up(orc, k, which, m):
-    n = 300
+    n = 4100 if k == 8192 else 300     # past 32 pairs from N = 4096: T = 32 loops over K
     what = f"ffn_gate_up_q4_0 M={m} N={n} K={k} with +-Inf/NaN scales in {which}"
     print(f"[nonfinite] {what}", flush=True)
     x = synth.activations(m, k, seed=k)
