@@ -530,7 +530,13 @@ def test_ffn_gate_up_exact_cases(orc):
                                              ("gemm", "q4_0", 512, 1024, 2048),
                                              ("gemm", "q8_0", 300, 700, 1024),
                                              ("gemm", "q4_0", 80, 8150, 512),
-                                             ("gemm", "q4_0", 100, 8193, 512)])
+                                             ("gemm", "q4_0", 100, 8193, 512),
+                                             ("gemv", "q4_0", 4, 4096, 4096),
+                                             ("gemv", "q8_0", 7, 20000, 1024),
+                                             ("gemv", "q4_0", 12, 4096, 2048),
+                                             ("gemv", "q4_k", 4, 12300, 2304),
+                                             ("gemv", "q4_k", 4, 8200, 4352),
+                                             ("gemm", "q8_0", 1000, 14000, 128)])
 def test_bitwise_repeatable(entry, fmt, m, n, k):
     x = synth.activations(m, k, seed=21)
     w = weights(fmt, n, k, seed=21)
