@@ -183,13 +183,13 @@ def gemv_q8_0(x, w, n: int, k: int, out=None):
 
 def gemm_q4_0(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q4_0 W, any M
-    (M <= 4: the f32 GEMV result, bit for bit)."""
+    (M <= 4, and M <= 16 with N <= 4096: the GEMV result, bit for bit)."""
     return _call(qmm_gemm_q4_0, "q4_0", x, w, n, k, out)
 
 
 def gemm_q8_0(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q8_0 W, any M
-    (M <= 4: the f32 GEMV result, bit for bit)."""
+    (M <= 4, and M <= 16 with N <= 4096: the GEMV result, bit for bit)."""
     return _call(qmm_gemm_q8_0, "q8_0", x, w, n, k, out)
 
 

@@ -418,20 +418,35 @@ template <int FMT>
 hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                       hipStream_t stream)
 {
-    if (N < 8192) {
-        // fewer than 256 workgroups of 32 rows: 16 rows per workgroup, eight
-        // waves over K (seven for M > 8, whose A fragments take twice the
-        // LDS; Q4_0, M = 16, N = 4096, K = 14336: 34.0 us on the 32-row
-        // weight slices, 28.8 with six waves, 24.4 with seven and prefetch)
+    if (N <= 4096) {
+        // at most 128 workgroups of 32 rows: 16 rows per workgroup (one per
+        // compute unit), eight waves over K (seven for M > 8, whose A
+        // fragments take twice the LDS; Q4_0, M = 16, N = 4096, K = 14336:
+        // 34.0 us on the 32-row weight slices, 28.8 with six waves, 24.4 with
+        // seven and prefetch)
         if (M <= 8)
             launch_shape<FMT, true, 1, 8, true>(x, w, y, M, N, K, stream);
         else
             launch_shape<FMT, false, 1, 7, true>(x, w, y, M, N, K, stream);
     } else if (M > 8) {
         // 32 weight rows per workgroup, six waves over K (from a launch
-        // sweep at M = 12 and 16, K = 2048, N = 8192)
-        launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
+        // sweep at M = 12 and 16, K = 2048, N = 8192); below N = 8192 the
+        // 16-row workgroups above would need a second round (Q4_0, M = 16,
+        // N = 6144, K = 4096: 18.4 -> 13.3 us; Q8_0 20.3 -> 16.8 us)
+        if constexpr (FMT == FMT_Q8_0)
+            launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
+        else if (N < 8192)
+            launch_shape<FMT, false, 2, 6, true>(x, w, y, M, N, K, stream);
+        else
+            launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
+    } else if (FMT == FMT_Q8_0 && N < 8192) {
+        // Q8_0 between N = 4096 and 8192: 16 rows in 4 waves (N = 6144,
+        // K = 4096, M = 6: 13.7 -> 12.1 us)
+        launch_shape<FMT, true, 1, 4, true>(x, w, y, M, N, K, stream);
     } else if (N <= 8192) {
+        // 32 rows in 8 waves, one workgroup per compute unit in one round
+        // (between N = 4096 and 8192 in place of 16 rows: Q4_0, N = 6144,
+        // K = 4096, M = 6: 11.7 -> 9.4 us; Q4_K 13.1 -> 10.9 us)
         if (K <= 8 * KW)
             launch_shape<FMT, true, 2, 8, true>(x, w, y, M, N, K, stream);
         else

@@ -113,9 +113,13 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
             return finish(fn, qmm::launch_gemv_q4_k(x, wb, y, (int)M, (int)N, (int)K, stream));
         return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
     }
-    // Up to 4 rows the GEMV's kernels (one pass over the weights): faster than
-    // any prefill tiling there, and well inside this entry point's bound.
-    if (M <= qmm::kGemvRowsMax) return finish(fn, gemv_launch(fmt, x, wb, y, M, N, K, stream));
+    // Up to 4 rows, and up to 16 rows with N <= 4096, the GEMV's kernels (one
+    // pass over the weights, held to the tighter GEMV bound): faster than any
+    // prefill tiling there (N = 2048, K = 8192: M = 5 19.3 -> 8.9 us, M = 16
+    // 21.1 -> 15.2 us; N = 4096, K = 14336, M = 5: 27.8 -> 13.7 us), while
+    // from N = 6144 the medium-M GEMM is level or faster from 9 rows.
+    if (M <= qmm::kGemvRowsMax || (M <= QMM_GEMV_MAX_M && N <= 4096))
+        return finish(fn, gemv_launch(fmt, x, wb, y, M, N, K, stream));
     return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
 }
 

@@ -113,8 +113,9 @@ QMM_API int qmm_gemv_q8_0(const float *x, const void *w, float *y, int64_t M,
  * Prefill GEMM over Q4_0 weights, any M >= 1 (M = prompt tokens). x is
  * rounded to bf16 (round-to-nearest-even) and each weight d * (q - 8) to
  * bf16 inside the kernel; products accumulate in f32 on the matrix cores.
- * M <= 4 runs qmm_gemv_q4_0's kernels instead (the same results, bit for
- * bit), which are faster there and well inside this bound.
+ * M <= 4, and M <= 16 with N <= 4096, run qmm_gemv_q4_0's kernels instead
+ * (the same results, bit for bit), which are faster there and well inside
+ * this bound.
  */
 QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
@@ -122,7 +123,8 @@ QMM_API int qmm_gemm_q4_0(const float *x, const void *w, float *y, int64_t M,
 /*
  * Prefill GEMM over Q8_0 weights (a Q8_0 projection, e.g. the vocabulary
  * head, over many tokens): same contract as qmm_gemm_q4_0, each weight
- * d * q rounded once to bf16 (M <= 4: as qmm_gemv_q8_0).
+ * d * q rounded once to bf16 (M <= 4, and M <= 16 with N <= 4096: as
+ * qmm_gemv_q8_0).
  */
 QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

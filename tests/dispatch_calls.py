@@ -32,8 +32,10 @@ LIB_KERNELS = ("gemv_m1_kernel", "gemv_small_m_kernel", "gemv_slice_kernel", "ge
 GEMV = ("gemv_m1_kernel", "gemv_small_m_kernel", "gemv_slice_kernel")
 ROUTES = {
     "gemv_q4_0": GEMV, "gemv_q8_0": GEMV,
-    "gemm_q4_0": ("gemv_m1_kernel", "gemv_small_m_kernel", "gemm_kernel", "gemm_mid_kernel"),
-    "gemm_q8_0": ("gemv_m1_kernel", "gemv_small_m_kernel", "gemm_kernel", "gemm_mid_kernel"),
+    "gemm_q4_0": ("gemv_m1_kernel", "gemv_small_m_kernel", "gemv_slice_kernel", "gemm_kernel",
+                  "gemm_mid_kernel"),
+    "gemm_q8_0": ("gemv_m1_kernel", "gemv_small_m_kernel", "gemv_slice_kernel", "gemm_kernel",
+                  "gemm_mid_kernel"),
     "gemv_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemv_small_m_kernel",
                   "gemv_slice_kernel"),
     "gemm_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemm_kernel", "gemm_mid_kernel"),
@@ -49,6 +51,8 @@ CASES = [
     ("gemv_q4_0", 2, 4096, 8192), ("gemv_q4_0", 4, 4096, 8192), ("gemv_q8_0", 1, 2048, 8192),
     ("gemv_q4_0", 8, 16384, 2048), ("gemv_q8_0", 8, 16384, 2048), ("gemv_q4_0", 7, 65536, 2048),
     ("gemv_q4_0", 3, 4096, 4096), ("gemv_q8_0", 4, 14336, 4096), ("gemm_q4_0", 4, 4096, 4096),
+    ("gemv_q4_0", 6, 6144, 4096), ("gemv_q8_0", 6, 6144, 4096), ("gemv_q4_0", 16, 6144, 4096),
+    ("gemm_q4_0", 12, 2048, 8192), ("gemm_q8_0", 16, 4096, 320),
     ("gemv_q8_0", 1, 262144, 2048), ("gemv_q8_0", 2, 1000, 2048), ("gemv_q8_0", 4, 300, 8192),
     ("gemv_q8_0", 6, 300, 1024), ("gemv_q8_0", 12, 8192, 1024), ("gemv_q8_0", 12, 300, 1024),
     ("gemm_q4_0", 3, 300, 1024), ("gemm_q4_0", 16, 8192, 2048), ("gemm_q4_0", 100, 2048, 8192),

@@ -130,7 +130,11 @@ void gemm_entries()
         common_rejections(f, (int64_t)INT_MAX / 2);
         for (int64_t m = 1; m <= 4; ++m) routed(f, m, 257, 512, "gemv_m1");
         routed(f, 4, 4096, 4096, "gemv_small_m");                 // as the GEMV
-        routed(f, 5, 257, 512, "gemm");
+        routed(f, 5, 257, 512, "gemv_small_m");                   // M <= 16, N <= 4096
+        routed(f, 16, 4096, 512, "gemv_small_m");
+        routed(f, 12, 4096, 320, "gemv_slices");                  // K % 256 != 0
+        routed(f, 17, 257, 512, "gemm");
+        routed(f, 5, 4097, 512, "gemm");
         routed(f, 2048, 8192, 2048, "gemm");
         routed(f, (int64_t)INT_MAX / 2, 16, 64, "gemm");
         rejected(f, A, B, C, 5, QMM_GEMM_MAX_N + 1, 64, QMM_EUNSUPPORTED);

@@ -159,6 +159,9 @@ GEMV_SHAPES = [
     # 9-16 rows below N = 8192 over a ragged number of slices per wave
     (6, 65537, 1024), (7, 65536, 2560), (8, 8200, 2048), (6, 8192, 4096), (10, 4096, 14336),
     (16, 2048, 8448),
+    # 5-16 rows between N = 4096 and 8192: 32-row workgroups (Q8_0 with 5-8
+    # rows: 16 rows in 4 waves), ragged N, with and without prefetch
+    (6, 5000, 2048), (7, 6000, 4352), (12, 6000, 1024), (16, 4097, 2304),
     # 5-8 rows over wide matrices: 16 rows in 4 waves up to N = 12288, 32
     # rows in 4 waves up to 16384, then 2 waves (Q8_0: 16 rows in 4 waves)
     (6, 10000, 2304), (8, 12289, 2304), (5, 14336, 4096), (7, 20000, 4096),
@@ -195,11 +198,12 @@ def test_gemv_rows_match_single_row_bitwise(fmt, n, k):
             f"M={m}: {int((y != single[:m]).sum())} outputs differ from one-row calls"
 
 
-# The GEMM entry points hand M <= 4 to the decode GEMV kernel: the same
-# launches, so the same bits.
+# The GEMM entry points hand M <= 4, and M <= 16 with N <= 4096, to the
+# GEMV's kernels: the same launches, so the same bits.
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("m,n,k", [(1, 1000, 2048), (2, 257, 1024), (3, 333, 4096),
-                                   (4, 2049, 8192), (4, 4096, 4096), (3, 8192, 8448)])
+                                   (4, 2049, 8192), (4, 4096, 4096), (3, 8192, 8448),
+                                   (5, 2048, 8192), (12, 4096, 2048), (16, 300, 320)])
 def test_gemm_small_m_is_gemv(fmt, m, n, k):
     note(f"[bitwise] gemm_{fmt} vs gemv_{fmt} M={m} N={n} K={k}")
     x = synth.activations(m, k, seed=n)
@@ -745,7 +749,7 @@ Q4_K_MANY_ROWS_SHAPES = [
     (9, 8192, 2048), (12, 2049, 4352), (16, 8192, 2048), (16, 2048, 8192), (13, 17, 256),
     (16, 50, 65536), (11, 4099, 8448), (5, 1, 256), (10, 9000, 1024), (14, 65537, 256),
     (16, 8200, 65536), (9, 8193, 256), (12, 12000, 1280), (6, 65536, 2048), (8, 8192, 4096),
-    (7, 12300, 2048), (8, 10000, 1024),
+    (7, 12300, 2048), (8, 10000, 1024), (6, 5000, 2048), (13, 6000, 1024),
 ]
 
 
