@@ -74,18 +74,22 @@ int finish(const char *fn, hipError_t err)
 
 // The Q4_0 / Q8_0 GEMV for 1 <= M <= 16 (validated). Up to 4 rows take the
 // f32 FMA kernel, which streams the weights once and decodes each weight
-// once for all rows; from 3 rows over large matrices (K and N >= 4096) its
-// four FMAs per weight make it VALU-bound and the matrix-core kernel is
-// faster (Q4_0, N = 13824, K = 5120, M = 4: 30.3 -> 17.9 us; N = 4096,
-// K = 14336: 18.9 -> 13.5 us; N = 14336, K = 4096: 18.1 -> 15.3 us; at the
-// FFN shapes, N = 8192, K = 2048 and N = 2048, K = 8192, the two are level
-// or the FMA kernel is faster). 9-16 rows over wide matrices take the
-// 32-row weight-slice kernel, and so does any K that is not a multiple of
-// 256 (the 16x16 kernel takes K in slices of 256).
+// once for all rows; from 3 rows over large matrices (K and N >= 4096, or
+// K > 2048 with 2048 < N < 4096) its four FMAs per weight make it
+// VALU-bound and the matrix-core kernel is faster (Q4_0, M = 4: N = 13824,
+// K = 5120 30.3 -> 17.9 us; N = 4096, K = 14336 18.9 -> 13.5 us; N = 2304,
+// K = 8192 13.2 -> 8.5 us; N = 2560, K = 2560 6.0 -> 4.8 us; Q8_0 N = 3072,
+// K = 8192 15.3 -> 10.9 us). Up to N = 2048 (the FFN down shape, K = 8192:
+// 7.8 against 8.5 us) and at K = 2048 (level below N = 4096; the FFN up
+// shape, N = 8192) the FMA kernel is as fast or faster.
+// 9-16 rows over wide matrices take the 32-row weight-slice kernel, and so
+// does any K that is not a multiple of 256 (the 16x16 kernel takes K in
+// slices of 256).
 hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream)
 {
-    const bool matrix_cores = M > 2 && N >= 4096 && K >= 4096 && K % 256 == 0;
+    const bool large = (N >= 4096 && K >= 4096) || (N > 2048 && N < 4096 && K > 2048);
+    const bool matrix_cores = M > 2 && large && K % 256 == 0;
     if (M <= qmm::kGemvRowsMax && !matrix_cores)
         return qmm::launch_gemv_m1(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
     if ((M > 8 && N >= 8192) || K % 256)

@@ -113,14 +113,19 @@ void gemv_entries()
     routed(qmm_gemv_q4_0, 9, 8192, 1024, "gemv_slices");
     routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // N < 8192
     routed(qmm_gemv_q8_0, 12, 8192, 1024, "gemv_slices");
-    // 3-4 rows over large matrices (K, N >= 4096, K % 256 == 0): matrix cores
+    // 3-4 rows over large matrices (K % 256 == 0 and K, N >= 4096, or K > 2048
+    // with 2048 < N < 4096): matrix cores
     for (Entry f : {qmm_gemv_q4_0, qmm_gemv_q8_0}) {
         routed(f, 2, 4096, 4096, "gemv_m1");
         routed(f, 3, 4096, 4096, "gemv_small_m");
         routed(f, 4, 14336, 4096, "gemv_small_m");
-        routed(f, 4, 4095, 4096, "gemv_m1");
+        routed(f, 4, 4095, 4096, "gemv_small_m");
         routed(f, 4, 4096, 4032, "gemv_m1");
         routed(f, 4, 4096, 4160, "gemv_m1");                      // K % 256 != 0
+        routed(f, 3, 3072, 2304, "gemv_small_m");                 // 2048 < N < 4096, K > 2048
+        routed(f, 4, 2049, 8192, "gemv_small_m");
+        routed(f, 4, 2048, 8192, "gemv_m1");
+        routed(f, 4, 3072, 2048, "gemv_m1");
     }
 }
 
