@@ -81,7 +81,11 @@ int finish(const char *fn, hipError_t err)
 // K = 8192 13.2 -> 8.5 us; N = 2560, K = 2560 6.0 -> 4.8 us; Q8_0 N = 3072,
 // K = 8192 15.3 -> 10.9 us). Up to N = 2048 (the FFN down shape, K = 8192:
 // 7.8 against 8.5 us) and at K = 2048 (level below N = 4096; the FFN up
-// shape, N = 8192) the FMA kernel is as fast or faster.
+// shape, N = 8192) the FMA kernel is as fast or faster, except just past
+// K = 8192 between N = 1024 and 2048: the FMA kernel stages four rows of x
+// in chunks of 128 pairs, and a second, nearly empty chunk costs it almost
+// as much as the first (Q4_0, N = 1536, K = 8960: 11.3 against 9.1 us on
+// the matrix cores; level from K = 12288, and for Q8_0 from K = 9728).
 // 9-16 rows over wide matrices take the 32-row weight-slice kernel, and so
 // does any K that is not a multiple of 256 (the 16x16 kernel takes K in
 // slices of 256).
@@ -89,7 +93,9 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
                        int64_t N, int64_t K, hipStream_t stream)
 {
     const bool large = (N >= 4096 && K >= 4096) || (N > 2048 && N < 4096 && K > 2048);
-    const bool matrix_cores = M > 2 && large && K % 256 == 0;
+    const bool past_chunk = N >= 1024 && N <= 2048 && K > 8192 &&
+                            K <= (fmt == qmm::FMT_Q4_0 ? 11264 : 9216);
+    const bool matrix_cores = M > 2 && (large || past_chunk) && K % 256 == 0;
     if (M <= qmm::kGemvRowsMax && !matrix_cores)
         return qmm::launch_gemv_m1(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
     if ((M > 8 && N >= 8192) || K % 256)

@@ -22,8 +22,8 @@ inline constexpr int block_bytes(int fmt) { return fmt == FMT_Q4_0 ? kQ4Bytes : 
 // hipGetLastError() of its launch.
 // GEMV with f32 FMAs for M <= kGemvRowsMax activation rows (the weights
 // streamed once per launch); more rows, and for Q4_0 and Q8_0 three or four
-// rows over large matrices (K a multiple of 256 and K, N >= 4096, or
-// K > 2048 with 2048 < N < 4096), take the matrix-core kernels.
+// rows at the matrix shapes where the FMA kernel is the slower one (the
+// entry points choose), take the matrix-core kernels.
 constexpr int kGemvRowsMax = 4;
 hipError_t launch_gemv_m1(int fmt, const float *x, const uint8_t *w, float *y, int M,
                           int N, int K, hipStream_t stream);

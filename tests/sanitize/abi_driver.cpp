@@ -113,8 +113,9 @@ void gemv_entries()
     routed(qmm_gemv_q4_0, 9, 8192, 1024, "gemv_slices");
     routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // N < 8192
     routed(qmm_gemv_q8_0, 12, 8192, 1024, "gemv_slices");
-    // 3-4 rows over large matrices (K % 256 == 0 and K, N >= 4096, or K > 2048
-    // with 2048 < N < 4096): matrix cores
+    // 3-4 rows at some shapes (K % 256 == 0 and K, N >= 4096, or K > 2048
+    // with 2048 < N < 4096, or 1024 <= N <= 2048 with K just past 8192):
+    // matrix cores
     for (Entry f : {qmm_gemv_q4_0, qmm_gemv_q8_0}) {
         routed(f, 2, 4096, 4096, "gemv_m1");
         routed(f, 3, 4096, 4096, "gemv_small_m");
@@ -126,7 +127,13 @@ void gemv_entries()
         routed(f, 4, 2049, 8192, "gemv_small_m");
         routed(f, 4, 2048, 8192, "gemv_m1");
         routed(f, 4, 3072, 2048, "gemv_m1");
+        routed(f, 3, 1536, 8960, "gemv_small_m");                 // 1024 <= N <= 2048, K past 8192
+        routed(f, 4, 1024, 12288, "gemv_m1");
+        routed(f, 4, 1023, 8960, "gemv_m1");
     }
+    routed(qmm_gemv_q4_0, 4, 2048, 10240, "gemv_small_m");       // up to K = 11264
+    routed(qmm_gemv_q8_0, 4, 2048, 10240, "gemv_m1");            // up to K = 9216
+    routed(qmm_gemv_q8_0, 4, 2048, 9216, "gemv_small_m");
 }
 
 void gemm_entries()
