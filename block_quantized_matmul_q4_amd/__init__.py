@@ -200,7 +200,7 @@ def gemv_q4_k(x, w, n: int, k: int, out=None):
 
 def gemm_q4_k(x, w, n: int, k: int, out=None):
     """y[M, N] = bf16(x) @ bf16(W)^T with f32 accumulation, Q4_K W, any M
-    (M <= 4: the f32 GEMV result, bit for bit)."""
+    (M <= 4, and M <= 16 with N <= 4096: the GEMV result, bit for bit)."""
     return _call(qmm_gemm_q4_k, "q4_k", x, w, n, k, out)
 
 

@@ -103,6 +103,21 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
     return qmm::launch_gemv_small_m(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
 }
 
+// The Q4_K GEMV (validated, K % 256 == 0): up to 4 rows f32 FMAs on each
+// weight formed once; 5 to 16 rows the matrix-core kernels (codes exact in
+// bf16, x as two bf16 terms), 9 to 16 rows over wide matrices on 32-row
+// weight slices (N = 8192, K = 2048, M = 16: 8.3 against 11.4 us; N =
+// 65536: 53 against 82 us; level below).
+hipError_t gemv_q4_k_launch(const float *x, const uint8_t *w, float *y, int64_t M, int64_t N,
+                            int64_t K, hipStream_t stream)
+{
+    if (M > 8 && N >= 8192)
+        return qmm::launch_gemv_slices(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);
+    if (M > qmm::kGemvRowsMax)
+        return qmm::launch_gemv_small_m(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);
+    return qmm::launch_gemv_q4_k(x, w, y, (int)M, (int)N, (int)K, stream);
+}
+
 int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const void *w,
                float *y, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
@@ -115,12 +130,14 @@ int gemm_entry(const char *fn, int fmt, int block_bytes, const float *x, const v
                     "%s: N=%lld M=%lld unsupported (need N <= %d and at most %d tiles)", fn,
                     (long long)N, (long long)M, QMM_GEMM_MAX_N, INT_MAX - 8);
     const uint8_t *wb = (const uint8_t *)w;
-    // Q4_K: up to 4 rows take its GEMV (f32, each weight rounded once),
+    // Q4_K: up to 4 rows, and up to 16 rows with N <= 4096, take its GEMV,
     // which streams the weights once (FFN shapes, M = 2 and 4: 5.1 and 8.3 us
-    // against 9.6 us on the medium-M kernel; 6.3 and 8.1 against 20 us)
+    // against 9.6 us on the medium-M kernel; 6.3 and 8.1 against 20 us; M =
+    // 6: N = 2048, K = 8192 19.1 -> 10.9 us, N = 4096, K = 14336 30.5 -> 16.4
+    // us, N = 1024, K = 4096 9.9 -> 6.8 us)
     if (fmt == qmm::FMT_Q4_K) {
-        if (M <= qmm::kGemvRowsMax)
-            return finish(fn, qmm::launch_gemv_q4_k(x, wb, y, (int)M, (int)N, (int)K, stream));
+        if (M <= qmm::kGemvRowsMax || (M <= QMM_GEMV_MAX_M && N <= 4096))
+            return finish(fn, gemv_q4_k_launch(x, wb, y, M, N, K, stream));
         return finish(fn, qmm::launch_gemm(fmt, x, wb, y, (int)M, (int)N, (int)K, stream));
     }
     // Up to 4 rows, and up to 16 rows with N <= 4096, the GEMV's kernels (one
@@ -210,18 +227,7 @@ QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
     // weight as Q4_0's 18 per 32: the shared size and overlap checks apply
     int st = validate(fn, x, w, y, M, N, K, qmm::kQ4Bytes, QMM_GEMV_MAX_M);
     if (st != QMM_OK) return st;
-    // up to 4 rows: f32 FMAs on each weight formed once; 5 to 16 rows: the
-    // matrix-core kernels (codes exact in bf16, x as two bf16 terms), 9 to 16
-    // rows over wide matrices on 32-row weight slices (N = 8192, K = 2048,
-    // M = 16: 8.3 against 11.4 us; N = 65536: 53 against 82 us; level below)
-    if (M > 8 && N >= 8192)
-        return finish(fn, qmm::launch_gemv_slices(qmm::FMT_Q4_K, x, (const uint8_t *)w, y,
-                                                  (int)M, (int)N, (int)K, stream));
-    if (M > qmm::kGemvRowsMax)
-        return finish(fn, qmm::launch_gemv_small_m(qmm::FMT_Q4_K, x, (const uint8_t *)w, y,
-                                                   (int)M, (int)N, (int)K, stream));
-    return finish(fn, qmm::launch_gemv_q4_k(x, (const uint8_t *)w, y, (int)M, (int)N, (int)K,
-                                            stream));
+    return finish(fn, gemv_q4_k_launch(x, (const uint8_t *)w, y, M, N, K, stream));
 }
 
 QMM_API const char *qmm_status_string(int status)

@@ -188,9 +188,13 @@ QMM_API int qmm_gemv_q4_k(const float *x, const void *w, float *y, int64_t M,
  * pages' CLIP/CLAP path runs whole sequences through it): the contract of
  * qmm_gemm_q4_0, any M >= 1, with each weight d * sc * q - dmin * mn formed
  * in f32 (rounded once) and rounded to bf16 (nearest even); x rounded to
- * bf16, f32 accumulation. M <= 4 runs qmm_gemv_q4_k instead (f32). Errors as
- * for qmm_gemm_q4_0, plus QMM_EINVAL for K not a multiple of 256.
- * Accuracy: |y - sum_k x w| <= 8e-3 * sum_k |x w|.
+ * bf16, f32 accumulation. M <= 4, and M <= 16 with N <= 4096, run
+ * qmm_gemv_q4_k's kernels instead (the same results, bit for bit). Errors
+ * as for qmm_gemm_q4_0, plus QMM_EINVAL for K not a multiple of 256.
+ * Accuracy: |y - sum_k x w| <= 8e-3 * sum_k |x w|; where qmm_gemv_q4_k's
+ * kernels run, its bound, which for 5 to 16 rows exceeds this one only
+ * where the weights' scale and minimum terms cancel:
+ * sum_k (|d sc q| + |dmin mn|) |x| > 80 * sum_k |x w|.
  */
 QMM_API int qmm_gemm_q4_k(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);

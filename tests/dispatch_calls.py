@@ -38,7 +38,8 @@ ROUTES = {
                   "gemm_mid_kernel"),
     "gemv_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemv_small_m_kernel",
                   "gemv_slice_kernel"),
-    "gemm_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemm_kernel", "gemm_mid_kernel"),
+    "gemm_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemv_small_m_kernel", "gemm_kernel",
+                  "gemm_mid_kernel"),
     "ffn_gate_up_q4_0": ("gemv_m1_kernel",),
 }
 # (entry point, M, N, K): every launch branch of every entry point
@@ -68,6 +69,7 @@ CASES = [
     ("gemv_q4_k", 1, 4096, 8192), ("gemv_q4_k", 4, 16384, 2048), ("gemv_q4_k", 2, 4096, 4096),
     ("gemv_q4_k", 4, 4096, 8192),
     ("gemm_q4_k", 3, 300, 1024), ("gemm_q4_k", 40, 300, 1024), ("gemm_q4_k", 2048, 8192, 2048),
+    ("gemm_q4_k", 8, 2048, 8192), ("gemm_q4_k", 12, 5000, 1024),
     ("ffn_gate_up_q4_0", 1, 8192, 2048), ("ffn_gate_up_q4_0", 1, 2048, 8192),
     ("ffn_gate_up_q4_0", 2, 8192, 2048), ("ffn_gate_up_q4_0", 4, 2048, 8192),
     ("ffn_gate_up_q4_0", 1, 4096, 8192),

@@ -154,7 +154,10 @@ void gemm_entries()
     common_rejections(qmm_gemm_q4_k, (int64_t)INT_MAX / 2, QMM_EINVAL);
     rejected(qmm_gemm_q4_k, A, B, C, 5, 8, 320, QMM_EINVAL);    // not a multiple of 256
     routed(qmm_gemm_q4_k, 3, 257, 512, "gemv_q4_k");
-    routed(qmm_gemm_q4_k, 5, 257, 512, "gemm");
+    routed(qmm_gemm_q4_k, 5, 257, 512, "gemv_small_m");           // M <= 16, N <= 4096
+    routed(qmm_gemm_q4_k, 16, 4096, 512, "gemv_small_m");
+    routed(qmm_gemm_q4_k, 5, 4097, 512, "gemm");
+    routed(qmm_gemm_q4_k, 17, 257, 512, "gemm");
 }
 
 void q4_k_gemv()

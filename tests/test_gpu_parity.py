@@ -808,13 +808,14 @@ def test_gemv_q4_k_many_rows_exact(orc, m, n):
     assert np.all(run("gemv", "q4_k", x, w, n, k) == 0.0)
 
 
-# Q4_K through the prefill GEMM: M <= 4 takes the GEMV (bitwise), 5-128 rows
-# the medium-M kernel, more the tiles (small and large)
+# Q4_K through the prefill GEMM: M <= 4, and M <= 16 with N <= 4096, take the
+# GEMV (bitwise), other rows up to 128 the medium-M kernel, more the tiles
+# (small and large)
 Q4_K_GEMM_SHAPES = [
     (2048, 8192, 2048),                              # the prefill workload's shape
     (2, 300, 512), (4, 1000, 2048), (5, 257, 768), (33, 4097, 1024), (64, 8192, 2048),
     (128, 2049, 8192), (130, 257, 512), (300, 700, 1280), (1000, 2048, 8192),
-    (512, 1024, 2048), (257, 8193, 256),
+    (512, 1024, 2048), (257, 8193, 256), (12, 5000, 1024), (16, 4096, 1024), (17, 1000, 2048),
     # the medium-M launch choices from N = 4096 (as for Q4_0)
     (20, 5000, 512), (70, 4090, 512), (80, 8150, 512), (100, 8193, 1024), (200, 8150, 512),
 ]
@@ -825,9 +826,10 @@ def test_gemm_q4_k_shapes(orc, m, n, k):
     check(orc, "gemm", "q4_k", m, n, k, seed=m + n + k)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
-def test_gemm_q4_k_few_rows_is_gemv(m):
-    n, k = 3000, 2048
+@pytest.mark.parametrize("m,n", [(1, 3000), (2, 3000), (3, 3000), (4, 3000), (5, 3000),
+                                 (8, 4096), (16, 1000), (12, 2048)])
+def test_gemm_q4_k_few_rows_is_gemv(m, n):
+    k = 2048
     x = synth.activations(m, k, seed=35)
     w = synth.q4_k_weights(n, k, seed=35)
     note(f"[exact] gemm_q4_k M={m} is the GEMV")
