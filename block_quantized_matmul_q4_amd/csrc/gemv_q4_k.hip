@@ -374,11 +374,11 @@ hipError_t launch(const float *x, const uint8_t *w, float *y, int M, int N, int 
 //    45.4 us; at N = 4096, T = 64 in 512 threads stays faster);
 //  * four rows take two weight rows per thread (the pair kernel: each
 //    staged activation float4 read once for both, since at four rows those
-//    LDS reads set the pace) with T = 16 and 512 threads where that gives at
-//    least 192 workgroups (N >= 12288) and a row has 17-128 chunks (N =
-//    14336, K = 4096: 26.8 -> 16.1 us; N = 13824, K = 5120: 43.5 -> 19.3 us;
-//    N = 28672, K = 8192: 89.5 -> 57.6 us; N = 16384, K = 2048: 11.4 -> 9.9
-//    us), else past 32 chunks T = 32 in 256 threads above N = 4096 (N =
+//    LDS reads set the pace) with T = 16 and 512 threads above N = 8192
+//    where a row has 17-128 chunks (N = 14336, K = 4096: 26.8 -> 16.1 us;
+//    N = 13824, K = 5120: 43.5 -> 19.3 us; N = 28672, K = 8192: 89.5 ->
+//    57.6 us; N = 16384, K = 2048: 11.4 -> 9.9 us; N = 11008, K = 2048:
+//    11.2 -> 9.4 us), else past 32 chunks T = 32 in 256 threads above N = 4096 (N =
 //    8192, K = 8192: 27.3 -> 18.5 us; K = 28672: 81.1 -> 59.2 us; N = 6144,
 //    K = 4096: 12.6 -> 10.1 us) and T = 64 in 512 threads at N = 4096
 //    (exactly one 16-row workgroup per compute unit: K = 4096 8.9 -> 7.3 us;
@@ -391,7 +391,7 @@ hipError_t launch_rows(const float *x, const uint8_t *w, float *y, int M, int N,
                        hipStream_t stream)
 {
     if constexpr (MR == 4) {
-        if (N >= 12288 && C > 16 && C <= 128)
+        if (N > 8192 && C > 16 && C <= 128)
             return launch<16, 512, MR, 2>(x, w, y, M, N, C, stream);
         if (N >= 8192 && C > 16 && C <= 32) return launch<16, 512, MR>(x, w, y, M, N, C, stream);
         if (N > 4096 && C > 32) return launch<32, 256, MR, 2>(x, w, y, M, N, C, stream);

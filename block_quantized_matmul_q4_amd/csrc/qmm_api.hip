@@ -107,13 +107,27 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
 // weight formed once; 5 to 16 rows the matrix-core kernels (codes exact in
 // bf16, x as two bf16 terms), 9 to 16 rows over wide matrices on 32-row
 // weight slices (N = 8192, K = 2048, M = 16: 8.3 against 11.4 us; N =
-// 65536: 53 against 82 us; level below).
+// 65536: 53 against 82 us; level below). Three and four rows take the
+// matrix cores too where a timing sweep (N = 2048-28672, K = 2048-14336,
+// four rows) found them faster than every FMA launch shape: 2048 < N < 4096
+// from K = 4096 (N = 3072, K = 8192: 14.4 -> 10.5 us), N = 4096 from K =
+// 8192 (K = 14336: 18.9 -> 15.7 us), 8192 < N <= 12288 from K = 4096 (N =
+// 11008, K = 8192: 28.6 -> 24.5 us) and from K = 14336 at any N > 2048 (N =
+// 28672: 100.3 -> 89.5 us); the FMA kernels are faster or level elsewhere
+// (N <= 2048, K = 2048, N = 4097-8192 below K = 14336, N > 12288).
+bool q4_k_rows_on_matrix_cores(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 3 || N <= 2048) return false;
+    return K >= 14336 || (N < 4096 && K >= 4096) || (N == 4096 && K >= 8192) ||
+           (N > 8192 && N <= 12288 && K >= 4096);
+}
+
 hipError_t gemv_q4_k_launch(const float *x, const uint8_t *w, float *y, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream)
 {
     if (M > 8 && N >= 8192)
         return qmm::launch_gemv_slices(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);
-    if (M > qmm::kGemvRowsMax)
+    if (M > qmm::kGemvRowsMax || q4_k_rows_on_matrix_cores(M, N, K))
         return qmm::launch_gemv_small_m(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);
     return qmm::launch_gemv_q4_k(x, w, y, (int)M, (int)N, (int)K, stream);
 }

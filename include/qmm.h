@@ -169,10 +169,13 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
  * x is f32[M][K], y f32[M][N] (overwritten); the weights stream from HBM
  * once per call. Errors as for qmm_gemv_q4_0, plus QMM_EINVAL for K not a
  * multiple of 256 (qmm_gemm_q4_k takes any M).
- * Accuracy, 1 to 4 rows: each weight is formed once in f32 (one rounding)
- * and applied to every activation row in f32; a row of the result does not
- * depend on the other rows; |y - sum_k x w| <= 1e-4 * sum_k |x w|.
- * 5 to 16 rows (bf16 matrix cores): the nibbles are exact in bf16, x is
+ * Accuracy, 1 to 4 rows on the f32 FMA kernels: each weight is formed once
+ * in f32 (one rounding) and applied to every activation row in f32; a row
+ * of the result does not depend on the other rows;
+ * |y - sum_k x w| <= 1e-4 * sum_k |x w|.
+ * 5 to 16 rows, and 3 or 4 rows where N > 2048 and K >= 14336, N < 4096
+ * with K >= 4096, N = 4096 with K >= 8192, or 8192 < N <= 12288 with
+ * K >= 4096 (bf16 matrix cores): the nibbles are exact in bf16, x is
  * carried as two bf16 terms (within 2^-17 |x|, as in qmm_gemv_q4_0), and
  * per sub-block the f32 result is d*sc * sum(q x) - dmin*mn * sum(x), the
  * two sums taken from the same bf16 terms; since the two parts are rounded

@@ -67,7 +67,7 @@ CASES = [
     ("gemv_q4_k", 5, 300, 1024), ("gemv_q4_k", 8, 65536, 512), ("gemv_q4_k", 16, 8192, 2048),
     ("gemv_q4_k", 12, 4096, 1024), ("gemv_q4_k", 4, 8192, 2048), ("gemv_q4_k", 4, 8192, 8192),
     ("gemv_q4_k", 1, 4096, 8192), ("gemv_q4_k", 4, 16384, 2048), ("gemv_q4_k", 2, 4096, 4096),
-    ("gemv_q4_k", 4, 4096, 8192),
+    ("gemv_q4_k", 4, 4096, 8192), ("gemv_q4_k", 3, 3072, 8192), ("gemv_q4_k", 4, 11008, 2048),
     ("gemm_q4_k", 3, 300, 1024), ("gemm_q4_k", 40, 300, 1024), ("gemm_q4_k", 2048, 8192, 2048),
     ("gemm_q4_k", 8, 2048, 8192), ("gemm_q4_k", 12, 5000, 1024),
     ("ffn_gate_up_q4_0", 1, 8192, 2048), ("ffn_gate_up_q4_0", 1, 2048, 8192),

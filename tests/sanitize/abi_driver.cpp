@@ -168,6 +168,19 @@ void q4_k_gemv()
     for (int64_t m = 5; m <= QMM_GEMV_MAX_M; ++m) routed(qmm_gemv_q4_k, m, 300, 1280, "gemv_small_m");
     routed(qmm_gemv_q4_k, 16, 33, QMM_MAX_K, "gemv_small_m");
     routed(qmm_gemv_q4_k, 8, 8192, 2048, "gemv_small_m");
+    // three and four rows on the matrix cores at some shapes
+    routed(qmm_gemv_q4_k, 4, 3072, 4096, "gemv_small_m");        // 2048 < N < 4096, K >= 4096
+    routed(qmm_gemv_q4_k, 4, 3072, 3840, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 3, 4096, 8192, "gemv_small_m");        // N = 4096, K >= 8192
+    routed(qmm_gemv_q4_k, 4, 4096, 7936, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 4, 11008, 4096, "gemv_small_m");       // 8192 < N <= 12288, K >= 4096
+    routed(qmm_gemv_q4_k, 4, 11008, 2048, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 4, 12289, 4096, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 4, 8192, 8192, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 3, 28672, 14336, "gemv_small_m");      // any N > 2048, K >= 14336
+    routed(qmm_gemv_q4_k, 4, 2048, 14336, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 2, 3072, 8192, "gemv_q4_k");
+    routed(qmm_gemm_q4_k, 4, 3072, 4096, "gemv_small_m");
     for (int64_t m = 9; m <= QMM_GEMV_MAX_M; ++m) routed(qmm_gemv_q4_k, m, 8192, 2048, "gemv_slices");
 }
 
