@@ -481,8 +481,9 @@ def main():
                   w_up[(i + 1) % len(w_up)].data_ptr(), hf.data_ptr(), 1, up["N"], up["K"])
                  for i in range(0, 2 * n, 2)],
                 bytes=2 * w_up_h.nbytes + x_up_h.nbytes + hf.numel() * 4)
-        # the same over 2 and 4 tokens (batched decode)
-        for m in (2, 4):
+        # the same over 2 to 16 tokens (batched decode; from 5 tokens on the
+        # matrix cores)
+        for m in (2, 4, 8, 16):
             xm = torch.from_numpy(synth.activations(m, up["K"])).to(dev)
             hm = torch.empty((m, up["N"]), device=dev)
             keep += [xm, hm]

@@ -207,12 +207,6 @@ template <> struct Pair<FMT_Q8_0> {
 //     one-row call.
 // Every load is unconditional from a clamped in-bounds address: rows past N
 // are computed and dropped, pairs past P are masked by a select.
-__device__ __forceinline__ float gelu_tanh(float g)
-{
-    const float c = 0.7978845608028654f;        // sqrt(2 / pi)
-    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
-}
-
 template <int FMT, int T, int RPT, int CH, int WG, bool SX, bool NT, bool GATED, int MR>
 __global__ __launch_bounds__(WG) void gemv_m1_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,

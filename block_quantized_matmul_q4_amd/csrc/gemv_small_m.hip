@@ -230,10 +230,14 @@ __device__ __forceinline__ int afrag(int s)
     return 4 * s + 4 * (g + (g >> 3));
 }
 
-template <int FMT, bool PACK, int NT, int WAVES, bool PF>
+// GATED (NT = 2): the gated FFN front half. Weight tile 0 is rows n0 ..
+// n0 + 15 of the gate matrix w, tile 1 the same rows of the up matrix w2,
+// and the output is y[m][n] = gelu_tanh(gate) * up, formed in f32 once the
+// waves' sums are complete. Grid: ceil(N / 16) workgroups.
+template <int FMT, bool PACK, int NT, int WAVES, bool PF, bool GATED = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w,
-    float *__restrict__ y, int M, int N, int K)
+    float *__restrict__ y, int M, int N, int K, const uint8_t *__restrict__ w2 = nullptr)
 {
     using L = Fmt<FMT>;
     constexpr int TERMS = PACK ? 1 : 2;             // A operands per block
@@ -250,6 +254,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     static_assert(PPL * 64 == WROWS * PPW, "pairs must tile the wave");
     static_assert(PPW % PPL == 0, "a lane's pairs lie in one weight row");
     static_assert(WAVES * NT * 64 * 4 <= WAVES * REGION, "reduction fits in LDS");
+    static_assert(!GATED || NT == 2, "a gated tile is 16 gate rows and 16 up rows");
     __shared__ __attribute__((aligned(16))) uint32_t lds[WAVES * REGION];
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     uint32_t *wl = af + AF;
     const int P = K / 64;
     const int64_t row_bytes = (int64_t)P * L::kPairBytes;
-    const int n0 = blockIdx.x * WROWS;
+    const int n0 = blockIdx.x * (GATED ? 16 : WROWS);
 
     // A rows without an activation row stay zero for the whole kernel
     for (int i = lane; i < AF; i += 64) af[i] = 0u;
@@ -265,7 +270,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
     // this lane's weight pairs: row lrow of the tile, local pairs lp0 + u
     const int lrow = lane / (PPW / PPL);
     const int lp0 = (lane % (PPW / PPL)) * PPL;
-    const uint8_t *wsrc = w + (int64_t)min(n0 + lrow, N - 1) * row_bytes;
+    const uint8_t *wsrc;
+    if constexpr (GATED)
+        wsrc = (lrow < 16 ? w : w2) + (int64_t)min(n0 + lrow % 16, N - 1) * row_bytes;
+    else
+        wsrc = w + (int64_t)min(n0 + lrow, N - 1) * row_bytes;
 
     f32x4 acc[NT];
 #pragma unroll
@@ -371,6 +380,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_small_m_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
     __syncthreads();
+    if constexpr (GATED) {
+        for (int o = threadIdx.x; o < 16 * 16; o += 64 * WAVES) {
+            const int m = o / 16, c = o % 16;
+            const int n = n0 + c;
+            if (m >= M || n >= N) continue;
+            float s[2] = {0.f, 0.f};
+            for (int q = 0; q < WAVES; ++q) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    s[t] += red[(q * NT + t) * 64 + 16 * (m / 4) + c][m % 4];
+                    if constexpr (PACK)
+                        s[t] += red[(q * NT + t) * 64 + 16 * ((M + m) / 4) + c][(M + m) % 4];
+                }
+            }
+            y[(int64_t)m * N + n] = gelu_tanh(s[0] * L::kOutScale) * (s[1] * L::kOutScale);
+        }
+        return;
+    }
     for (int o = threadIdx.x; o < 16 * WROWS; o += 64 * WAVES) {
         const int m = o / WROWS, nl = o % WROWS;
         const int t = nl / 16, c = nl % 16;
@@ -469,6 +496,16 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
     return hipGetLastError();
 }
 
+// Gated FFN front half for 5-16 tokens: 16 gate and 16 up rows per
+// workgroup.
+template <bool PACK, int WAVES, bool PF>
+void launch_gated_shape(const float *x, const uint8_t *wg, const uint8_t *wu, float *h, int M,
+                        int N, int K, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemv_small_m_kernel<FMT_Q4_0, PACK, 2, WAVES, PF, true>),
+                       dim3((N + 15) / 16), dim3(64 * WAVES), 0, stream, x, wg, h, M, N, K, wu);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float *y,
@@ -477,6 +514,37 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
     if (fmt == FMT_Q4_K) return launch_fmt<FMT_Q4_K>(x, w, y, M, N, K, stream);
     return fmt == FMT_Q4_0 ? launch_fmt<FMT_Q4_0>(x, w, y, M, N, K, stream)
                            : launch_fmt<FMT_Q8_0>(x, w, y, M, N, K, stream);
+}
+
+// Gated launch shapes from a timing sweep (random weights, cold copies; N =
+// 2048-28672, M = 5, 8, 12, 16): as for the GEMV, the most waves whose
+// workgroups (N / 16 of them) all fit the chip at once. Up to 8 rows (13.5
+// KB of LDS per wave): 8 waves to N = 4096, 4 to N = 8192, 2 to N = 20480,
+// then 4 again (N = 28672, K = 8192, M = 5: 81.2 us, against 98.4 with 2
+// waves); 9-16 rows (22.3 KB per wave): 6 waves to N = 4096, else 3. Against
+// two GEMV launches for gate and up: N = 8192, K = 2048, M = 5 12.8 ->
+// 9.9 us, M = 16 16.3 -> 15.6 us; N = 13824, K = 5120, M = 5 35.8 -> 31.2
+// us; N = 4096, K = 4096, M = 16 20.0 -> 13.1 us.
+hipError_t launch_ffn_gate_up_small_m(const float *x, const uint8_t *w_gate,
+                                      const uint8_t *w_up, float *h, int M, int N, int K,
+                                      hipStream_t stream)
+{
+    if (M <= 8) {
+        if (N <= 4096)
+            launch_gated_shape<true, 8, true>(x, w_gate, w_up, h, M, N, K, stream);
+        else if (N <= 8192)
+            launch_gated_shape<true, 4, false>(x, w_gate, w_up, h, M, N, K, stream);
+        else if (N <= 20480)
+            launch_gated_shape<true, 2, true>(x, w_gate, w_up, h, M, N, K, stream);
+        else
+            launch_gated_shape<true, 4, true>(x, w_gate, w_up, h, M, N, K, stream);
+    } else {
+        if (N <= 4096)
+            launch_gated_shape<false, 6, true>(x, w_gate, w_up, h, M, N, K, stream);
+        else
+            launch_gated_shape<false, 3, true>(x, w_gate, w_up, h, M, N, K, stream);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace qmm

@@ -36,9 +36,13 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
 // on the small-M kernel; Q8_0 at N = 65536 54 against 79 us)
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream);
-// Gated FFN front half over Q4_0, M <= kGemvRowsMax activation rows.
+// Gated FFN front half over Q4_0, M <= kGemvRowsMax activation rows (f32
+// FMAs), and on the matrix cores for up to 16 rows (K % 256 == 0).
 hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8_t *w_up,
                               float *h, int M, int N, int K, hipStream_t stream);
+hipError_t launch_ffn_gate_up_small_m(const float *x, const uint8_t *w_gate,
+                                      const uint8_t *w_up, float *h, int M, int N, int K,
+                                      hipStream_t stream);
 // Q4_K GEMV, 1 to 4 activation rows (K % 256 == 0).
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream);
@@ -93,6 +97,14 @@ __device__ __forceinline__ void lds_only_barrier()
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// The gated FFN's activation, the tanh form of GELU, in f32:
+// gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+__device__ __forceinline__ float gelu_tanh(float g)
+{
+    const float c = 0.7978845608028654f;        // sqrt(2 / pi)
+    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
 }
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes

@@ -132,8 +132,8 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream);
 
 /*
- * Gated FFN front half over Q4_0 weights for 1 <= M <= 4 tokens (M = 1 for
- * one decoded token, 2..4 for batched or speculative decode; the step
+ * Gated FFN front half over Q4_0 weights for 1 <= M <= 16 tokens (M = 1 for
+ * one decoded token, 2..16 for batched or speculative decode; the step
  * either side of the path):
  *   h[m][n] = gelu_tanh(g[m][n]) * u[m][n],  g = x * W_gate^T,  u = x * W_up^T,
  *   gelu_tanh(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))).
@@ -142,10 +142,13 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
  * activation; the tanh form of GELU is the Gemma family's. W_gate and W_up
  * are both N rows of K/32 Q4_0 blocks (same layout as the GEMV's w); both
  * stream in one launch that reads x once. x is f32[M][K], h f32[M][N],
- * overwritten; each weight is decoded once for all rows and a row of h
- * equals the one-row result bit for bit. Errors as above, plus QMM_EINVAL
- * for a null or overlapping w_up, QMM_EALIGN for a w_up not 16-byte
- * aligned, QMM_EUNSUPPORTED for M > 4.
+ * overwritten; each weight is decoded once for all rows. Up to 4 rows take
+ * f32 FMAs, and a row of h equals the one-row result bit for bit; 5 to 16
+ * rows, and 3 or 4 where K % 256 == 0, K >= 4096, N >= 3072 and N is not
+ * between 4097 and 8191, take the bf16 matrix cores with x as two bf16
+ * terms (as qmm_gemv_q4_0). Errors as above, plus QMM_EINVAL for a null or
+ * overlapping w_up, QMM_EALIGN for a w_up not 16-byte aligned,
+ * QMM_EUNSUPPORTED for M > 4 with K not a multiple of 256.
  * Accuracy: g and u within the GEMV bound (1e-4 of their abs-sums); the
  * activation and product in f32.
  */

@@ -202,7 +202,7 @@ void gated()
     CHECK(gate_up(A, B, 0, C, 1, 300, 2048) == QMM_EINVAL);       // null w_up
     CHECK(gate_up(A, B, D + 2, C, 1, 300, 2048) == QMM_EALIGN);
     CHECK(gate_up(A, B, D, D + 32, 1, 300, 2048) == QMM_EINVAL);  // h inside w_up
-    CHECK(gate_up(A, B, D, C, 5, 300, 2048) == QMM_EUNSUPPORTED);
+    CHECK(gate_up(A, B, D, C, 5, 300, 2112) == QMM_EUNSUPPORTED);  // 5+ rows: K % 256
     CHECK(gate_up(A, B, D, C, 17, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(0, B, D, C, 1, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(A, B, D, C, 1, 300, 96) == QMM_EUNSUPPORTED);
@@ -212,6 +212,22 @@ void gated()
         CHECK(std::strcmp(g_stub.route, "ffn_gate_up") == 0 && g_stub.M == m && g_stub.N == 300);
     }
     CHECK(g_stub.calls == before + 4);
+    // 3-4 rows on the matrix cores from K = 4096 and N = 3072, outside
+    // 4096 < N < 8192
+    CHECK(gate_up(A, B, D, C, 3, 3072, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 8192, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 6144, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 2048, 8192) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 2, 8192, 8192) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 8192, 4160) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(g_stub.calls == before + 11);
+    for (int64_t m = 5; m <= QMM_GEMV_MAX_M; ++m) {
+        CHECK(gate_up(A, B, D, C, m, 300, 2048) == QMM_OK);
+        CHECK(std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0 && g_stub.M == m &&
+              g_stub.N == 300 && g_stub.K == 2048);
+    }
+    CHECK(g_stub.calls == before + 23);
 }
 
 void strings_and_threads()

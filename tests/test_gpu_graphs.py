@@ -38,6 +38,8 @@ CASES = [
     ("gemv", "q4_0", 8, 10000, 2048), ("gemv", "q4_0", 12, 4096, 2048),
     ("gemv", "q4_k", 4, 8200, 4352), ("gated", "q4_0", 3, 4100, 5120),
     ("gemm", "q4_0", 512, 1000, 1024), ("gemm", "q8_0", 1000, 14000, 128),
+    # the gated front half on the matrix cores (packed and apart)
+    ("gated", "q4_0", 8, 8192, 2048), ("gated", "q4_0", 12, 1000, 1024), ("gated", "q4_0", 4, 8192, 4096),
 ]
 
 

@@ -150,7 +150,7 @@ def test_nonfinite_scales(orc, entry, fmt, m, n, k):
         expect_nonfinite(y, yref, s, TAU_GEMM if entry == "gemm" else TAU_GEMV, planted, what)
 
 
-@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("m", [1, 3, 6, 12])
 @pytest.mark.parametrize("k", [1024, 2048, 8192])
 @pytest.mark.parametrize("which", ["gate", "up"])
 def test_nonfinite_scales_ffn_gate_up(orc, k, which, m):

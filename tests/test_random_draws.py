@@ -9,6 +9,11 @@ def test_draw_covers_every_entry_point():
     assert seen == set(ENTRIES)
 
 
+def test_draw_reaches_both_gated_paths():
+    gated = [draw(i)[2] for i in range(CASES) if draw(i)[0] == "ffn_gate_up_q4_0"]
+    assert any(m <= 4 for m in gated) and any(m > 8 for m in gated) and any(4 < m <= 8 for m in gated)
+
+
 def test_draw_wide_reaches_every_route():
     # 256 x 256 tiles need at least 192 of them (M >= 1536 at these N): the
     # fixed prefill shapes cover those
