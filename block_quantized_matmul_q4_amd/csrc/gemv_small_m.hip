@@ -434,7 +434,8 @@ void launch_shape(const float *x, const uint8_t *w, float *y, int M, int N, int 
 // once: 32 rows and 8 waves (one workgroup per CU) up to N = 8192; 16 rows
 // and 4 waves (three per CU, 768 in all) up to N = 12288 (Q4_0, N = 10240,
 // K = 4096: 18.0 -> 14.5 us; Q8_0 24.4 -> 18.6 us); 32 rows and 4 waves (two
-// per CU) up to N = 16384 (Q4_0, N = 14336, K = 4096: 18.5 -> 16.6 us).
+// per CU) up to N = 16384 (Q4_0, N = 14336, K = 4096: 18.5 -> 16.6 us; Q4_K
+// with the prefetch, N = 13824, K = 5120: 22.6 -> 21.3 us).
 // Beyond that Q4_0 runs 32 rows in 2-wave workgroups (N = 28672, K = 8192:
 // 58.0 -> 51.0 us; N = 128256, K = 4096: 116.2 -> 101.6 us), Q4_K 32 rows in
 // 4-wave ones (N = 65536, K = 4096: 73.1 -> 66.2 us), and Q8_0, whose weight
@@ -486,7 +487,7 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
     } else {
         if (N <= 12288)
             launch_shape<FMT, true, 1, 4, true>(x, w, y, M, N, K, stream);
-        else if (N <= 16384)
+        else if (N <= 16384 && FMT != FMT_Q4_K)
             launch_shape<FMT, true, 2, 4, false>(x, w, y, M, N, K, stream);
         else if constexpr (FMT == FMT_Q4_K)
             launch_shape<FMT, true, 2, 4, true>(x, w, y, M, N, K, stream);

@@ -767,7 +767,7 @@ Q4_K_MANY_ROWS_SHAPES = [
     (9, 8192, 2048), (12, 2049, 4352), (16, 8192, 2048), (16, 2048, 8192), (13, 17, 256),
     (16, 50, 65536), (11, 4099, 8448), (5, 1, 256), (10, 9000, 1024), (14, 65537, 256),
     (16, 8200, 65536), (9, 8193, 256), (12, 12000, 1280), (6, 65536, 2048), (8, 8192, 4096),
-    (7, 12300, 2048), (8, 10000, 1024), (6, 5000, 2048), (13, 6000, 1024),
+    (7, 12300, 2048), (8, 10000, 1024), (6, 5000, 2048), (13, 6000, 1024), (6, 14000, 4096),
 ]
 
 
