@@ -86,6 +86,10 @@ int finish(const char *fn, hipError_t err)
 // in chunks of 128 pairs, and a second, nearly empty chunk costs it almost
 // as much as the first (Q4_0, N = 1536, K = 8960: 11.3 against 9.1 us on
 // the matrix cores; level from K = 12288, and for Q8_0 from K = 9728).
+// Q4_0 rows over wide matrices (N >= 16384) take the matrix cores from
+// K = 1536 too (N = 151936, K = 1536: 60.6 -> 44.6 us; N = 262144, K =
+// 2048: 104.0 -> 91.3 us; level at N = 65536), while Q8_0's FMA kernel
+// stays faster there (M = 4, N = 262144: 122 against 147 us).
 // 9-16 rows over wide matrices take the 32-row weight-slice kernel, and so
 // does any K that is not a multiple of 256 (the 16x16 kernel takes K in
 // slices of 256).
@@ -95,7 +99,8 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
     const bool large = (N >= 4096 && K >= 4096) || (N > 2048 && N < 4096 && K > 2048);
     const bool past_chunk = N >= 1024 && N <= 2048 && K > 8192 &&
                             K <= (fmt == qmm::FMT_Q4_0 ? 11264 : 9216);
-    const bool matrix_cores = M > 2 && (large || past_chunk) && K % 256 == 0;
+    const bool wide = fmt == qmm::FMT_Q4_0 && N >= 16384 && K >= 1536;
+    const bool matrix_cores = M > 2 && (large || past_chunk || wide) && K % 256 == 0;
     if (M <= qmm::kGemvRowsMax && !matrix_cores)
         return qmm::launch_gemv_m1(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
     if ((M > 8 && N >= 8192) || K % 256)

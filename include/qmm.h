@@ -93,8 +93,9 @@ typedef enum qmm_status {
  * codes converted exactly to f32, and each row rounds as in a one-row call
  * of the same launch shape; 5 to 16 rows, and 3 or 4 rows where K is a
  * multiple of 256 and either K >= 4096 with N >= 4096, K > 2048 with
- * 2048 < N < 4096, or 1024 <= N <= 2048 with 8192 < K <= 11264 (Q4_0) or
- * K <= 9216 (Q8_0), take the bf16 matrix cores: the
+ * 2048 < N < 4096, 1024 <= N <= 2048 with 8192 < K <= 11264 (Q4_0) or
+ * K <= 9216 (Q8_0), or (Q4_0) N >= 16384 with K >= 1536, take the bf16
+ * matrix cores: the
  * codes are exact in bf16 and x is carried as two bf16 terms, hi = bf16(x)
  * and lo = bf16(x - hi), which represent x to within 2^-17 |x| (about 16 of
  * its 24 significand bits); each code-term product is exact, sums are f32

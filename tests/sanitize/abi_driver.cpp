@@ -134,6 +134,10 @@ void gemv_entries()
     routed(qmm_gemv_q4_0, 4, 2048, 10240, "gemv_small_m");       // up to K = 11264
     routed(qmm_gemv_q8_0, 4, 2048, 10240, "gemv_m1");            // up to K = 9216
     routed(qmm_gemv_q8_0, 4, 2048, 9216, "gemv_small_m");
+    routed(qmm_gemv_q4_0, 4, 16384, 1536, "gemv_small_m");       // Q4_0, N >= 16384, K >= 1536
+    routed(qmm_gemv_q8_0, 4, 16384, 1536, "gemv_m1");
+    routed(qmm_gemv_q4_0, 4, 16384, 1280, "gemv_m1");
+    routed(qmm_gemv_q4_0, 3, 16383, 2048, "gemv_m1");
 }
 
 void gemm_entries()

@@ -140,7 +140,7 @@ GEMV_SHAPES = [
     (2, 100, 1024), (4, 17, 512), (2, 1000, 2048), (4, 1000, 2048), (3, 333, 4096),
     (2, 2049, 8192), (4, 65, 16384), (3, 4099, 8448), (2, 65539, 1280), (3, 65537, 2048),
     (4, 4096, 4096), (3, 9000, 5120), (4, 4100, 4160), (4, 2560, 6912), (3, 3000, 3072),
-    (4, 2049, 2816), (4, 1536, 8960), (3, 2048, 10240),
+    (4, 2049, 2816), (4, 1536, 8960), (3, 2048, 10240), (4, 16400, 1536), (3, 40000, 2048),
     # 5-16 rows with N < 8192 (16-row matrix-core workgroups)
     (5, 2048, 8192), (12, 2049, 8448),
     # K at its maximum on the multi-row kernels
@@ -189,14 +189,16 @@ def test_gemv_shapes(orc, fmt, m, n, k):
 @pytest.mark.parametrize("n,k", [(1000, 1024), (8192, 2048), (333, 4096), (4099, 8448),
                                  (8200, 8448), (2049, 8192), (4100, 8256), (4095, 8448),
                                  (3000, 3072), (2048, 8192), (3000, 2048),
-                                 (1536, 8960), (1024, 9728), (2048, 11520)])
+                                 (1536, 8960), (1024, 9728), (2048, 11520), (16384, 2048),
+                                 (20000, 1536)])
 def test_gemv_rows_match_single_row_bitwise(fmt, n, k):
     note(f"[bitwise] gemv_{fmt} rows vs single-row calls N={n} K={k}")
     x = synth.activations(4, k, seed=n)
     w = weights(fmt, n, k, seed=n + 1)
     single = np.stack([run("gemv", fmt, x[m:m + 1], w, n, k)[0] for m in range(4)])
     large = (n >= 4096 and k >= 4096) or (2048 < n < 4096 and k > 2048) or \
-        (1024 <= n <= 2048 and 8192 < k <= (11264 if fmt == "q4_0" else 9216))
+        (1024 <= n <= 2048 and 8192 < k <= (11264 if fmt == "q4_0" else 9216)) or \
+        (fmt == "q4_0" and n >= 16384 and k >= 1536)
     matrix_cores = large and k % 256 == 0
     for m in ((2,) if matrix_cores else (2, 3, 4)):
         y = run("gemv", fmt, x[:m], w, n, k)
