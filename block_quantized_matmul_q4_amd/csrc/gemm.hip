@@ -902,15 +902,28 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
 {
     if (M > 16) return hipErrorInvalidValue;
     const dim3 grid((N + 31) / 32);
-    // Q4_0: 16 waves (more K steps in flight per slice: M = 16, N = 2048,
-    // K = 8192 20.3 us against 22.0 with 8); Q8_0: 8 (its wider windows)
-    if (fmt == FMT_Q4_0)
-        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 16>), grid, dim3(1024), 0, stream, x, w,
-                           y, M, N, K);
-    else if (fmt == FMT_Q4_K)
-        hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_K, 16>), grid, dim3(1024), 0, stream, x, w,
-                           y, M, N, K);
-    else
+    // Q4_0 and Q4_K: 8 waves from N = 8192 (a sweep of 4, 8 and 16 at M =
+    // 12 and 16: FFN up shape 8.3 -> 7.6 us, N = 28672, K = 8192 76.1 ->
+    // 68.3 us, N = 65536, K = 2048 53.0 -> 40.0 us, N = 262144 204.5 ->
+    // 150.0 us for Q4_0, M = 16), 16 on narrower matrices, which keep more
+    // K steps in flight per slice (M = 16, N = 2048, K = 8192 20.3 us
+    // against 22.0 with 8); Q8_0: 8 (its wider windows; level with 4)
+    const bool wide = N >= 8192;
+    if (fmt == FMT_Q4_0) {
+        if (wide)
+            hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 8>), grid, dim3(512), 0, stream, x, w,
+                               y, M, N, K);
+        else
+            hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 16>), grid, dim3(1024), 0, stream, x,
+                               w, y, M, N, K);
+    } else if (fmt == FMT_Q4_K) {
+        if (wide)
+            hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_K, 8>), grid, dim3(512), 0, stream, x, w,
+                               y, M, N, K);
+        else
+            hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_K, 16>), grid, dim3(1024), 0, stream, x,
+                               w, y, M, N, K);
+    } else
         hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q8_0, 8>), grid, dim3(512), 0, stream, x, w, y,
                            M, N, K);
     return hipGetLastError();

@@ -1,12 +1,12 @@
 // Small-M GEMV (2 <= M <= 16 activation rows: batched or speculative
 // decode) over GGUF Q4_0 / Q8_0 weights, and 5 <= M <= 16 over Q4_K
 // super-blocks, on the bf16 matrix cores. The C-ABI sends 5 <= M <= 8, and
-// 9 <= M <= 16 with N < 8192, here when K % 256 == 0 (each wave takes K in
-// slices of 256; always so for Q4_K), and for Q4_0 and Q8_0 also 3-4 rows
-// where K and N >= 4096: up to 4 rows the f32 FMA kernels that stream the
-// weights for one row are faster elsewhere (they decode each weight once
-// for all rows), and from 9 rows over wide matrices (N >= 8192) the 32-row
-// weight-slice kernel is.
+// 9 <= M <= 16 up to N = 4096 (below N = 3072 at K <= 2048), here when
+// K % 256 == 0 (each wave takes K in slices of 256; always so for Q4_K),
+// and 3-4 rows at the shapes where this kernel beats the f32 FMA kernels
+// that stream the weights for one row (they decode each weight once for
+// all rows); for 9 rows and more elsewhere the 32-row weight-slice kernel
+// is faster.
 //
 // With several activation rows the f32 FMA count (M per weight) outgrows
 // the weight stream, so the contraction moves to v_mfma_f32_16x16x32_bf16:
@@ -458,15 +458,10 @@ hipError_t launch_fmt(const float *x, const uint8_t *w, float *y, int M, int N, 
             launch_shape<FMT, false, 1, 7, true>(x, w, y, M, N, K, stream);
     } else if (M > 8) {
         // 32 weight rows per workgroup, six waves over K (from a launch
-        // sweep at M = 12 and 16, K = 2048, N = 8192); below N = 8192 the
-        // 16-row workgroups above would need a second round (Q4_0, M = 16,
-        // N = 6144, K = 4096: 18.4 -> 13.3 us; Q8_0 20.3 -> 16.8 us)
-        if constexpr (FMT == FMT_Q8_0)
-            launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
-        else if (N < 8192)
-            launch_shape<FMT, false, 2, 6, true>(x, w, y, M, N, K, stream);
-        else
-            launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
+        // sweep at M = 12 and 16, K = 2048, N = 8192). The entry points send
+        // 9-16 rows over N > 4096 to the 32-row weight slices, which are
+        // faster there, so this shape only backs the launcher's contract.
+        launch_shape<FMT, false, 2, 6, false>(x, w, y, M, N, K, stream);
     } else if (FMT == FMT_Q8_0 && N < 8192) {
         // Q8_0 between N = 4096 and 8192: 16 rows in 4 waves (N = 6144,
         // K = 4096, M = 6: 13.7 -> 12.1 us)

@@ -90,9 +90,18 @@ int finish(const char *fn, hipError_t err)
 // K = 1536 too (N = 151936, K = 1536: 60.6 -> 44.6 us; N = 262144, K =
 // 2048: 104.0 -> 91.3 us; level at N = 65536), while Q8_0's FMA kernel
 // stays faster there (M = 4, N = 262144: 122 against 147 us).
-// 9-16 rows over wide matrices take the 32-row weight-slice kernel, and so
-// does any K that is not a multiple of 256 (the 16x16 kernel takes K in
-// slices of 256).
+// 9-16 rows take the 32-row weight-slice kernel above N = 4096 and, from
+// N = 3072, at K <= 2048 (a sweep at M = 16, N = 3072-7168, K = 2048-14336,
+// all three formats: Q4_0, N = 6144, K = 2048 9.6 -> 6.7 us; Q4_K, K =
+// 8192 27.9 -> 21.0 us; Q8_0, N = 5120, K = 4096 16.9 -> 13.6 us; at
+// N <= 4096 from K = 4096 the 16x16 kernel stays faster, N = 4096, K =
+// 14336 24.7 against 34.2 us), and so does any K that is not a multiple of
+// 256 (the 16x16 kernel takes K in slices of 256).
+bool rows_on_slices(int64_t M, int64_t N, int64_t K)
+{
+    return M > 8 && (N > 4096 || (N >= 3072 && K <= 2048));
+}
+
 hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream)
 {
@@ -103,16 +112,16 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
     const bool matrix_cores = M > 2 && (large || past_chunk || wide) && K % 256 == 0;
     if (M <= qmm::kGemvRowsMax && !matrix_cores)
         return qmm::launch_gemv_m1(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
-    if ((M > 8 && N >= 8192) || K % 256)
+    if (rows_on_slices(M, N, K) || K % 256)
         return qmm::launch_gemv_slices(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
     return qmm::launch_gemv_small_m(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
 }
 
 // The Q4_K GEMV (validated, K % 256 == 0): up to 4 rows f32 FMAs on each
 // weight formed once; 5 to 16 rows the matrix-core kernels (codes exact in
-// bf16, x as two bf16 terms), 9 to 16 rows over wide matrices on 32-row
-// weight slices (N = 8192, K = 2048, M = 16: 8.3 against 11.4 us; N =
-// 65536: 53 against 82 us; level below). Three and four rows take the
+// bf16, x as two bf16 terms), 9 to 16 rows on 32-row weight slices where
+// the Q4_0 GEMV takes them (N = 8192, K = 2048, M = 16: 7.9 against 11.4
+// us; N = 6144, K = 8192: 21.0 against 27.9 us). Three and four rows take the
 // matrix cores too where a timing sweep (N = 2048-28672, K = 2048-14336,
 // four rows) found them faster than every FMA launch shape: 2048 < N < 4096
 // from K = 4096 (N = 3072, K = 8192: 14.4 -> 10.5 us), N = 4096 from K =
@@ -130,7 +139,7 @@ bool q4_k_rows_on_matrix_cores(int64_t M, int64_t N, int64_t K)
 hipError_t gemv_q4_k_launch(const float *x, const uint8_t *w, float *y, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream)
 {
-    if (M > 8 && N >= 8192)
+    if (rows_on_slices(M, N, K))
         return qmm::launch_gemv_slices(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);
     if (M > qmm::kGemvRowsMax || q4_k_rows_on_matrix_cores(M, N, K))
         return qmm::launch_gemv_small_m(qmm::FMT_Q4_K, x, w, y, (int)M, (int)N, (int)K, stream);

@@ -31,9 +31,10 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
                                int M, int N, int K, hipStream_t stream);
 // GEMV to the f32 bound on the matrix cores over 32-row weight slices (x as
 // two bf16 terms, within 2^-17 |x|), M <= 16
-// (taken for 9 <= M <= 16 from N = 8192, and for Q4_0 and Q8_0 wherever
-// K % 256 != 0: Q4_0 at M = 16, N = 8192, K = 2048 7.9 us against 10.6 us
-// on the small-M kernel; Q8_0 at N = 65536 54 against 79 us)
+// (taken for 9 <= M <= 16 above N = 4096 and, from N = 3072, at K <= 2048,
+// and for Q4_0 and Q8_0 wherever K % 256 != 0: Q4_0 at M = 16, N = 8192,
+// K = 2048 7.6 us against 10.6 us on the small-M kernel; Q8_0 at N = 65536
+// 54 against 79 us)
 hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *y, int M,
                               int N, int K, hipStream_t stream);
 // Gated FFN front half over Q4_0, M <= kGemvRowsMax activation rows (f32

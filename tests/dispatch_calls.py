@@ -53,7 +53,7 @@ CASES = [
     ("gemv_q4_0", 8, 16384, 2048), ("gemv_q8_0", 8, 16384, 2048), ("gemv_q4_0", 7, 65536, 2048),
     ("gemv_q4_0", 3, 4096, 4096), ("gemv_q8_0", 4, 14336, 4096), ("gemm_q4_0", 4, 4096, 4096),
     ("gemv_q4_0", 4, 2560, 6912), ("gemv_q8_0", 3, 3072, 3072), ("gemv_q4_0", 4, 1536, 8960),
-    ("gemv_q4_0", 4, 32768, 2048),
+    ("gemv_q4_0", 4, 32768, 2048), ("gemv_q4_0", 12, 5000, 2048), ("gemv_q4_k", 12, 5000, 8192),
     ("gemv_q4_0", 6, 6144, 4096), ("gemv_q8_0", 6, 6144, 4096), ("gemv_q4_0", 16, 6144, 4096),
     ("gemm_q4_0", 12, 2048, 8192), ("gemm_q8_0", 16, 4096, 320),
     ("gemv_q8_0", 1, 262144, 2048), ("gemv_q8_0", 2, 1000, 2048), ("gemv_q8_0", 4, 300, 8192),

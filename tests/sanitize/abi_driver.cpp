@@ -109,10 +109,16 @@ void gemv_entries()
     routed(qmm_gemv_q8_0, 16, 33, QMM_MAX_K, "gemv_small_m");
     routed(qmm_gemv_q4_0, 5, 300, 1024, "gemv_small_m");
     routed(qmm_gemv_q4_0, 8, 8192, 2048, "gemv_small_m");
-    routed(qmm_gemv_q4_0, 9, 300, 1024, "gemv_small_m");         // N < 8192
+    // 9-16 rows: weight slices above N = 4096, and from N = 3072 at K <= 2048
+    routed(qmm_gemv_q4_0, 9, 300, 1024, "gemv_small_m");
     routed(qmm_gemv_q4_0, 9, 8192, 1024, "gemv_slices");
-    routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");        // N < 8192
+    routed(qmm_gemv_q8_0, 12, 300, 1024, "gemv_small_m");
     routed(qmm_gemv_q8_0, 12, 8192, 1024, "gemv_slices");
+    routed(qmm_gemv_q4_0, 12, 4097, 8192, "gemv_slices");
+    routed(qmm_gemv_q4_0, 12, 4096, 4096, "gemv_small_m");
+    routed(qmm_gemv_q8_0, 16, 3072, 2048, "gemv_slices");
+    routed(qmm_gemv_q8_0, 16, 3071, 2048, "gemv_small_m");
+    routed(qmm_gemv_q4_0, 16, 3072, 2304, "gemv_small_m");
     // 3-4 rows at some shapes (K % 256 == 0 and K, N >= 4096, or K > 2048
     // with 2048 < N < 4096, or 1024 <= N <= 2048 with K just past 8192):
     // matrix cores
@@ -147,7 +153,8 @@ void gemm_entries()
         for (int64_t m = 1; m <= 4; ++m) routed(f, m, 257, 512, "gemv_m1");
         routed(f, 4, 4096, 4096, "gemv_small_m");                 // as the GEMV
         routed(f, 5, 257, 512, "gemv_small_m");                   // M <= 16, N <= 4096
-        routed(f, 16, 4096, 512, "gemv_small_m");
+        routed(f, 16, 4096, 512, "gemv_slices");                  // as the GEMV
+        routed(f, 16, 2048, 512, "gemv_small_m");
         routed(f, 12, 4096, 320, "gemv_slices");                  // K % 256 != 0
         routed(f, 17, 257, 512, "gemm");
         routed(f, 5, 4097, 512, "gemm");
@@ -159,7 +166,10 @@ void gemm_entries()
     rejected(qmm_gemm_q4_k, A, B, C, 5, 8, 320, QMM_EINVAL);    // not a multiple of 256
     routed(qmm_gemm_q4_k, 3, 257, 512, "gemv_q4_k");
     routed(qmm_gemm_q4_k, 5, 257, 512, "gemv_small_m");           // M <= 16, N <= 4096
-    routed(qmm_gemm_q4_k, 16, 4096, 512, "gemv_small_m");
+    routed(qmm_gemm_q4_k, 16, 4096, 512, "gemv_slices");
+    routed(qmm_gemm_q4_k, 16, 2048, 512, "gemv_small_m");
+    routed(qmm_gemv_q4_k, 12, 5000, 8192, "gemv_slices");
+    routed(qmm_gemv_q4_k, 12, 4096, 4096, "gemv_small_m");
     routed(qmm_gemm_q4_k, 5, 4097, 512, "gemm");
     routed(qmm_gemm_q4_k, 17, 257, 512, "gemm");
 }

@@ -32,10 +32,11 @@ CASES = [
     ("gated", "q4_0", 1, 8192, 2048), ("gated", "q4_0", 4, 2048, 8192),
     # wide-matrix branches: 64 threads per row past 64 pairs, matrix-core
     # 3-4 rows, 5-8 rows in 4-wave workgroups with prefetch, 9-16 rows on the
-    # 16x16 kernel below N = 8192, the Q4_K pair kernel, the gated kernel
+    # 16x16 kernel up to N = 4096 and on 16-wave slices below N = 8192, the
+    # Q4_K pair kernel, the gated kernel
     # looping over 32-pair chunks, few-tile and 220-tile GEMMs
     ("gemv", "q4_0", 1, 4100, 8192), ("gemv", "q8_0", 4, 4096, 4096),
-    ("gemv", "q4_0", 8, 10000, 2048), ("gemv", "q4_0", 12, 4096, 2048),
+    ("gemv", "q4_0", 8, 10000, 2048), ("gemv", "q4_0", 12, 4096, 4096), ("gemv", "q4_0", 12, 5000, 2048),
     ("gemv", "q4_k", 4, 8200, 4352), ("gated", "q4_0", 3, 4100, 5120),
     ("gemm", "q4_0", 512, 1000, 1024), ("gemm", "q8_0", 1000, 14000, 128),
     # the gated front half on the matrix cores (packed and apart)

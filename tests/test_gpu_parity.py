@@ -147,9 +147,11 @@ GEMV_SHAPES = [
     (2, 40, 65536), (8, 65, 65536), (16, 33, 65536),
     # one row, wide N, K <= 4096 (32 lanes x 2 chunks per row, ragged K)
     (1, 32769, 3328),
-    # 9-16 rows with N >= 8192 (f32-exact 32-row weight slices): ragged M and
+    # 9-16 rows on the 32-row weight slices (8 waves from N = 8192, 16
+    # below; above N = 4096, and from N = 3072 at K <= 2048): ragged M and
     # N, K steps not a multiple of the waves, wide N
     (9, 8193, 1024), (12, 8192, 8448), (16, 65537, 512), (13, 9000, 256),
+    (12, 5000, 8192), (16, 3072, 2048), (10, 7000, 4352), (14, 4097, 14336), (9, 3100, 1280),
     # K > 4096 from N = 4096 (64 threads per row looping over K; two weight
     # rows per thread at M = 4, and at M = 2 from N = 8192, K = 8192): ragged
     # N and a last chunk of 1-8 pairs
@@ -157,11 +159,12 @@ GEMV_SHAPES = [
     # 5-16 rows on the 16x16 kernel with next-slice prefetch: 2-wave
     # workgroups from N = 65536 (several slices per wave), 32 weight rows at
     # K = 2048 (ragged N) and without prefetch over two slices per wave, and
-    # 9-16 rows below N = 8192 over a ragged number of slices per wave
+    # 9-16 rows up to N = 4096 over a ragged number of slices per wave
     (6, 65537, 1024), (7, 65536, 2560), (8, 8200, 2048), (6, 8192, 4096), (10, 4096, 14336),
-    (16, 2048, 8448),
-    # 5-16 rows between N = 4096 and 8192: 32-row workgroups (Q8_0 with 5-8
-    # rows: 16 rows in 4 waves), ragged N, with and without prefetch
+    (16, 2048, 8448), (16, 4096, 8192), (12, 3071, 2048),
+    # 5-8 rows between N = 4096 and 8192: 32-row workgroups (Q8_0: 16 rows
+    # in 4 waves), ragged N, with and without prefetch; 9-16 rows there on
+    # the weight slices
     (6, 5000, 2048), (7, 6000, 4352), (12, 6000, 1024), (16, 4097, 2304),
     # 5-8 rows over wide matrices: 16 rows in 4 waves up to N = 12288, 32
     # rows in 4 waves up to 16384, then 2 waves (Q8_0: 16 rows in 4 waves)
