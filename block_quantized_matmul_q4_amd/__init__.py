@@ -205,8 +205,7 @@ def gemm_q4_k(x, w, n: int, k: int, out=None):
 
 
 def ffn_gate_up_q4_0(x, w_gate, w_up, n: int, k: int, out=None):
-    """h[M, N] = gelu_tanh(x @ W_gate^T) * (x @ W_up^T) for Q4_0 W_gate, W_up (1 <= M <= 16;
-    5-16 rows need K a multiple of 256)."""
+    """h[M, N] = gelu_tanh(x @ W_gate^T) * (x @ W_up^T) for Q4_0 W_gate, W_up (1 <= M <= 16)."""
     import torch
 
     if not isinstance(w_up, torch.Tensor):

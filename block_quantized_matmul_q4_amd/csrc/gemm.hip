@@ -675,10 +675,17 @@ hipError_t launch_mid(const float *x, const uint8_t *w, float *y, int M, int N, 
 // scale is d sc, and dmin mn times the sum of the block's activations (two
 // more MFMAs of the same A operand against a B operand of ones) is
 // subtracted in f32.
-template <int FMT, int WAVES>
+// GATED (Q4_0): the gated FFN front half. Weight rows 0-15 of the slice are
+// rows n0 .. n0 + 15 of the gate matrix w, rows 16-31 the same rows of the
+// up matrix w2, and the output is y[m][n] = gelu_tanh(gate) * up in f32.
+// Each lane issues its window loads against both matrices' buffer
+// resources, the one it does not own at an offset past the resource's end,
+// which the hardware's range check answers with zeros: the loads stay
+// branch-free and the two results are merged with an OR. Grid: ceil(N / 16).
+template <int FMT, int WAVES, bool GATED = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ w, float *__restrict__ y,
-    int M, int N, int K)
+    int M, int N, int K, const uint8_t *__restrict__ w2 = nullptr)
 {
     using BF = BFmt<FMT>;
     constexpr int BM = 32, BN = 32;
@@ -691,7 +698,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
     // compiler knows it (and the K steps derived from it) to be uniform, so
     // the buffer loads' scalar offsets need no per-lane loop
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
-    const int n0 = blockIdx.x * BN;
+    const int n0 = blockIdx.x * (GATED ? BN / 2 : BN);
     const int P = K / 64;
     const int row_bytes = P * BF::kPairBytes;
     __bf16 *As = lds + wave * REGION;
@@ -700,14 +707,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
 
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(x), 0, M * K * 4, kBufferWord3);
+    const int b_len = min(GATED ? BN / 2 : BN, N - n0) * row_bytes;
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, min(BN, N - n0) * row_bytes,
-        kBufferWord3);
+        const_cast<uint8_t *>(w + (int64_t)n0 * row_bytes), 0, b_len, kBufferWord3);
     // activation row lane / 16 + 4 u (u < 4), columns 4 (lane % 16) .. +3
     const int a_col = 4 * (lane % 16);
     const int a_voff0 = ((lane / 16) * K + a_col) * 4;
     const int b_row = lane / 2, b_blk = lane % 2;
-    const int b_roff = b_row * row_bytes;
+    const int b_roff = (GATED ? b_row % 16 : b_row) * row_bytes;
 
     float4 a_reg[4];
     uint32_t b_reg[BF::kWin];
@@ -718,7 +725,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
                 a_rsrc, a_voff0 + 16 * K * u, p * 256, 0);
             a_reg[u] = __builtin_bit_cast(float4, v);
         }
-        BF::load_step(b_rsrc, b_roff, b_blk, p, b_reg);
+        if constexpr (GATED) {
+            // gate rows from w, up rows from w2; the other load lands past
+            // its resource's end and reads zeros
+            const __amdgpu_buffer_rsrc_t u_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(w2 + (int64_t)n0 * row_bytes), 0, b_len, kBufferWord3);
+            uint32_t u_reg[BF::kWin];
+            BF::load_step(b_rsrc, b_row < 16 ? b_roff : b_len, b_blk, p, b_reg);
+            BF::load_step(u_rsrc, b_row < 16 ? b_len : b_roff, b_blk, p, u_reg);
+#pragma unroll
+            for (int i = 0; i < BF::kWin; ++i) b_reg[i] |= u_reg[i];
+        } else {
+            BF::load_step(b_rsrc, b_roff, b_blk, p, b_reg);
+        }
     };
 
     f32x16 acc;
@@ -790,6 +809,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_slice_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
     __syncthreads();
+    if constexpr (GATED) {
+        // column c < 16 of the tile is gate row n0 + c, column c + 16 the
+        // same up row
+        for (int o = threadIdx.x; o < 8 * 64; o += 64 * WAVES) {
+            const int l = o % 64, e = o / 64;
+            if (l % 32 >= 16) continue;
+            const int m = 8 * (e / 4) + 4 * (l / 32) + e % 4;
+            const int n = n0 + l % 32;
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int q = 0; q < WAVES; ++q) {
+                g += red[(q * 16 + e) * 64 + l];
+                u += red[(q * 16 + e) * 64 + l + 16];
+            }
+            float g_lo = 0.f, u_lo = 0.f;
+#pragma unroll
+            for (int q = 0; q < WAVES; ++q) {
+                g_lo += red[(q * 16 + e + 8) * 64 + l];
+                u_lo += red[(q * 16 + e + 8) * 64 + l + 16];
+            }
+            if (m < M && n < N)
+                y[(int64_t)m * N + n] =
+                    gelu_tanh((g + g_lo) * BF::kCodeScale) * ((u + u_lo) * BF::kCodeScale);
+        }
+        return;
+    }
     for (int o = threadIdx.x; o < 8 * 64; o += 64 * WAVES) {
         const int l = o % 64, e = o / 64;
         const int m = 8 * (e / 4) + 4 * (l / 32) + e % 4;
@@ -926,6 +971,16 @@ hipError_t launch_gemv_slices(int fmt, const float *x, const uint8_t *w, float *
     } else
         hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q8_0, 8>), grid, dim3(512), 0, stream, x, w, y,
                            M, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_gate_up_slices(const float *x, const uint8_t *w_gate,
+                                     const uint8_t *w_up, float *h, int M, int N, int K,
+                                     hipStream_t stream)
+{
+    if (M > 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_slice_kernel<FMT_Q4_0, 8, true>), dim3((N + 15) / 16), dim3(512), 0,
+                       stream, x, w_gate, h, M, N, K, w_up);
     return hipGetLastError();
 }
 

@@ -236,8 +236,10 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
     const uint64_t w_len = (uint64_t)N * (uint64_t)(K / 32) * (uint64_t)qmm::kQ4Bytes;
     if (overlaps((uintptr_t)h, (uint64_t)M * (uint64_t)N * 4u, (uintptr_t)w_up, w_len))
         return fail(QMM_EINVAL, "%s: h overlaps w_up", fn);
-    // 5-16 rows: the small-M matrix-core kernel with gate and up tiles side
-    // by side, which takes K in slices of 256; 3-4 rows there too where a
+    // 5-16 rows: the matrix-core kernels with gate and up tiles side by
+    // side, as for the GEMV: 9-16 rows on the 32-row weight slices where the
+    // GEMV takes them, and any K that is not a multiple of 256 there too
+    // (the 16x16 kernel takes K in slices of 256); 3-4 rows on the 16x16 kernel where a
     // sweep (N = 2048-28672, K = 1024-8192) found it faster than the f32
     // FMA kernel: from K = 4096 and N = 3072, except between N = 4096 and
     // 8192 (N = 14336, K = 4096, M = 3: 26.4 -> 23.7 us; N = 28672, K =
@@ -245,15 +247,14 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
     // K = 2048 level, two rows faster on it everywhere)
     const bool rows_on_matrix_cores = M >= 3 && K % 256 == 0 && K >= 4096 && N >= 3072 &&
                                       !(N > 4096 && N < 8192);
-    if (M > qmm::kGemvRowsMax || rows_on_matrix_cores) {
-        if (K % 256)
-            return fail(QMM_EUNSUPPORTED,
-                        "%s: M=%lld needs K a multiple of 256 (K=%lld; up to %d rows take any K)",
-                        fn, (long long)M, (long long)K, qmm::kGemvRowsMax);
+    if (M > qmm::kGemvRowsMax && (rows_on_slices(M, N, K) || K % 256))
+        return finish(fn, qmm::launch_ffn_gate_up_slices(x, (const uint8_t *)w_gate,
+                                                         (const uint8_t *)w_up, h, (int)M,
+                                                         (int)N, (int)K, stream));
+    if (M > qmm::kGemvRowsMax || rows_on_matrix_cores)
         return finish(fn, qmm::launch_ffn_gate_up_small_m(x, (const uint8_t *)w_gate,
                                                           (const uint8_t *)w_up, h, (int)M,
                                                           (int)N, (int)K, stream));
-    }
     return finish(fn, qmm::launch_ffn_gate_up(x, (const uint8_t *)w_gate,
                                               (const uint8_t *)w_up, h, (int)M, (int)N, (int)K,
                                               stream));

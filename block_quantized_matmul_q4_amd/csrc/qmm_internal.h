@@ -44,6 +44,10 @@ hipError_t launch_ffn_gate_up(const float *x, const uint8_t *w_gate, const uint8
 hipError_t launch_ffn_gate_up_small_m(const float *x, const uint8_t *w_gate,
                                       const uint8_t *w_up, float *h, int M, int N, int K,
                                       hipStream_t stream);
+// ... and on the 32-row weight slices (16 gate and 16 up rows), M <= 16.
+hipError_t launch_ffn_gate_up_slices(const float *x, const uint8_t *w_gate,
+                                     const uint8_t *w_up, float *h, int M, int N, int K,
+                                     hipStream_t stream);
 // Q4_K GEMV, 1 to 4 activation rows (K % 256 == 0).
 hipError_t launch_gemv_q4_k(const float *x, const uint8_t *w, float *y, int M, int N, int K,
                             hipStream_t stream);

@@ -148,8 +148,7 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
  * rows, and 3 or 4 where K % 256 == 0, K >= 4096, N >= 3072 and N is not
  * between 4097 and 8191, take the bf16 matrix cores with x as two bf16
  * terms (as qmm_gemv_q4_0). Errors as above, plus QMM_EINVAL for a null or
- * overlapping w_up, QMM_EALIGN for a w_up not 16-byte aligned,
- * QMM_EUNSUPPORTED for M > 4 with K not a multiple of 256.
+ * overlapping w_up and QMM_EALIGN for a w_up not 16-byte aligned.
  * Accuracy: g and u within the GEMV bound (1e-4 of their abs-sums); the
  * activation and product in f32.
  */

@@ -40,7 +40,7 @@ ROUTES = {
                   "gemv_slice_kernel"),
     "gemm_q4_k": ("gemv_q4_k_kernel", "gemv_q4_k_pair_kernel", "gemv_small_m_kernel", "gemm_kernel",
                   "gemm_mid_kernel"),
-    "ffn_gate_up_q4_0": ("gemv_m1_kernel", "gemv_small_m_kernel"),
+    "ffn_gate_up_q4_0": ("gemv_m1_kernel", "gemv_small_m_kernel", "gemv_slice_kernel"),
 }
 # (entry point, M, N, K): every launch branch of every entry point
 CASES = [
@@ -75,6 +75,7 @@ CASES = [
     ("ffn_gate_up_q4_0", 2, 8192, 2048), ("ffn_gate_up_q4_0", 4, 2048, 8192),
     ("ffn_gate_up_q4_0", 1, 4096, 8192), ("ffn_gate_up_q4_0", 8, 8192, 2048),
     ("ffn_gate_up_q4_0", 16, 2048, 8192), ("ffn_gate_up_q4_0", 4, 8192, 4096),
+    ("ffn_gate_up_q4_0", 12, 8192, 2048), ("ffn_gate_up_q4_0", 6, 300, 320),
 ]
 
 

@@ -216,7 +216,6 @@ void gated()
     CHECK(gate_up(A, B, 0, C, 1, 300, 2048) == QMM_EINVAL);       // null w_up
     CHECK(gate_up(A, B, D + 2, C, 1, 300, 2048) == QMM_EALIGN);
     CHECK(gate_up(A, B, D, D + 32, 1, 300, 2048) == QMM_EINVAL);  // h inside w_up
-    CHECK(gate_up(A, B, D, C, 5, 300, 2112) == QMM_EUNSUPPORTED);  // 5+ rows: K % 256
     CHECK(gate_up(A, B, D, C, 17, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(0, B, D, C, 1, 300, 2048) == QMM_EINVAL);
     CHECK(gate_up(A, B, D, C, 1, 300, 96) == QMM_EUNSUPPORTED);
@@ -242,6 +241,15 @@ void gated()
               g_stub.N == 300 && g_stub.K == 2048);
     }
     CHECK(g_stub.calls == before + 23);
+    // 9-16 rows on the weight slices where the GEMV takes them, and 5-16
+    // rows there for any K not a multiple of 256
+    CHECK(gate_up(A, B, D, C, 9, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_slices") == 0);
+    CHECK(gate_up(A, B, D, C, 16, 3072, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_slices") == 0);
+    CHECK(gate_up(A, B, D, C, 16, 4096, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 8, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 5, 300, 2112) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_slices") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 300, 2112) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(g_stub.calls == before + 29);
 }
 
 void strings_and_threads()

@@ -48,6 +48,11 @@ hipError_t launch_ffn_gate_up_small_m(const float *, const uint8_t *, const uint
 {
     return record("ffn_gate_up_small_m", FMT_Q4_0, M, N, K);
 }
+hipError_t launch_ffn_gate_up_slices(const float *, const uint8_t *, const uint8_t *, float *,
+                                     int M, int N, int K, hipStream_t)
+{
+    return record("ffn_gate_up_slices", FMT_Q4_0, M, N, K);
+}
 hipError_t launch_gemv_q4_k(const float *, const uint8_t *, float *, int M, int N, int K,
                             hipStream_t)
 {

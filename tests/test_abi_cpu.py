@@ -124,7 +124,6 @@ def test_tensor_front_end_checks_types():
     ((A, B, 0, C, 1, 8, 256), qmm.QMM_EINVAL, "null pointer (w_up)"),
     ((A, B, B + 8 * 8 * 18 + 2, C, 1, 8, 256), qmm.QMM_EALIGN, "w_up"),
     ((A, B, C, C + 16, 1, 8, 256), qmm.QMM_EINVAL, "overlaps w_up"),
-    ((A, B, B + 4096, C, 5, 8, 320), qmm.QMM_EUNSUPPORTED, "needs K a multiple of 256"),
     ((A, B, B + 4096, C, 17, 8, 256), qmm.QMM_EINVAL, "exceeds 16"),
     ((0, B, B + 4096, C, 1, 8, 256), qmm.QMM_EINVAL, "null pointer"),
     ((A, B, B + 4096, C, 1, 8, 96), qmm.QMM_EUNSUPPORTED, "unsupported"),

@@ -41,6 +41,7 @@ CASES = [
     ("gemm", "q4_0", 512, 1000, 1024), ("gemm", "q8_0", 1000, 14000, 128),
     # the gated front half on the matrix cores (packed and apart)
     ("gated", "q4_0", 8, 8192, 2048), ("gated", "q4_0", 12, 1000, 1024), ("gated", "q4_0", 4, 8192, 4096),
+    ("gated", "q4_0", 16, 8192, 2048),
 ]
 
 

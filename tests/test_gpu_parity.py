@@ -493,14 +493,19 @@ def test_ffn_gate_up(orc, n, k):
 # 16384, N >= 4096 with K = 8192), ragged N, M = 3 (four rows run, three
 # stored); 5-16 tokens, and 3-4 from K = 4096 and N = 3072 outside
 # 4096 < N < 8192, on the matrix cores (hi and lo terms packed up to 8 rows,
-# apart above; each launch shape of the gated table), ragged N, N = 1, deep K
+# apart above; each launch shape of the gated table; the weight slices),
+# ragged N, N = 1, deep K
 FFN_ROWS_SHAPES = [(2, 8192, 2048), (4, 8192, 2048), (4, 2048, 8192), (3, 1000, 256),
                    (2, 333, 512), (3, 257, 1024), (4, 100, 4096), (3, 65, 16384),
                    (2, 8200, 4352), (4, 300, 64), (3, 1, 256), (4, 9000, 8192),
                    (5, 8192, 2048), (8, 8192, 2048), (9, 8192, 2048), (16, 8192, 2048),
                    (6, 333, 512), (12, 1000, 1024), (7, 8200, 4352), (16, 65, 16384),
                    (9, 1, 256), (8, 4100, 8192), (4, 6000, 8192), (3, 3072, 4096),
-                   (6, 12000, 2048), (5, 21000, 1024), (10, 5000, 1024)]
+                   (6, 12000, 2048), (5, 21000, 1024), (10, 5000, 1024),
+                   # the gated weight slices (9-16 rows where the GEMV takes
+                   # them, 5-16 rows for K not a multiple of 256)
+                   (12, 8192, 2048), (16, 3072, 2048), (13, 4097, 8192), (10, 20000, 4096),
+                   (5, 300, 320), (12, 5000, 1088), (16, 8193, 64)]
 
 
 @pytest.mark.parametrize("m,n,k", FFN_ROWS_SHAPES)

@@ -3,8 +3,7 @@ every entry point, each compared element by element with the f64 oracle.
 
 Case i draws, from numpy's generator seeded with i, an entry point and a
 shape: M from the entry point's range (GEMVs 1-16, GEMM 1-300, gated front
-half 1-16), N in 1..1200, K a multiple of 64 (Q4_K, and the gated front
-half from 5 rows: of 256) up to
+half 1-16), N in 1..1200, K a multiple of 64 (Q4_K: of 256) up to
 4096, redrawn while M N K exceeds 2^24 so that the oracle stays fast; the
 weights and activations come from the seeded generators with seed i. The
 bound is the entry point's contract: 1e-4 sum_k |w x| for the GEMVs, 8e-3
@@ -60,9 +59,7 @@ def draw(i):
         else:
             m = int(rng.integers(1, 17))
         n = int(rng.integers(1, 1201))
-        # Q4_K super-blocks, and the gated front half from 5 rows, take K in
-        # multiples of 256
-        step = 256 if fmt == "q4_k" or (entry == "ffn_gate_up_q4_0" and m > 4) else 64
+        step = 256 if fmt == "q4_k" else 64     # Q4_K super-blocks
         k = step * int(rng.integers(1, 4096 // step + 1))
         if m * n * k <= 1 << 24:
             return entry, fmt, m, n, k
