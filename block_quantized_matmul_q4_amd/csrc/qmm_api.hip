@@ -124,7 +124,8 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
 // us; N = 6144, K = 8192: 21.0 against 27.9 us). Three and four rows take the
 // matrix cores too where a timing sweep (N = 2048-28672, K = 2048-14336,
 // four rows) found them faster than every FMA launch shape: 2048 < N < 4096
-// from K = 4096 (N = 3072, K = 8192: 14.4 -> 10.5 us), N = 4096 from K =
+// above K = 2048 (N = 3072, K = 8192: 14.4 -> 10.5 us; K = 3072: 7.7 -> 5.5
+// us), N = 4096 from K =
 // 8192 (K = 14336: 18.9 -> 15.7 us), 8192 < N <= 12288 from K = 4096 (N =
 // 11008, K = 8192: 28.6 -> 24.5 us) and from K = 14336 at any N > 2048 (N =
 // 28672: 100.3 -> 89.5 us); the FMA kernels are faster or level elsewhere
@@ -132,7 +133,7 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
 bool q4_k_rows_on_matrix_cores(int64_t M, int64_t N, int64_t K)
 {
     if (M < 3 || N <= 2048) return false;
-    return K >= 14336 || (N < 4096 && K >= 4096) || (N == 4096 && K >= 8192) ||
+    return K >= 14336 || (N < 4096 && K > 2048) || (N == 4096 && K >= 8192) ||
            (N > 8192 && N <= 12288 && K >= 4096);
 }
 

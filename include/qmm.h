@@ -177,7 +177,7 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
  * of the result does not depend on the other rows;
  * |y - sum_k x w| <= 1e-4 * sum_k |x w|.
  * 5 to 16 rows, and 3 or 4 rows where N > 2048 and K >= 14336, N < 4096
- * with K >= 4096, N = 4096 with K >= 8192, or 8192 < N <= 12288 with
+ * with K > 2048, N = 4096 with K >= 8192, or 8192 < N <= 12288 with
  * K >= 4096 (bf16 matrix cores): the nibbles are exact in bf16, x is
  * carried as two bf16 terms (within 2^-17 |x|, as in qmm_gemv_q4_0), and
  * per sub-block the f32 result is d*sc * sum(q x) - dmin*mn * sum(x), the

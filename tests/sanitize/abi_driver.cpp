@@ -183,8 +183,9 @@ void q4_k_gemv()
     routed(qmm_gemv_q4_k, 16, 33, QMM_MAX_K, "gemv_small_m");
     routed(qmm_gemv_q4_k, 8, 8192, 2048, "gemv_small_m");
     // three and four rows on the matrix cores at some shapes
-    routed(qmm_gemv_q4_k, 4, 3072, 4096, "gemv_small_m");        // 2048 < N < 4096, K >= 4096
-    routed(qmm_gemv_q4_k, 4, 3072, 3840, "gemv_q4_k");
+    routed(qmm_gemv_q4_k, 4, 3072, 4096, "gemv_small_m");        // 2048 < N < 4096, K > 2048
+    routed(qmm_gemv_q4_k, 4, 3072, 2304, "gemv_small_m");
+    routed(qmm_gemv_q4_k, 4, 3072, 2048, "gemv_q4_k");
     routed(qmm_gemv_q4_k, 3, 4096, 8192, "gemv_small_m");        // N = 4096, K >= 8192
     routed(qmm_gemv_q4_k, 4, 4096, 7936, "gemv_q4_k");
     routed(qmm_gemv_q4_k, 4, 11008, 4096, "gemv_small_m");       // 8192 < N <= 12288, K >= 4096

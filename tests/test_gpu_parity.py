@@ -728,7 +728,7 @@ def test_gemv_q4_k_repeatable_and_errors():
 # ragged N, M = 3 (four rows run, the fourth not stored)
 Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8192),
                     (2, 17, 256), (3, 4099, 8448), (4, 65, 16384), (2, 50, 65536),
-                    (4, 2049, 3840), (3, 9000, 1024),
+                    (4, 2049, 2048), (3, 9000, 1024), (4, 1000, 3840),
                     # four rows over 17-32 chunks at N = 8192: T = 16, one row per
                     # thread
                     (4, 8193, 1280),
@@ -738,10 +738,10 @@ Q4_K_ROWS_SHAPES = [(2, 300, 512), (3, 1000, 2048), (4, 8192, 2048), (4, 2048, 8
                     (3, 40000, 2048), (4, 12289, 2304), (3, 12300, 5120), (4, 16385, 2048),
                     (4, 6000, 8448), (3, 9000, 3072), (4, 11008, 2048), (4, 4100, 4608),
                     (4, 4096, 3072), (3, 4096, 7936),
-                    # three and four rows on the matrix cores: 2048 < N < 4096 from
-                    # K = 4096, N = 4096 from K = 8192, 8192 < N <= 12288 from
-                    # K = 4096, any N > 2048 from K = 14336
-                    (4, 2049, 4352), (3, 3000, 8192), (3, 4096, 8448), (4, 8200, 8448),
+                    # three and four rows on the matrix cores: 2048 < N < 4096
+                    # above K = 2048, N = 4096 from K = 8192, 8192 < N <= 12288
+                    # from K = 4096, any N > 2048 from K = 14336
+                    (4, 2049, 4352), (3, 3000, 2304), (3, 3000, 8192), (3, 4096, 8448), (4, 8200, 8448),
                     (3, 9000, 5120), (4, 12288, 4096), (4, 6000, 14336), (3, 2050, 14336),
                     # two rows past 32 chunks above N = 4096: T = 32; at N = 4096: T = 64
                     (2, 4097, 2304), (2, 8192, 8448), (2, 4096, 4352)]
