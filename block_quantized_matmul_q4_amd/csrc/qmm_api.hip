@@ -242,12 +242,16 @@ QMM_API int qmm_ffn_gate_up_q4_0(const float *x, const void *w_gate, const void 
     // GEMV takes them, and any K that is not a multiple of 256 there too
     // (the 16x16 kernel takes K in slices of 256); 3-4 rows on the 16x16 kernel where a
     // sweep (N = 2048-28672, K = 1024-8192) found it faster than the f32
-    // FMA kernel: from K = 4096 and N = 3072, except between N = 4096 and
-    // 8192 (N = 14336, K = 4096, M = 3: 26.4 -> 23.7 us; N = 28672, K =
-    // 8192: 89.4 -> 74.8 us; N = 6144 stays 5-9 % faster on the FMA kernel,
-    // K = 2048 level, two rows faster on it everywhere)
-    const bool rows_on_matrix_cores = M >= 3 && K % 256 == 0 && K >= 4096 && N >= 3072 &&
-                                      !(N > 4096 && N < 8192);
+    // FMA kernel: from K = 1024 and N = 3072, except above K = 1024 between
+    // N = 4096 and 8192 and below K = 4096 beyond N = 16384 (M = 4: N =
+    // 4096, K = 2048 7.7 -> 6.6 us; N = 8192, K = 2048 10.4 -> 9.7 us; N =
+    // 11008, K = 1024 10.5 -> 8.8 us; N = 14336, K = 4096, M = 3 26.4 -> 23.7
+    // us; N = 28672, K = 8192 89.4 -> 74.8 us; N = 6144 from K = 2048 and N =
+    // 28672 at K = 2048 stay 2-9 % faster on the FMA kernel, and two rows
+    // are faster on it everywhere)
+    const bool rows_on_matrix_cores = M >= 3 && K % 256 == 0 && K >= 1024 && N >= 3072 &&
+                                      !(N > 4096 && N < 8192 && K > 1024) &&
+                                      !(N > 16384 && K < 4096);
     if (M > qmm::kGemvRowsMax && (rows_on_slices(M, N, K) || K % 256))
         return finish(fn, qmm::launch_ffn_gate_up_slices(x, (const uint8_t *)w_gate,
                                                          (const uint8_t *)w_up, h, (int)M,

@@ -145,9 +145,9 @@ QMM_API int qmm_gemm_q8_0(const float *x, const void *w, float *y, int64_t M,
  * stream in one launch that reads x once. x is f32[M][K], h f32[M][N],
  * overwritten; each weight is decoded once for all rows. Up to 4 rows take
  * f32 FMAs, and a row of h equals the one-row result bit for bit; 5 to 16
- * rows, and 3 or 4 where K % 256 == 0, K >= 4096, N >= 3072 and N is not
- * between 4097 and 8191, take the bf16 matrix cores with x as two bf16
- * terms (as qmm_gemv_q4_0). Errors as above, plus QMM_EINVAL for a null or
+ * rows, and 3 or 4 where K % 256 == 0, K >= 1024 and N >= 3072, except
+ * K > 1024 with 4096 < N < 8192 and K < 4096 with N > 16384, take the
+ * bf16 matrix cores with x as two bf16 terms (as qmm_gemv_q4_0). Errors as above, plus QMM_EINVAL for a null or
  * overlapping w_up and QMM_EALIGN for a w_up not 16-byte aligned.
  * Accuracy: g and u within the GEMV bound (1e-4 of their abs-sums); the
  * activation and product in f32.

@@ -226,22 +226,26 @@ void gated()
         CHECK(std::strcmp(g_stub.route, "ffn_gate_up") == 0 && g_stub.M == m && g_stub.N == 300);
     }
     CHECK(g_stub.calls == before + 4);
-    // 3-4 rows on the matrix cores from K = 4096 and N = 3072, outside
-    // 4096 < N < 8192
+    // 3-4 rows on the matrix cores from K = 1024 and N = 3072, except above
+    // K = 1024 at 4096 < N < 8192 and below K = 4096 beyond N = 16384
     CHECK(gate_up(A, B, D, C, 3, 3072, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
     CHECK(gate_up(A, B, D, C, 4, 8192, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
     CHECK(gate_up(A, B, D, C, 4, 6144, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
-    CHECK(gate_up(A, B, D, C, 4, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 6144, 1024) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
+    CHECK(gate_up(A, B, D, C, 3, 3072, 768) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 28672, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
+    CHECK(gate_up(A, B, D, C, 4, 28672, 4096) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
     CHECK(gate_up(A, B, D, C, 4, 2048, 8192) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
     CHECK(gate_up(A, B, D, C, 2, 8192, 8192) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
     CHECK(gate_up(A, B, D, C, 4, 8192, 4160) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
-    CHECK(g_stub.calls == before + 11);
+    CHECK(g_stub.calls == before + 15);
     for (int64_t m = 5; m <= QMM_GEMV_MAX_M; ++m) {
         CHECK(gate_up(A, B, D, C, m, 300, 2048) == QMM_OK);
         CHECK(std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0 && g_stub.M == m &&
               g_stub.N == 300 && g_stub.K == 2048);
     }
-    CHECK(g_stub.calls == before + 23);
+    CHECK(g_stub.calls == before + 27);
     // 9-16 rows on the weight slices where the GEMV takes them, and 5-16
     // rows there for any K not a multiple of 256
     CHECK(gate_up(A, B, D, C, 9, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_slices") == 0);
@@ -250,7 +254,7 @@ void gated()
     CHECK(gate_up(A, B, D, C, 8, 8192, 2048) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_small_m") == 0);
     CHECK(gate_up(A, B, D, C, 5, 300, 2112) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up_slices") == 0);
     CHECK(gate_up(A, B, D, C, 4, 300, 2112) == QMM_OK && std::strcmp(g_stub.route, "ffn_gate_up") == 0);
-    CHECK(g_stub.calls == before + 29);
+    CHECK(g_stub.calls == before + 33);
 }
 
 void strings_and_threads()

@@ -505,7 +505,9 @@ FFN_ROWS_SHAPES = [(2, 8192, 2048), (4, 8192, 2048), (4, 2048, 8192), (3, 1000, 
                    # the gated weight slices (9-16 rows where the GEMV takes
                    # them, 5-16 rows for K not a multiple of 256)
                    (12, 8192, 2048), (16, 3072, 2048), (13, 4097, 8192), (10, 20000, 4096),
-                   (5, 300, 320), (12, 5000, 1088), (16, 8193, 64)]
+                   (5, 300, 320), (12, 5000, 1088), (16, 8193, 64),
+                   # 3-4 tokens on either kernel at K = 1024-2048
+                   (4, 6144, 2048), (3, 3072, 1024), (4, 11008, 1024), (3, 20000, 2048)]
 
 
 @pytest.mark.parametrize("m,n,k", FFN_ROWS_SHAPES)
@@ -522,8 +524,9 @@ def test_ffn_gate_up_rows(orc, m, n, k):
                            f"{float(np.max(err / bound)):.3g}")
 
 
-@pytest.mark.parametrize("m,n,k", [(2, 1000, 256), (3, 8192, 2048), (4, 2048, 8192),
-                                   (4, 65, 16384), (4, 4100, 5120)])
+@pytest.mark.parametrize("m,n,k", [(2, 1000, 256), (3, 6144, 2048), (4, 2048, 8192),
+                                   (4, 65, 16384), (4, 4100, 5120), (2, 8192, 2048),
+                                   (4, 28672, 2048), (3, 8192, 768)])
 def test_ffn_gate_up_rows_match_single_row_bitwise(m, n, k):
     x = synth.activations(m, k, seed=39)
     wg, wu = synth.q4_0_weights(n, k, seed=39), synth.q4_0_weights(n, k, seed=40)
