@@ -72,31 +72,35 @@ int finish(const char *fn, hipError_t err)
     return QMM_OK;
 }
 
-// The Q4_0 / Q8_0 GEMV for 1 <= M <= 16 (validated). Up to 4 rows take the
-// f32 FMA kernel, which streams the weights once and decodes each weight
-// once for all rows; from 3 rows over large matrices (K and N >= 4096, or
-// K > 2048 with 2048 < N < 4096) its four FMAs per weight make it
-// VALU-bound and the matrix-core kernel is faster (Q4_0, M = 4: N = 13824,
-// K = 5120 30.3 -> 17.9 us; N = 4096, K = 14336 18.9 -> 13.5 us; N = 2304,
-// K = 8192 13.2 -> 8.5 us; N = 2560, K = 2560 6.0 -> 4.8 us; Q8_0 N = 3072,
-// K = 8192 15.3 -> 10.9 us). Up to N = 2048 (the FFN down shape, K = 8192:
-// 7.8 against 8.5 us) and at K = 2048 (level below N = 4096; the FFN up
-// shape, N = 8192) the FMA kernel is as fast or faster, except just past
-// K = 8192 between N = 1024 and 2048: the FMA kernel stages four rows of x
-// in chunks of 128 pairs, and a second, nearly empty chunk costs it almost
-// as much as the first (Q4_0, N = 1536, K = 8960: 11.3 against 9.1 us on
-// the matrix cores; level from K = 12288, and for Q8_0 from K = 9728).
-// Q4_0 rows over wide matrices (N >= 16384) take the matrix cores from
-// K = 1536 too (N = 151936, K = 1536: 60.6 -> 44.6 us; N = 262144, K =
-// 2048: 104.0 -> 91.3 us; level at N = 65536), while Q8_0's FMA kernel
-// stays faster there (M = 4, N = 262144: 122 against 147 us).
-// 9-16 rows take the 32-row weight-slice kernel above N = 4096 and, from
-// N = 3072, at K <= 2048 (a sweep at M = 16, N = 3072-7168, K = 2048-14336,
-// all three formats: Q4_0, N = 6144, K = 2048 9.6 -> 6.7 us; Q4_K, K =
-// 8192 27.9 -> 21.0 us; Q8_0, N = 5120, K = 4096 16.9 -> 13.6 us; at
-// N <= 4096 from K = 4096 the 16x16 kernel stays faster, N = 4096, K =
-// 14336 24.7 against 34.2 us), and so does any K that is not a multiple of
-// 256 (the 16x16 kernel takes K in slices of 256).
+// The Q4_0 / Q8_0 GEMV for 1 <= M <= 16 (validated). Each route below was
+// chosen by timing sweeps on random weights, cold copies:
+//  * 1-4 rows: the f32 FMA kernel, which streams the weights once and
+//    decodes each weight once for all rows (the FFN shapes: N = 8192,
+//    K = 2048 level with the matrix cores at four rows; N = 2048, K = 8192
+//    7.8 against 8.5 us);
+//  * 3-4 rows take the 16x16 matrix-core kernel where the FMA kernel's four
+//    FMAs per weight, or its activation staging, cost more:
+//    - K, N >= 4096 (Q4_0, M = 4: N = 13824, K = 5120 30.3 -> 17.9 us;
+//      N = 4096, K = 14336 18.9 -> 13.5 us);
+//    - 2048 < N < 4096 above K = 2048 (N = 2304, K = 8192 13.2 -> 8.5 us;
+//      N = 2560, K = 2560 6.0 -> 4.8 us; Q8_0 N = 3072, K = 8192 15.3 ->
+//      10.9 us);
+//    - 1024 <= N <= 2048 just past K = 8192, where the FMA kernel stages
+//      four rows of x in chunks of 128 pairs and the second, nearly empty
+//      chunk costs almost as much as the first (Q4_0, N = 1536, K = 8960:
+//      11.3 -> 9.1 us; level from K = 12288, Q8_0 from K = 9728);
+//    - Q4_0 from N = 16384 at K >= 1536 (N = 151936, K = 1536: 60.6 -> 44.6
+//      us; N = 262144, K = 2048: 104.0 -> 91.3 us; level at N = 65536),
+//      while Q8_0's FMA kernel stays faster there (N = 262144: 122 against
+//      147 us);
+//  * 5-16 rows: the 16x16 matrix-core kernel, and 9-16 rows the 32-row
+//    weight-slice kernel above N = 4096 and, from N = 3072, at K <= 2048 (a
+//    sweep at M = 16, N = 3072-7168, K = 2048-14336, all three formats:
+//    Q4_0, N = 6144, K = 2048 9.6 -> 6.7 us; Q4_K, K = 8192 27.9 -> 21.0 us;
+//    Q8_0, N = 5120, K = 4096 16.9 -> 13.6 us; at N <= 4096 from K = 4096
+//    the 16x16 kernel stays faster, N = 4096, K = 14336 24.7 against 34.2
+//    us), as does any K that is not a multiple of 256 (the 16x16 kernel
+//    takes K in slices of 256).
 bool rows_on_slices(int64_t M, int64_t N, int64_t K)
 {
     return M > 8 && (N > 4096 || (N >= 3072 && K <= 2048));
@@ -117,19 +121,21 @@ hipError_t gemv_launch(int fmt, const float *x, const uint8_t *w, float *y, int6
     return qmm::launch_gemv_small_m(fmt, x, w, y, (int)M, (int)N, (int)K, stream);
 }
 
-// The Q4_K GEMV (validated, K % 256 == 0): up to 4 rows f32 FMAs on each
-// weight formed once; 5 to 16 rows the matrix-core kernels (codes exact in
-// bf16, x as two bf16 terms), 9 to 16 rows on 32-row weight slices where
-// the Q4_0 GEMV takes them (N = 8192, K = 2048, M = 16: 7.9 against 11.4
-// us; N = 6144, K = 8192: 21.0 against 27.9 us). Three and four rows take the
-// matrix cores too where a timing sweep (N = 2048-28672, K = 2048-14336,
-// four rows) found them faster than every FMA launch shape: 2048 < N < 4096
-// above K = 2048 (N = 3072, K = 8192: 14.4 -> 10.5 us; K = 3072: 7.7 -> 5.5
-// us), N = 4096 from K =
-// 8192 (K = 14336: 18.9 -> 15.7 us), 8192 < N <= 12288 from K = 4096 (N =
-// 11008, K = 8192: 28.6 -> 24.5 us) and from K = 14336 at any N > 2048 (N =
-// 28672: 100.3 -> 89.5 us); the FMA kernels are faster or level elsewhere
-// (N <= 2048, K = 2048, N = 4097-8192 below K = 14336, N > 12288).
+// The Q4_K GEMV (validated, K % 256 == 0), routed like the Q4_0 one:
+//  * 1-4 rows: f32 FMAs on each weight formed once;
+//  * 3-4 rows take the 16x16 matrix-core kernel where a sweep (N =
+//    2048-28672, K = 2048-14336, four rows, ten FMA launch shapes) found it
+//    faster than every FMA shape: 2048 < N < 4096 above K = 2048 (N = 3072,
+//    K = 8192 14.4 -> 10.5 us; K = 3072 7.7 -> 5.5 us), N = 4096 from
+//    K = 8192 (K = 14336 18.9 -> 15.7 us), 8192 < N <= 12288 from K = 4096
+//    (N = 11008, K = 8192 28.6 -> 24.5 us) and any N > 2048 from K = 14336
+//    (N = 28672 100.3 -> 89.5 us); the FMA kernels are faster or level
+//    elsewhere (N <= 2048, K = 2048, N = 4097-8192 below K = 14336,
+//    N > 12288 below K = 14336);
+//  * 5-16 rows: the matrix-core kernels (codes exact in bf16, x as two bf16
+//    terms), 9-16 rows on the weight slices where the Q4_0 GEMV takes them
+//    (N = 8192, K = 2048, M = 16: 7.9 against 11.4 us; N = 6144, K = 8192:
+//    21.0 against 27.9 us).
 bool q4_k_rows_on_matrix_cores(int64_t M, int64_t N, int64_t K)
 {
     if (M < 3 || N <= 2048) return false;
