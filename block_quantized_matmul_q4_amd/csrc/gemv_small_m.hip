@@ -517,10 +517,11 @@ hipError_t launch_gemv_small_m(int fmt, const float *x, const uint8_t *w, float 
 // workgroups (N / 16 of them) all fit the chip at once. Up to 8 rows (13.5
 // KB of LDS per wave): 8 waves to N = 4096, 4 to N = 8192, 2 to N = 20480,
 // then 4 again (N = 28672, K = 8192, M = 5: 81.2 us, against 98.4 with 2
-// waves); 9-16 rows (22.3 KB per wave): 6 waves to N = 4096, else 3. Against
-// two GEMV launches for gate and up: N = 8192, K = 2048, M = 5 12.8 ->
-// 9.9 us, M = 16 16.3 -> 15.6 us; N = 13824, K = 5120, M = 5 35.8 -> 31.2
-// us; N = 4096, K = 4096, M = 16 20.0 -> 13.1 us.
+// waves); 9-16 rows (22.3 KB per wave): 6 waves to N = 4096, else 3 (the
+// entry point now sends 9-16 rows over N > 4096 to the gated weight
+// slices, which are faster there). Against two GEMV launches for gate and
+// up: N = 8192, K = 2048, M = 5 12.8 -> 9.9 us; N = 13824, K = 5120, M = 5
+// 35.8 -> 31.2 us; N = 4096, K = 4096, M = 16 20.0 -> 13.1 us.
 hipError_t launch_ffn_gate_up_small_m(const float *x, const uint8_t *w_gate,
                                       const uint8_t *w_up, float *h, int M, int N, int K,
                                       hipStream_t stream)
