@@ -57,7 +57,7 @@ Timing:
 The CPU baseline times the f64 oracle (test infrastructure, plain C with
 OpenMP) on full decode steps for a bounded number of seconds.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
+Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 10]
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 
@@ -95,7 +95,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="replay the warmup work for at least this long before each "
