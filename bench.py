@@ -249,7 +249,7 @@ def library_gemm_reference(xp, m, n, k, settle_ms, reps=50):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
 
